@@ -1,0 +1,388 @@
+"""Plain, slow CPU oracle of the load-balanced MoE token path.
+
+TEST INFRASTRUCTURE.  Only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import this module.  It shares no code with
+the HIP library and imports nothing from it; the product path never calls it.
+
+Every step is written from the pages' description, in their notation:
+
+  S tokens per rank, K experts per token, E routed experts, R ranks (each
+  owning E/R "home" experts), B prefetch slots per rank, T_e pairs routed to
+  expert e, T̄ = mean of T_e, max_vio = max_e T_e/T̄ - 1.
+
+Sources (page title, then section):
+  [MoonEP-GR]  TWO DOTS, "MoonEP: πώς η εξισορρόπηση των AI experts αλλάζει
+               την υποδομή των MoE μοντέλων"
+  [MoonEP-FR]  hamidun.com news, "Moonshot AI открыла код MoonEP ..."
+  [UltraEP]    remio.ai, "Xiaohongshuと北京大学がUltraEPを発表、静的MoE負荷分散に挑戦"
+  [AlignSort]  新智元 article on SGLang's MoE Align & Sort kernel
+
+Where the pages leave a step open, the plain reading taken is stated at the
+function.  Floating point is fp64 except where the method itself fixes fp32
+(the top-K key is an fp32 value; bf16 rows widen exactly to fp32).
+
+Parity pins (see tests/test_oracle_*.py): brute-force top-K, closed-form gates,
+numpy bincount, hand-derived plans W1-W3, brute-force enumeration of
+rule-conforming plans, the balanced-routing special case (textbook stable
+counting sort), invariants, and the identity-expert closed form for combine.
+Gate values' last fp32 bit is pinned only to 1e-6 relative (parity partially
+unpinned there); rows past each rank's padded end are unspecified.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SOFTMAX = 0
+SIGMOID = 1
+UNSPECIFIED = -2          # marker for sorted_ids rows the method leaves undefined
+
+
+# --------------------------------------------------------------------------- O1
+def route_topk(logits, K, score_fn, sel_bias=None, renorm=False):
+    """Router top-K.  [AlignSort] (the MoE layer gates each token to its Top-K
+    experts by gate score, with DeepSeek's per-expert gating bias) and
+    [MoonEP-GR] section "Γιατί τα Mixture-of-Experts δημιουργούν πρόβλημα
+    κατανομής" (the router picks each token's top K experts).
+
+    Readings: the selection key is the fp32 value logit[t,e] (+ sel_bias[e],
+    one fp32 round-to-nearest-even add); experts are ordered by key
+    descending, ties (IEEE equality, so -0.0 == +0.0) to the lower expert
+    index; the output keeps that order.  The gating bias only steers
+    selection: gates are score_fn of the raw logit (sigmoid, or softmax over
+    all E raw logits), optionally renormalised over the K chosen.  NaN keys
+    are not allowed.
+
+    Returns ids int32 [N,K] and gates fp64 [N,K].
+    """
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    N, E = logits.shape
+    if not 1 <= K <= E:
+        raise ValueError("need 1 <= K <= E")
+    key = logits
+    if sel_bias is not None:
+        key = logits + np.asarray(sel_bias, dtype=np.float32)[None, :]
+    expert = np.broadcast_to(np.arange(E, dtype=np.int64), (N, E))
+    # lexsort: last key is primary -> descending key, then ascending expert
+    order = np.lexsort((expert, -key), axis=-1)
+    ids = order[:, :K].astype(np.int32)
+
+    l64 = logits.astype(np.float64)
+    if score_fn == SIGMOID:
+        score = 1.0 / (1.0 + np.exp(-l64))
+    elif score_fn == SOFTMAX:
+        m = l64.max(axis=1, keepdims=True)
+        ex = np.exp(l64 - m)
+        score = ex / ex.sum(axis=1, keepdims=True)
+    else:
+        raise ValueError("score_fn")
+    gates = np.take_along_axis(score, ids.astype(np.int64), axis=1)
+    if renorm:
+        gates = gates / gates.sum(axis=1, keepdims=True)
+    return ids, gates
+
+
+# --------------------------------------------------------------------------- O2
+def load_matrix(ids, R, S, E):
+    """Exact post-routing load matrix counts[src][e]: how many of source rank
+    src's (token, expert) pairs chose expert e.  [UltraEP] section
+    "その仕組みは高速なエキスパート複製に依存する" (the runtime starts from the
+    exact load matrix of per-source-rank token counts per logical expert).
+    Reading: token t belongs to source rank t // S."""
+    ids = np.asarray(ids)
+    N, K = ids.shape
+    if N != R * S:
+        raise ValueError("N != R*S")
+    if ids.size and (ids.min() < 0 or ids.max() >= E):
+        raise ValueError("expert id out of range")
+    counts = np.zeros((R, E), dtype=np.int64)
+    src = np.repeat(np.arange(N, dtype=np.int64) // S, K)
+    np.add.at(counts, (src, ids.reshape(-1).astype(np.int64)), 1)
+    return counts
+
+
+def imbalance(counts, S, K):
+    """max_vio = max_e(T_e / T̄) - 1 with T̄ the mean per-expert load
+    ([MoonEP-FR] "Pourquoi le parallélisme d'experts est-il nécessaire";
+    [MoonEP-GR] maxvio, zero = perfect balance) and the per-rank view
+    max_r L_r / (S K) - 1 of the same skew before balancing."""
+    counts = np.asarray(counts, dtype=np.int64)
+    R, E = counts.shape
+    T = counts.sum(axis=0)
+    P = int(T.sum())
+    nh = E // R
+    L = T.reshape(R, nh).sum(axis=1)
+    Tbar = P / E
+    return {
+        "T": T,
+        "L": L,
+        "max_vio": float(T.max() / Tbar - 1.0) if P else 0.0,
+        "rank_imbalance": float(L.max() / (S * K) - 1.0) if P else 0.0,
+    }
+
+
+# --------------------------------------------------------------------------- O3
+def capacity(E, K, S, blk, cap=0):
+    """Static rows per rank of the receive buffer.  Each rank holds exactly S*K
+    real rows in at most min(E, S*K) non-empty expert segments, each padded
+    to a multiple of blk, so S*K + min(E, S*K)*(blk-1) rows (rounded up to
+    blk) always suffice.  Static shapes: [MoonEP-GR] section "Online planning,
+    zero copy και στατικά σχήματα".  A caller may ask for a smaller cap."""
+    if cap:
+        return int(cap)
+    SK = S * K
+    need = SK + min(E, SK) * (blk - 1)
+    return ((need + blk - 1) // blk) * blk
+
+
+def plan_balance(counts, K, S, B, blk, cap=0):
+    """Online redundant-expert plan giving every rank exactly S*K pairs.
+
+    [MoonEP-GR] sections "Η βασική υπόσχεση του MoonEP: σταθερό φορτίο S × K"
+    (every rank receives exactly S*K; a few temporary expert copies are placed
+    on other ranks, planned online from the current router output) and "Το
+    memory contract ..." (weight rows 0..E-1 hold the ranks' experts, rows
+    E..E+B-1 are local prefetch slots found by row index; when remote experts
+    exceed the slots they are read from the home rank, still correct).
+    [UltraEP] "その仕組みは..." (replicas exist only when the plan gives them
+    work; per-token destinations come from cumulative quotas).
+
+    The fixed rule: home rank r keeps min(L_r, S*K) of its pairs; the overflow
+    segments fill deficit ranks in ascending order.  Readings taken:
+      * home experts of rank r are [r*E/R, (r+1)*E/R);
+      * the pairs r keeps are the first S*K of its home stream (its experts
+        ascending, each expert's pairs by ascending flat index f = t*K + k);
+      * the overflow stream lists (expert e, o_e) for o_e > 0 in ascending e
+        (= rank ascending, expert ascending); the deficit stream lists ranks
+        with def_r > 0 in ascending r; both are laid on one line and every
+        non-empty intersection [O_e, O_e+o_e) ∩ [D_d, D_d+def_d) is one
+        replica segment (e, d, count);
+      * on rank d the replica segments, in line order, take prefetch slots
+        0..B-1 (weight row E+j); further ones are remote (weight row e);
+      * the segment table of rank r is its E/R home experts ascending (count
+        h_e, possibly 0) then its replica segments in line order; each count
+        is padded up to a multiple of blk and the padded starts are the
+        exclusive prefix sums (the cu_seqlens of the grouped GEMM).
+    """
+    counts = np.asarray(counts, dtype=np.int64)
+    R, E = counts.shape
+    if E % R:
+        raise ValueError("E must be a multiple of R")
+    nh = E // R
+    SK = S * K
+    C = capacity(E, K, S, blk, cap)
+    home = lambda e: e // nh  # noqa: E731
+
+    T = counts.sum(axis=0)
+    if int(T.sum()) != R * SK:
+        raise ValueError("counts do not sum to R*S*K")
+
+    # per-rank load and the keep / overflow / deficit split
+    L = np.array([T[r * nh:(r + 1) * nh].sum() for r in range(R)], dtype=np.int64)
+    keep = np.minimum(L, SK)
+    over = L - keep
+    deficit = SK - keep
+
+    # home stream of each rank: expert e occupies [Pe, Pe + T_e)
+    h = np.zeros(E, dtype=np.int64)
+    o = np.zeros(E, dtype=np.int64)
+    for r in range(R):
+        Pe = 0
+        for e in range(r * nh, (r + 1) * nh):
+            h[e] = min(max(SK - Pe, 0), T[e])
+            o[e] = T[e] - h[e]
+            Pe += T[e]
+
+    # overflow stream offsets O_e and deficit stream offsets D_r
+    O = np.zeros(E, dtype=np.int64)
+    acc = 0
+    for e in range(E):
+        O[e] = acc
+        acc += o[e]
+    D = np.zeros(R + 1, dtype=np.int64)
+    acc = 0
+    for r in range(R):
+        D[r] = acc
+        acc += deficit[r]
+    D[R] = acc
+
+    # replica segments = non-empty intersections, in line order
+    reps = []
+    for e in range(E):
+        if o[e] == 0:
+            continue
+        for d in range(R):
+            if deficit[d] == 0:
+                continue
+            lo = max(O[e], D[d])
+            hi = min(O[e] + o[e], D[d] + deficit[d])
+            if hi > lo:
+                reps.append((int(lo), e, d, int(hi - lo)))
+    reps.sort()
+
+    # per-rank segment tables
+    segs = [[(e, e, int(h[e]), None) for e in range(r * nh, (r + 1) * nh)] for r in range(R)]
+    n_slots = np.zeros(R, dtype=np.int64)
+    n_remote = np.zeros(R, dtype=np.int64)
+    replicas = []
+    for (lo, e, d, c) in reps:
+        j = n_slots[d] + n_remote[d]
+        if j < B:
+            wrow = E + j
+            n_slots[d] += 1
+        else:
+            wrow = e
+            n_remote[d] += 1
+        segs[d].append((e, wrow, c, lo))
+        replicas.append({"expert": e, "rank": d, "count": c, "line": lo, "wrow": wrow})
+
+    pad = lambda c: ((c + blk - 1) // blk) * blk  # noqa: E731
+    seg_tables = []
+    n_rows_padded = np.zeros(R, dtype=np.int64)
+    home_row = np.zeros(E, dtype=np.int64)
+    rep_row = {}
+    for r in range(R):
+        start = 0
+        table = []
+        for (e, wrow, c, lo) in segs[r]:
+            table.append({"expert": e, "wrow": wrow, "count": c, "start": start})
+            if lo is None:
+                home_row[e] = start
+            else:
+                rep_row[(e, r)] = start
+            start += pad(c)
+        n_rows_padded[r] = start
+        seg_tables.append(table)
+    for rp in replicas:
+        rp["row"] = rep_row[(rp["expert"], rp["rank"])]
+
+    return {
+        "E": E, "K": K, "R": R, "S": S, "B": B, "blk": blk, "C": C, "SK": SK,
+        "T": T, "L": L, "keep": keep, "over": over, "deficit": deficit,
+        "h": h, "o": o, "O": O, "D": D,
+        "replicas": replicas, "segments": seg_tables,
+        "n_rows_padded": n_rows_padded, "n_slots": n_slots, "n_remote": n_remote,
+        "home_row": home_row,
+        "capacity_ok": bool(n_rows_padded.max() <= C) if R else True,
+    }
+
+
+# --------------------------------------------------------------------------- O4
+def align_sort(ids, plan):
+    """Block-aligned sort of the (token, expert) pairs into each rank's expert
+    segments.  [AlignSort]: pairs are sorted by expert id with every expert's
+    share padded to the GEMM block so the grouped GEMM takes whole blocks; the
+    permutation records the source -> destination map.  [UltraEP]: per-token
+    destinations follow from a local lookup against cumulative quotas.
+
+    For pair f = t*K + k with e = ids[t,k] and q = #{f' < f : ids[f'] = e}:
+      q < h_e  -> home rank of e, row = home start of e + q
+      q >= h_e -> o = O_e + (q - h_e); d is the rank with D_d <= o < D_d+def_d;
+                  row = start of e's replica segment on d + (o - max(O_e, D_d)).
+    slot[f] = d*C + row and sorted_ids[d*C + row] = f.  Readings: padding rows
+    below a rank's padded end hold the sentinel P (one past the last pair);
+    rows at or past the padded end are left unspecified (UNSPECIFIED here);
+    block tables give, per blk-row block, the weight row and expert of the
+    segment covering it, or -1 past the padded end.
+    """
+    ids = np.asarray(ids)
+    N, K = ids.shape
+    P = N * K
+    E, R, C, blk = plan["E"], plan["R"], plan["C"], plan["blk"]
+    nh = E // R
+    h, O, D, deficit = plan["h"], plan["O"], plan["D"], plan["deficit"]
+    flat = ids.reshape(-1).astype(np.int64)
+
+    # q: stable rank of each pair inside its expert (library stable sort)
+    order = np.argsort(flat, kind="stable")
+    sorted_e = flat[order]
+    group_start = np.searchsorted(sorted_e, sorted_e, side="left")
+    q = np.empty(P, dtype=np.int64)
+    q[order] = np.arange(P, dtype=np.int64) - group_start
+
+    rep_start = np.full((E, R), -1, dtype=np.int64)
+    for rp in plan["replicas"]:
+        rep_start[rp["expert"], rp["rank"]] = rp["row"]
+
+    at_home = q < h[flat]
+    d = np.where(at_home, flat // nh, 0)
+    row = np.where(at_home, plan["home_row"][flat] + q, 0)
+    ov = ~at_home
+    if ov.any():
+        e_ov = flat[ov]
+        o_pos = O[e_ov] + (q[ov] - h[e_ov])
+        # the deficit rank whose interval holds o_pos (ranks without deficit
+        # have empty intervals and are never the last with D_d <= o_pos)
+        d_ov = np.searchsorted(D[:R], o_pos, side="right") - 1
+        assert np.all(D[d_ov] <= o_pos) and np.all(o_pos < D[d_ov] + deficit[d_ov])
+        start = rep_start[e_ov, d_ov]
+        assert np.all(start >= 0)
+        d[ov] = d_ov
+        row[ov] = start + (o_pos - np.maximum(O[e_ov], D[d_ov]))
+    slot = d * C + row
+
+    sorted_ids = np.full(R * C, UNSPECIFIED, dtype=np.int64)
+    nb = C // blk
+    block_wrow = np.full((R, nb), -1, dtype=np.int64)
+    block_expert = np.full((R, nb), -1, dtype=np.int64)
+    for r in range(R):
+        for sg in plan["segments"][r]:
+            plen = ((sg["count"] + blk - 1) // blk) * blk
+            lo = r * C + sg["start"]
+            sorted_ids[lo: lo + plen] = P                 # padding sentinel
+            for b in range(sg["start"] // blk, (sg["start"] + plen) // blk):
+                block_wrow[r, b] = sg["wrow"]
+                block_expert[r, b] = sg["expert"]
+    sorted_ids[slot] = np.arange(P, dtype=np.int64)
+    return {"slot": slot, "sorted_ids": sorted_ids,
+            "block_wrow": block_wrow, "block_expert": block_expert, "q": q}
+
+
+# --------------------------------------------------------------------------- O5
+def dispatch_rows(x_bits, slot, K):
+    """Zero-copy dispatch: pair f's token row is written straight to its final
+    expert-grouped row slot[f] of the static receive buffer ([MoonEP-GR]
+    "Online planning, zero copy ..."; tokens land in their final positions,
+    grouped per expert, and the caller gets views of that buffer).
+    Returns {row: bf16 bits} as (rows, data) with data[i] = x[f // K]."""
+    slot = np.asarray(slot, dtype=np.int64)
+    f = np.arange(slot.size, dtype=np.int64)
+    return slot, np.asarray(x_bits)[f // K]
+
+
+def dispatch(x_bits, slot, K, R, C):
+    """Full receive buffer [R*C, H] (bit copy); rows no pair maps to stay 0."""
+    x_bits = np.asarray(x_bits)
+    recv = np.zeros((R * C, x_bits.shape[1]), dtype=np.uint16)
+    rows, data = dispatch_rows(x_bits, slot, K)
+    recv[rows] = data
+    return recv
+
+
+# --------------------------------------------------------------------------- O6
+def bf16_to_f64(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)) \
+        .view(np.float32).astype(np.float64)
+
+
+def combine(out_rows_of, slot, gates, K, tokens=None):
+    """Inverse of dispatch: y[t] = sum_k gates[t,k] * out[slot[t*K+k]] in
+    ascending k ([MoonEP-GR]: combine returns the experts' results to their
+    source tokens; [UltraEP]: tokens come back after expert compute).
+    Computed in fp64 from the bf16 rows (exact widening) and the fp32 gates.
+    ``out_rows_of(rows)`` returns bf16 bits of the requested rows of the
+    expert-output buffer.  Returns fp64 y [len(tokens), H] and the fp64 sum
+    of |g * out| per element (the scale of the rounding-error bound)."""
+    slot = np.asarray(slot, dtype=np.int64)
+    gates = np.asarray(gates, dtype=np.float32)
+    N = gates.shape[0]
+    tokens = np.arange(N) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    y = None
+    mag = None
+    for k in range(K):
+        rows = slot[tokens * K + k]
+        v = bf16_to_f64(out_rows_of(rows))
+        g = gates[tokens, k].astype(np.float64)[:, None]
+        term = g * v
+        y = term if y is None else y + term
+        mag = np.abs(term) if mag is None else mag + np.abs(term)
+    return y, mag

@@ -1,0 +1,215 @@
+"""Pins for the oracle's balancing plan and align-sort (CPU only).
+
+Hand-derived examples (tests/golden/W*.json), brute-force enumeration of
+rule-conforming plans, the balanced-routing special case (which must reduce
+to a textbook stable counting sort), and the invariants the pages state.
+"""
+import glob
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import brute_force as bf
+from workloads import WORKLOADS, router_logits
+
+GOLDEN = sorted(glob.glob(os.path.join(os.path.dirname(__file__), "golden", "W*.json")))
+
+
+def _run(ids, E, R, S, K, B, blk, cap=0):
+    counts = oracle.load_matrix(ids, R, S, E)
+    plan = oracle.plan_balance(counts, K, S, B, blk, cap)
+    al = oracle.align_sort(ids, plan)
+    return counts, plan, al
+
+
+@pytest.mark.parametrize("path", GOLDEN, ids=[os.path.basename(p) for p in GOLDEN])
+def test_hand_examples(path):
+    g = json.load(open(path))
+    sh = g["shape"]
+    E, R, S, K, B, blk = (sh[k] for k in ("E", "R", "S", "K", "B", "blk"))
+    ids, _ = oracle.route_topk(np.array(g["logits"], np.float32), K, oracle.SIGMOID)
+    assert ids.tolist() == g["ids"]
+    counts, plan, al = _run(ids, E, R, S, K, B, blk)
+    assert counts.tolist() == g["counts"]
+    st = oracle.imbalance(counts, S, K)
+    assert st["max_vio"] == pytest.approx(g["max_vio"])
+    assert st["rank_imbalance"] == pytest.approx(g["rank_imbalance"])
+    for key in ("T", "L", "deficit", "h", "o", "O", "D", "n_rows_padded", "n_slots",
+                "n_remote", "home_row"):
+        assert plan[key].tolist() == g[key], key
+    assert plan["C"] == g["C"]
+    assert plan["replicas"] == g["replicas"]
+    assert plan["segments"] == g["segments"]
+    assert al["slot"].tolist() == g["slot"]
+    C = plan["C"]
+    for r in range(R):
+        want = g["sorted_ids"][r]
+        got = al["sorted_ids"][r * C:(r + 1) * C].tolist()
+        for w_, x_ in zip(want, got):
+            if w_ is None:
+                assert x_ == oracle.UNSPECIFIED
+            else:
+                assert x_ == w_
+    assert al["block_wrow"].tolist() == g["block_wrow"]
+    assert al["block_expert"].tolist() == g["block_expert"]
+    if len(ids) * K <= 12:
+        assert bf.min_replicas(ids.tolist(), E, R, S) == g["min_replicas"]
+
+
+def check_invariants(ids, plan, al):
+    """Everything the pages (and the fixed rule) say a plan must satisfy."""
+    E, R, K, B, blk, C, SK = (plan[k] for k in ("E", "R", "K", "B", "blk", "C", "SK"))
+    nh = E // R
+    N = ids.shape[0]
+    P = N * K
+    flat = ids.reshape(-1)
+    T = plan["T"]
+    # logical routing unchanged, every pair on a copy of its own expert
+    per_expert = np.array(plan["h"], dtype=np.int64).copy()
+    seen = set()
+    for rp in plan["replicas"]:
+        e, d = rp["expert"], rp["rank"]
+        assert rp["count"] > 0                      # a replica exists only with work
+        assert d != e // nh                         # never on the home rank
+        assert plan["deficit"][d] > 0               # only on deficit ranks
+        assert (e, d) not in seen                   # each (e, d) at most once
+        seen.add((e, d))
+        per_expert[e] += rp["count"]
+    assert (per_expert == T).all()
+    # exactly S*K real rows on every rank
+    real = np.zeros(R, dtype=np.int64)
+    for r in range(R):
+        for sg in plan["segments"][r]:
+            real[r] += sg["count"]
+    assert (real == SK).all()
+    # slotted replicas <= B, the rest read from home
+    assert (plan["n_slots"] <= B).all()
+    for r in range(R):
+        slotted = [sg for sg in plan["segments"][r] if sg["wrow"] >= E]
+        assert sorted(sg["wrow"] for sg in slotted) == list(range(E, E + len(slotted)))
+    # the greedy merge cuts the line only at overflow / deficit boundaries
+    n_over_seg = int((plan["o"] > 0).sum())
+    n_def = int((plan["deficit"] > 0).sum())
+    if n_over_seg:
+        assert len(plan["replicas"]) <= n_over_seg + n_def - 1
+    # align: slot is a bijection onto the real rows; sorted_ids inverts it
+    slot = al["slot"]
+    assert len(set(slot.tolist())) == P
+    assert (al["sorted_ids"][slot] == np.arange(P)).all()
+    for r in range(R):
+        for sg in plan["segments"][r]:
+            assert sg["start"] % blk == 0
+            rows = al["sorted_ids"][r * C + sg["start"]: r * C + sg["start"] + sg["count"]]
+            assert (np.diff(rows) > 0).all()                     # ascending f inside
+            assert (flat[rows] == sg["expert"]).all()            # right expert
+            plen = -(-sg["count"] // blk) * blk
+            pad = al["sorted_ids"][r * C + sg["start"] + sg["count"]: r * C + sg["start"] + plen]
+            assert (pad == P).all()
+    assert (plan["n_rows_padded"] <= C).all()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_invariants_random_small(seed):
+    rng = np.random.default_rng(seed)
+    R = int(rng.choice([1, 2, 3, 4, 8]))
+    nh = int(rng.integers(1, 4))
+    E = R * nh
+    K = int(rng.integers(1, E + 1))
+    S = int(rng.integers(1, 40))
+    B = int(rng.integers(0, 4))
+    blk = int(rng.choice([1, 2, 4, 8, 16]))
+    w = (np.arange(E, 0, -1.0) ** 3)[rng.permutation(E)]
+    logits = (np.log(w)[None, :] + rng.gumbel(size=(R * S, E))).astype(np.float32)
+    ids, _ = oracle.route_topk(logits, K, oracle.SIGMOID)
+    _, plan, al = _run(ids, E, R, S, K, B, blk)
+    check_invariants(ids, plan, al)
+
+
+@pytest.mark.parametrize("name", ["tiny", "wideep"])
+def test_invariants_on_workloads(name):
+    w = WORKLOADS[name]
+    if name != "tiny":
+        w = w.with_(S=32)
+    ids, _ = oracle.route_topk(router_logits(w, 0), w.K, oracle.SIGMOID)
+    _, plan, al = _run(ids, w.E, w.R, w.S, w.K, w.B, w.blk)
+    check_invariants(ids, plan, al)
+    assert len(plan["replicas"]) > 0
+
+
+def test_balanced_routing_is_textbook_align_sort():
+    """With every rank loaded exactly S*K there are no replicas, and each
+    rank's layout is the stable counting sort of its pairs by expert, padded
+    per expert to the block (the classic MoE align & sort)."""
+    rng = np.random.default_rng(3)
+    E, R, S, K, blk = 12, 3, 6, 2, 4
+    nh = E // R
+    # S tokens per home rank, each choosing K of that rank's experts, then
+    # shuffled so that every source rank mixes destinations: L_r = S*K exactly
+    rows = [rng.choice(np.arange(r * nh, (r + 1) * nh), K, replace=False)
+            for r in range(R) for _ in range(S)]
+    ids = np.stack(rows)[rng.permutation(R * S)]
+    _, plan, al = _run(ids, E, R, S, K, 1, blk)
+    assert plan["replicas"] == []
+    C = plan["C"]
+    flat = ids.reshape(-1)
+    for r in range(R):
+        mine = np.nonzero(flat // nh == r)[0]
+        order = mine[np.argsort(flat[mine], kind="stable")]
+        layout = []
+        for e in range(r * nh, (r + 1) * nh):
+            grp = order[flat[order] == e].tolist()
+            layout += grp + [len(flat)] * (-len(grp) % blk)
+        got = al["sorted_ids"][r * C: r * C + len(layout)].tolist()
+        assert got == layout
+        assert plan["n_rows_padded"][r] == len(layout)
+
+
+def _tiny_cases():
+    """Small routings (P <= 8) spanning overflow, deficit and fallback cases."""
+    cases = []
+    rng = np.random.default_rng(11)
+    for _ in range(40):
+        R = int(rng.choice([2, 3, 4]))
+        nh = int(rng.choice([1, 2]))
+        E = R * nh
+        K = int(rng.integers(1, min(E, 2) + 1))
+        S = max(1, 8 // (R * K))
+        S = int(rng.integers(1, S + 1))
+        skew = rng.permutation(E)
+        ids = []
+        for _t in range(R * S):
+            p = np.exp(-0.9 * skew)
+            ids.append(list(rng.choice(E, K, replace=False, p=p / p.sum())))
+        cases.append((np.array(ids), E, R, S, K))
+    return cases
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_brute_force_enumeration_agrees(case):
+    ids, E, R, S, K = _tiny_cases()[case]
+    _, plan, al = _run(ids, E, R, S, K, B=1, blk=1)
+    plans = bf.rule_conforming_plans(ids.tolist(), E, R, S)
+    # (i) the rule admits exactly one assignment, the oracle's
+    assert len(plans) == 1
+    C = plan["C"]
+    assert tuple(int(s) // C for s in al["slot"]) == plans[0]
+    reps = bf.replicas_of(plans[0], ids.tolist(), E, R)
+    assert reps == {(rp["expert"], rp["rank"]) for rp in plan["replicas"]}
+    for r in range(R):
+        assert len([x for x in reps if x[1] == r]) == plan["n_slots"][r] + plan["n_remote"][r]
+    # (ii) bound: brute-force minimum <= oracle replicas
+    assert bf.min_replicas(ids.tolist(), E, R, S) <= len(plan["replicas"])
+
+
+def test_capacity_formula_bounds_every_plan():
+    for name in ("tiny", "dsv3", "wideep", "kimi", "decode1", "decode16", "decode128"):
+        w = WORKLOADS[name]
+        C = oracle.capacity(w.E, w.K, w.S, w.blk)
+        assert C % w.blk == 0
+        assert C >= w.SK + min(w.E, w.SK) * (w.blk - 1)
+    assert oracle.capacity(256, 8, 4096, 128) == 65280
+    assert oracle.capacity(384, 8, 8192, 128) == 114304
+    assert oracle.capacity(256, 8, 512, 64) == 20224

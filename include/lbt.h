@@ -1,0 +1,233 @@
+/*
+ * lbt.h -- C ABI of the load-balanced MoE token path on one MI355X (gfx950).
+ *
+ * The path: router top-K -> per-expert token histogram -> online
+ * redundant-expert balancing plan giving every (virtual) rank exactly S*K
+ * token slots -> block-aligned sort (MoE Align & Sort) -> zero-copy dispatch
+ * into static per-rank buffers -> inverse combine.  All R expert-parallel
+ * ranks are logical partitions of one device buffer.
+ *
+ * Sources (page title, then section):
+ *   [MoonEP-GR] TWO DOTS, "MoonEP: πώς η εξισορρόπηση των AI experts αλλάζει
+ *               την υποδομή των MoE μοντέλων"
+ *   [MoonEP-FR] hamidun.com, "Moonshot AI открыла код MoonEP ..."
+ *   [UltraEP]   remio.ai, "Xiaohongshuと北京大学がUltraEPを発表、静的MoE負荷分散に挑戦"
+ *   [AlignSort] 新智元 article on SGLang's MoE Align & Sort kernel
+ *
+ * Conventions shared by every call
+ *   - Every data pointer is a DEVICE pointer owned by the caller; the
+ *     library allocates nothing and keeps no state between calls.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream) and never synchronises the host.
+ *   - Arguments are checked on the host: a call returns LBT_OK (0) or a
+ *     negative LBT_E* code and then launches nothing.  LBT_EHIP reports a
+ *     failed launch.  Data-dependent problems (inconsistent counts, an id
+ *     out of range, a rank needing more rows than the capacity) are reported
+ *     through the device status word (LBT_ST_* bits) that plan_balance
+ *     writes and align_sort / histogram OR into; the caller reads it when it
+ *     wants to.
+ *   - Sizes of every buffer come from lbt_query_sizes().
+ *   - Integer outputs are bit-for-bit deterministic (no order-dependent
+ *     atomics feed them).
+ *
+ * Notation: N = R*S tokens, P = N*K (token, expert) pairs, flat pair index
+ * f = t*K + k, SK = S*K slots per rank, E/R home experts per rank (rank r
+ * owns experts [r*E/R, (r+1)*E/R)), token t comes from source rank t / S,
+ * C = static rows per rank of the receive buffer.
+ */
+#ifndef LBT_H
+#define LBT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LBT_VERSION 1
+
+/* return codes */
+#define LBT_OK 0
+#define LBT_EINVAL (-1)      /* bad dimension, null or misaligned pointer */
+#define LBT_EHIP (-2)        /* a kernel launch failed */
+#define LBT_EUNSUPPORTED (-3)/* shape outside the supported limits below */
+
+/* device status bits */
+#define LBT_ST_BADCOUNT 1    /* the load matrix does not sum to R*S*K */
+#define LBT_ST_CAPACITY 2    /* a rank needs more than C rows; pairs that do not fit get slot -1 */
+#define LBT_ST_BADID 4       /* an expert id outside [0, E) was skipped */
+#define LBT_ST_DUPID 8       /* a token names the same expert twice */
+
+/* gate score function */
+#define LBT_SOFTMAX 0
+#define LBT_SIGMOID 1
+
+/* combine output type */
+#define LBT_Y_F32 0
+#define LBT_Y_BF16 1
+
+/* Supported limits: 1 <= R <= E <= 512, E % R == 0, 1 <= K <= min(E, 64),
+ * S >= 0, H >= 8 with H % 8 == 0, B >= 0, 1 <= blk <= 1024, cap % blk == 0,
+ * R*C and P below 2^31. */
+typedef struct lbt_shape {
+  int32_t E;        /* routed experts */
+  int32_t K;        /* experts per token */
+  int32_t R;        /* expert-parallel ranks (logical partitions) */
+  int32_t S;        /* tokens per rank */
+  int32_t H;        /* hidden size (bf16 elements per row) */
+  int32_t B;        /* prefetch slots per rank (weight rows E..E+B-1) */
+  int32_t blk;      /* alignment block of the grouped GEMM */
+  int32_t score_fn; /* LBT_SOFTMAX or LBT_SIGMOID */
+  int32_t renorm;   /* 1: gates renormalised over the K chosen */
+  int32_t cap;      /* rows per rank of recv; 0 = worst case (always enough) */
+} lbt_shape;
+
+/* Sizes (elements unless stated) and plan-blob word offsets. */
+typedef struct lbt_sizes {
+  int64_t N, P, SK;
+  int64_t C;              /* rows per rank of recv / out */
+  int64_t n_blocks;       /* C / blk blocks per rank */
+  int64_t tile_tokens;    /* tokens per histogram tile (tiles never cross ranks) */
+  int64_t tiles_per_rank; /* ceil(S / tile_tokens) */
+  int64_t n_tiles;        /* R * tiles_per_rank */
+  int64_t work_words;     /* int32 words of the route/histogram workspace */
+  int64_t max_seg;        /* segment-table entries per rank: E/R + min(E - E/R, SK) */
+  int64_t max_pieces;     /* replica-segment table entries: E + R */
+  int64_t plan_words;     /* int32 words of the plan blob */
+  /* plan blob layout: word offsets of each int32 field */
+  int64_t off_hdr;        /* [16] see LBT_HDR_* */
+  int64_t off_T;          /* [E]  T_e = pairs routed to expert e */
+  int64_t off_h;          /* [E]  pairs of e kept on its home rank */
+  int64_t off_O;          /* [E]  exclusive prefix of the overflow o_e = T_e - h_e */
+  int64_t off_home_row;   /* [E]  padded start row of e's home segment */
+  int64_t off_L;          /* [R]  L_r = load of rank r's home experts */
+  int64_t off_def;        /* [R]  def_r = S*K - min(L_r, S*K) */
+  int64_t off_D;          /* [R+1] exclusive prefix of def_r (D[R] = total) */
+  int64_t off_n_seg;      /* [R]  used segment-table entries: E/R + replicas */
+  int64_t off_n_rows_padded; /* [R] padded rows used by rank r (<= C) */
+  int64_t off_n_slots;    /* [R]  replicas held in prefetch slots (<= B) */
+  int64_t off_n_remote;   /* [R]  replicas read from their home rank */
+  int64_t off_seg_expert; /* [R][max_seg] logical expert, -1 when unused */
+  int64_t off_seg_wrow;   /* [R][max_seg] weight row ([E+B] pool), -1 when unused */
+  int64_t off_seg_count;  /* [R][max_seg] real rows, 0 when unused */
+  int64_t off_seg_start;  /* [R][max_seg+1] padded starts = cu_seqlens; unused
+                             entries and entry max_seg hold n_rows_padded[r] */
+  int64_t off_piece_expert; /* [max_pieces] replica segments in line order */
+  int64_t off_piece_rank;   /*   destination rank d */
+  int64_t off_piece_count;  /*   pairs */
+  int64_t off_piece_line;   /*   start on the shared overflow/deficit line */
+  int64_t off_piece_row;    /*   padded start row on rank d */
+} lbt_sizes;
+
+/* plan header words */
+#define LBT_HDR_N_PIECES 0
+#define LBT_HDR_MAX_T 1       /* max_e T_e  (max_vio = MAX_T*E/P - 1) */
+#define LBT_HDR_MAX_L 2       /* max_r L_r  (rank imbalance = MAX_L/SK - 1) */
+#define LBT_HDR_TOTAL_OVERFLOW 3
+#define LBT_HDR_N_DEFICIT_RANKS 4
+#define LBT_HDR_N_OVERFLOW_RANKS 5
+#define LBT_HDR_N_OVERFLOW_EXPERTS 6
+#define LBT_HDR_STATUS 7      /* LBT_ST_* bits raised by the plan */
+#define LBT_HDR_P 8           /* sum of the load matrix */
+#define LBT_HDR_WORDS 16
+
+/* Fill *out for shape *s.  Pure host function.  LBT_EINVAL/LBT_EUNSUPPORTED
+ * when the shape is outside the limits above. */
+int lbt_query_sizes(const lbt_shape* s, lbt_sizes* out);
+
+/* Router top-K and the per-tile expert histogram (one launch), then the
+ * per-rank load matrix and per-tile prefix offsets (a second launch).
+ * [AlignSort] (the MoE layer gates each token to its Top-K experts by gate
+ * score, DeepSeek's gating bias steering the choice); [UltraEP] section
+ * "その仕組みは高速なエキスパート複製に依存する" (the exact post-routing load
+ * matrix, per source rank and logical expert).
+ *   logits   [N, E] fp32 row-major, finite (no NaN)
+ *   sel_bias [E] fp32 or NULL; the key is the fp32 sum logits + sel_bias
+ *   ids      [N, K] int32 out: the K largest keys, descending, ties to the
+ *            lower expert index (-0.0 ties +0.0)
+ *   gates    [N, K] fp32 out: sigmoid(logit) or softmax over the E raw
+ *            logits (the bias only steers selection), evaluated in fp64 and
+ *            rounded once; optionally renormalised over the K chosen
+ *   counts   [R, E] int32 out: the load matrix
+ *   work     [work_words] int32 scratch the align step reads back; keep it
+ *            alive and unmodified until lbt_align_sort has run */
+int lbt_route_topk(const lbt_shape* s, const float* logits, const float* sel_bias,
+                   int32_t* ids, float* gates, int32_t* counts, int32_t* work, void* stream);
+
+/* The histogram step alone, for expert ids the caller already has (each
+ * token's K ids distinct, in [0, E)).  Same outputs as lbt_route_topk's
+ * counts/work.  Ids out of range are skipped and raise LBT_ST_BADID in
+ * *status when status is not NULL. */
+int lbt_histogram(const lbt_shape* s, const int32_t* ids, int32_t* counts, int32_t* work,
+                  int32_t* status, void* stream);
+
+/* Balancing plan from the load matrix; one workgroup, no host round trip.
+ * [MoonEP-GR] sections "Η βασική υπόσχεση του MoonEP: σταθερό φορτίο S × K"
+ * and "Το memory contract ..."; [UltraEP] "その仕組みは...".  Rule: rank r
+ * keeps min(L_r, S*K) pairs -- the first ones of its home stream (experts
+ * ascending, pairs by ascending f); overflow segments (experts ascending)
+ * fill deficit ranks in ascending order; every non-empty overlap is one
+ * replica segment; on its rank the first B replica segments take prefetch
+ * slots (weight rows E..E+B-1), later ones are remote (weight row = expert,
+ * read from home).  Segment table of rank r: its E/R home experts, then its
+ * replicas in line order; counts padded to blk; starts = cu_seqlens.
+ *   counts [R, E] int32 in
+ *   plan   [plan_words] int32 out, layout in lbt_sizes (every word written)
+ *   status int32 out (may be NULL): set to the plan's LBT_ST_* bits */
+int lbt_plan_balance(const lbt_shape* s, const int32_t* counts, int32_t* plan, int32_t* status,
+                     void* stream);
+
+/* Block-aligned sort: destination row of every pair.  [AlignSort] (pairs
+ * sorted by expert, each expert's share padded to the GEMM block; the
+ * permutation records source -> destination); [UltraEP] (per-token
+ * destinations by lookup against cumulative quotas).  For pair f with
+ * expert e and q = #{f' < f : ids[f'] = e}: q < h_e -> home rank of e, row
+ * home_row[e] + q; else o = O_e + q - h_e lies in one replica segment
+ * (d, line, row) -> rank d, row + o - line.
+ *   ids        [N, K] int32 in (the ids the histogram counted)
+ *   work       the workspace filled by lbt_route_topk / lbt_histogram
+ *   plan       the blob from lbt_plan_balance
+ *   slot       [P] int32 out: d*C + row, or -1 if it did not fit the capacity
+ *   sorted_ids [R*C] int32 out: row -> f; padding rows below a rank's
+ *              n_rows_padded hold P; rows at or past it are not written
+ *   block_wrow, block_expert [R, C/blk] int32 out: weight row / expert of
+ *              the segment covering each block, -1 past n_rows_padded
+ *   status     int32 in/out (may be NULL): LBT_ST_* bits ORed in */
+int lbt_align_sort(const lbt_shape* s, const int32_t* ids, const int32_t* work,
+                   const int32_t* plan, int32_t* slot, int32_t* sorted_ids,
+                   int32_t* block_wrow, int32_t* block_expert, int32_t* status, void* stream);
+
+/* Zero-copy dispatch: recv[slot[f]] = x[f / K], a bit copy of each bf16
+ * row, straight into its final expert-grouped row of the static per-rank
+ * buffer ([MoonEP-GR] "Online planning, zero copy και στατικά σχήματα").
+ * Padding rows and rows past n_rows_padded are not touched.  Views into
+ * recv stay valid until the next dispatch into the same buffer.
+ *   x    [N, H] bf16 bits, 16-byte aligned
+ *   slot [P] int32 (entries < 0 skipped)
+ *   recv [R*C, H] bf16 bits, 16-byte aligned */
+int lbt_dispatch(const lbt_shape* s, const uint16_t* x, const int32_t* slot, uint16_t* recv,
+                 void* stream);
+
+/* Combine, the inverse of dispatch: y[t] = sum_k gates[t,k] * out[slot[t*K+k]]
+ * with fp32 accumulation in ascending k (fused multiply-add), from the
+ * expert outputs laid out like recv ([MoonEP-GR]: combine returns expert
+ * results to the source tokens).
+ *   out   [R*C, H] bf16 bits, 16-byte aligned
+ *   slot  [P] int32 (entries < 0 contribute nothing)
+ *   gates [N, K] fp32
+ *   y     [N, H] fp32 (LBT_Y_F32) or bf16 bits rounded to nearest even
+ *         (LBT_Y_BF16), 16-byte aligned */
+int lbt_combine(const lbt_shape* s, const uint16_t* out, const int32_t* slot, const float* gates,
+                int32_t y_dtype, void* y, void* stream);
+
+/* Text for a return code. */
+const char* lbt_strerror(int code);
+
+/* LBT_VERSION of the built library. */
+int lbt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LBT_H */

@@ -1,0 +1,172 @@
+// MoE Align & Sort under the balancing plan: the destination row of every
+// (token, expert) pair, the inverse map, and the per-block weight-row table.
+//
+// [AlignSort]: pairs are sorted by expert id with each expert's share padded
+// to the grouped GEMM's block; the permutation records source -> target.
+// The prior kernel there computes aligned offsets in one block, then
+// scatters; here the offsets come from the plan and the per-tile prefix
+// counts, so every tile of 128 tokens works independently.
+// [UltraEP] section "その仕組みは高速なエキスパート複製に依存する": per-token
+// destinations are a local lookup against cumulative quotas.
+//
+// Stable rank of a pair inside its expert: q = (pairs of e in earlier tiles,
+// from the column scan) + (pairs of e in earlier 32-token sub-tiles of this
+// tile) + popcount of the sub-tile's bit mask of tokens holding e below this
+// token.  A token holds K distinct experts, so ranks by token order equal
+// ranks by flat index f = t*K + k.
+#include "lbt_internal.h"
+
+namespace lbt {
+
+constexpr int kAlignThreads = kTileTokens;       // one thread per token
+constexpr int kBlockWaves = kAlignThreads / kWave; // blocks handled per workgroup
+
+__device__ void align_blocks(const int32_t* __restrict__ plan, const Dims& d,
+                             int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_wrow,
+                             int32_t* __restrict__ block_expert) {
+  const PlanLayout& pl = d.pl;
+  const long long gb = (long long)(blockIdx.x - d.n_tiles) * kBlockWaves + wave_id();
+  if (gb >= (long long)d.R * d.n_blocks) return;
+  const int r = (int)(gb / d.n_blocks);
+  const int b = (int)(gb - (long long)r * d.n_blocks);
+  const int lane = lane_id();
+  const int nrp = plan[pl.n_rows_padded + r];
+  const int row0 = b * d.blk;
+  if (row0 >= nrp) {
+    if (lane == 0) {
+      block_wrow[gb] = -1;
+      block_expert[gb] = -1;
+    }
+    return;
+  }
+  const int ns = plan[pl.n_seg + r];
+  const int32_t* starts = plan + pl.seg_start + (long long)r * (pl.max_seg + 1);
+  int lo = 0, hi = ns;  // last segment starting at or before row0
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (starts[mid] <= row0) lo = mid + 1; else hi = mid;
+  }
+  const int s = lo - 1;
+  const long long si = (long long)r * pl.max_seg + s;
+  if (lane == 0) {
+    block_wrow[gb] = plan[pl.seg_wrow + si];
+    block_expert[gb] = plan[pl.seg_expert + si];
+  }
+  const int real_end = starts[s] + plan[pl.seg_count + si];
+  const int sentinel = (int)d.P;
+  for (int row = max(row0, real_end) + lane; row < row0 + d.blk; row += kWave)
+    sorted_ids[(long long)r * d.C + row] = sentinel;
+}
+
+__global__ __launch_bounds__(kAlignThreads) void k_align(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ work,
+    const int32_t* __restrict__ plan, Dims d, int32_t* __restrict__ slot,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_wrow,
+    int32_t* __restrict__ block_expert, int32_t* __restrict__ status) {
+  if ((int)blockIdx.x >= d.n_tiles) {
+    align_blocks(plan, d, sorted_ids, block_wrow, block_expert);
+    return;
+  }
+  __shared__ int sH[kMaxE], sO[kMaxE], sHome[kMaxE], sBase[kMaxE];
+  __shared__ uint32_t sMask[kSubTiles][kMaxE];
+  __shared__ int sSub[kSubTiles][kMaxE];
+  __shared__ int sPl[kMaxPieces], sPd[kMaxPieces], sPr[kMaxPieces], sPe[kMaxPieces];
+
+  const PlanLayout& pl = d.pl;
+  const int E = d.E, K = d.K, C = d.C, nh = d.nh;
+  const int tile = blockIdx.x;
+  const int r = tile / d.tpr, j = tile - r * d.tpr;
+  const int t0 = r * d.S + j * kTileTokens;
+  const int len = min(kTileTokens, d.S - j * kTileTokens);
+  const int nP = plan[pl.hdr + LBT_HDR_N_PIECES];
+  const int totOv = plan[pl.hdr + LBT_HDR_TOTAL_OVERFLOW];
+  const int32_t* tbase = work + work_tile_base(d) + (long long)tile * E;
+  const int tid = threadIdx.x;
+
+  for (int e = tid; e < E; e += kAlignThreads) {
+    sH[e] = plan[pl.h + e];
+    sO[e] = plan[pl.O + e];
+    sHome[e] = plan[pl.home_row + e];
+    sBase[e] = tbase[e];
+#pragma unroll
+    for (int s = 0; s < kSubTiles; ++s) sMask[s][e] = 0u;
+  }
+  for (int g = tid; g < nP; g += kAlignThreads) {
+    sPl[g] = plan[pl.piece_line + g];
+    sPd[g] = plan[pl.piece_rank + g];
+    sPr[g] = plan[pl.piece_row + g];
+    sPe[g] = plan[pl.piece_expert + g];
+  }
+  __syncthreads();
+
+  int flags = 0;
+  const int sub = tid / kSubTokens;
+  const uint32_t bit = 1u << (tid % kSubTokens);
+  const long long t = (long long)t0 + tid;
+  if (tid < len) {
+    for (int k = 0; k < K; ++k) {
+      const int e = ids[t * K + k];
+      if (e < 0 || e >= E) continue;
+      const uint32_t old = atomicOr(&sMask[sub][e], bit);
+      if (old & bit) flags |= LBT_ST_DUPID;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kAlignThreads) {
+    int run = 0;
+#pragma unroll
+    for (int s = 0; s < kSubTiles; ++s) {
+      sSub[s][e] = run;
+      run += __popc(sMask[s][e]);
+    }
+  }
+  __syncthreads();
+
+  if (tid < len) {
+    for (int k = 0; k < K; ++k) {
+      const long long f = t * K + k;
+      const int e = ids[f];
+      if (e < 0 || e >= E) {
+        flags |= LBT_ST_BADID;
+        slot[f] = -1;
+        continue;
+      }
+      const int q = sBase[e] + sSub[sub][e] + __popc(sMask[sub][e] & (bit - 1u));
+      const int h = sH[e];
+      int dd, row;
+      bool ok = true;
+      if (q < h) {
+        dd = e / nh;
+        row = sHome[e] + q;
+      } else {
+        const int o = sO[e] + (q - h);
+        const int g = upper_bound(sPl, nP, o) - 1;
+        ok = o < totOv && g >= 0 && sPe[g] == e;
+        dd = ok ? sPd[g] : 0;
+        row = ok ? sPr[g] + (o - sPl[g]) : 0;
+      }
+      if (!ok || row >= C) {
+        flags |= LBT_ST_CAPACITY;
+        slot[f] = -1;
+        continue;
+      }
+      const long long dst = (long long)dd * C + row;
+      slot[f] = (int)dst;
+      sorted_ids[dst] = (int)f;
+    }
+  }
+  if (flags && status != nullptr) atomicOr(status, flags);
+}
+
+hipError_t launch_align(const Dims& d, const int32_t* ids, const int32_t* work, const int32_t* plan,
+                        int32_t* slot, int32_t* sorted_ids, int32_t* block_wrow,
+                        int32_t* block_expert, int32_t* status, hipStream_t st) {
+  const long long nblk = (long long)d.R * d.n_blocks;
+  const long long grid = d.n_tiles + (nblk + kBlockWaves - 1) / kBlockWaves;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_align, dim3((unsigned)grid), dim3(kAlignThreads), 0, st, ids, work, plan, d,
+                     slot, sorted_ids, block_wrow, block_expert, status);
+  return hipGetLastError();
+}
+
+}  // namespace lbt

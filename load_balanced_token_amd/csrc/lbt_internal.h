@@ -1,0 +1,145 @@
+// Internal declarations of the HIP library behind include/lbt.h (gfx950,
+// wave64).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lbt.h"
+
+namespace lbt {
+
+constexpr int kWave = 64;
+constexpr int kTileTokens = 128;   // tokens per histogram tile
+constexpr int kSubTokens = 32;     // tokens per bit-mask sub-tile (one u32)
+constexpr int kSubTiles = kTileTokens / kSubTokens;
+constexpr int kMaxE = 512;
+constexpr int kMaxR = 512;
+constexpr int kMaxPieces = kMaxE + kMaxR;
+constexpr int kMaxK = 64;
+
+// Plan blob word offsets (mirrors lbt_sizes, 32-bit for the device).
+struct PlanLayout {
+  int E, R, max_seg, max_pieces;
+  int hdr, T, h, O, home_row, L, def, D, n_seg, n_rows_padded, n_slots, n_remote;
+  int seg_expert, seg_wrow, seg_count, seg_start;
+  int piece_expert, piece_rank, piece_count, piece_line, piece_row;
+  int total;
+};
+
+// Everything the kernels need about a shape, derived once on the host.
+struct Dims {
+  int E, K, R, S, H, B, blk, score_fn, renorm;
+  int nh;        // E / R home experts per rank
+  int N;         // R * S tokens
+  long long P;   // N * K pairs
+  int SK;        // S * K
+  int C;         // rows per rank
+  int n_blocks;  // C / blk
+  int tpr;       // tiles per rank
+  int n_tiles;   // R * tpr
+  PlanLayout pl;
+};
+
+// Host-side helpers (api.hip).
+int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z);
+
+// Launchers (one per kernel family).  Return hipError_t of the launch.
+hipError_t launch_route(const Dims& d, const float* logits, const float* bias, int32_t* ids,
+                        float* gates, int32_t* work, hipStream_t st);
+hipError_t launch_histogram(const Dims& d, const int32_t* ids, int32_t* work, int32_t* status,
+                            hipStream_t st);
+hipError_t launch_tile_scan(const Dims& d, int32_t* work, int32_t* counts, hipStream_t st);
+hipError_t launch_plan(const Dims& d, const int32_t* counts, int32_t* plan, int32_t* status,
+                       hipStream_t st);
+hipError_t launch_align(const Dims& d, const int32_t* ids, const int32_t* work, const int32_t* plan,
+                        int32_t* slot, int32_t* sorted_ids, int32_t* block_wrow,
+                        int32_t* block_expert, int32_t* status, hipStream_t st);
+hipError_t launch_dispatch(const Dims& d, const uint16_t* x, const int32_t* slot, uint16_t* recv,
+                           hipStream_t st);
+hipError_t launch_combine(const Dims& d, const uint16_t* out, const int32_t* slot,
+                          const float* gates, int y_dtype, void* y, hipStream_t st);
+
+// Workspace layout: tile_counts [E][n_tiles] (expert-major, for the column
+// scan) followed by tile_base [n_tiles][E] (tile-major, for the align step).
+__host__ __device__ inline long long work_tile_counts(const Dims&) { return 0; }
+__host__ __device__ inline long long work_tile_base(const Dims& d) {
+  return (long long)d.E * d.n_tiles;
+}
+
+// ---- device helpers -------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+
+// In-place exclusive prefix sum of arr[0..n) in LDS by the whole workgroup
+// (blockDim.x = NT threads, n <= IPT * NT); arr[n] receives the total, which
+// is also returned.  tmp needs NT/64 + 1 ints.  Contains barriers: every
+// thread of the workgroup must call it.
+template <int NT, int IPT>
+__device__ int block_excl_scan(int* arr, int n, int* tmp) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x;
+  int v[IPT];
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int idx = tid * IPT + i;
+    v[i] = idx < n ? arr[idx] : 0;
+    local += v[i];
+  }
+  const int incl = wave_incl_scan(local);
+  if (lane_id() == kWave - 1) tmp[wave_id()] = incl;
+  __syncthreads();
+  if (tid < kWave) {
+    const int w = tid < NW ? tmp[tid] : 0;
+    const int wi = wave_incl_scan(w);
+    if (tid < NW) tmp[tid] = wi - w;
+    if (tid == NW - 1) tmp[NW] = wi;
+  }
+  __syncthreads();
+  int run = incl - local + tmp[wave_id()];
+  const int total = tmp[NW];
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int idx = tid * IPT + i;
+    if (idx < n) arr[idx] = run;
+    run += v[i];
+  }
+  if (tid == 0) arr[n] = total;
+  __syncthreads();
+  return total;
+}
+
+// First index in a[0..n) whose value is > x (a non-decreasing).
+__device__ __forceinline__ int upper_bound(const int* a, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] <= x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace lbt

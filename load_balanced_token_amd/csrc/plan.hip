@@ -1,0 +1,231 @@
+// The online balancing plan: one workgroup turns the load matrix into the
+// replica segments and per-rank segment tables, entirely on the device.
+//
+// [MoonEP-GR] sections "Η βασική υπόσχεση του MoonEP: σταθερό φορτίο S × K"
+// (each rank receives exactly S*K; a few temporary expert copies, planned
+// online from the current router output) and "Το memory contract ..."
+// (weight rows 0..E-1 are the ranks' experts, E..E+B-1 local prefetch
+// slots, the grouped GEMM finds experts by row index and consumes the
+// planner's cu_seqlens; replicas beyond the slots are read from home).
+// [UltraEP] section "その仕組みは高速なエキスパート複製に依存する" (the
+// planner runs fully on the GPU, no host round trip inside a layer;
+// replicas exist only when given work).
+//
+// The rule: rank r keeps min(L_r, S*K) of its pairs, the first ones of its
+// home stream; the overflow of every expert (experts ascending) and the
+// deficit of every rank (ranks ascending) are laid on one line, and each
+// non-empty overlap is a replica segment ("piece").  All steps are LDS
+// prefix sums and binary searches over E <= 512 experts and R <= 512 ranks.
+#include "lbt_internal.h"
+
+namespace lbt {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / kWave;
+
+__device__ __forceinline__ int pad_to(int c, int blk) { return ((c + blk - 1) / blk) * blk; }
+
+__global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict__ counts, Dims d,
+                                                      int32_t* __restrict__ plan,
+                                                      int32_t* __restrict__ status) {
+  __shared__ int sT[kMaxE + 1];      // T_e
+  __shared__ int sX[kMaxE + 1];      // exclusive prefix of T over e
+  __shared__ int sH[kMaxE];          // h_e
+  __shared__ int sO[kMaxE + 1];      // o_e, then exclusive prefix O_e
+  __shared__ int sNp[kMaxE + 1];     // pieces of expert e, then exclusive prefix
+  __shared__ int sDlo[kMaxE];        // compact index of e's first deficit rank
+  __shared__ int sL[kMaxR];          // L_r
+  __shared__ int sDef[kMaxR];        // def_r
+  __shared__ int sD[kMaxR + 1];      // exclusive prefix D_r
+  __shared__ int sCidx[kMaxR + 1];   // compact index among deficit ranks
+  __shared__ int sDl[kMaxR];         // compact index -> rank
+  __shared__ int sRep[kMaxR + 1];    // replicas per rank, then first piece of rank
+  __shared__ int sPe[kMaxPieces], sPd[kMaxPieces], sPc[kMaxPieces], sPl[kMaxPieces],
+      sPj[kMaxPieces];
+  __shared__ int sF[kMaxE + kMaxPieces + 1];  // flat segment padded lengths -> starts
+  __shared__ int tmp[kPlanWaves + 1];
+  __shared__ int sStat[6];  // max_T, max_L, over ranks, over experts, status, -
+
+  const int tid = threadIdx.x;
+  const int E = d.E, R = d.R, nh = d.nh, SK = d.SK, B = d.B, blk = d.blk, C = d.C;
+  const PlanLayout pl = d.pl;
+  const int ms = pl.max_seg;
+
+  if (tid < 6) sStat[tid] = 0;
+  for (int e = tid; e < E; e += kPlanThreads) {
+    int s = 0;
+    for (int r = 0; r < R; ++r) s += counts[(long long)r * E + e];
+    sT[e] = s;
+    sX[e] = s;
+  }
+  __syncthreads();
+  const int Ptot = block_excl_scan<kPlanThreads, 1>(sX, E, tmp);
+  const bool consistent = (long long)Ptot == (long long)R * SK;
+
+  // home keep / overflow per expert; load and deficit per rank
+  for (int e = tid; e < E; e += kPlanThreads) {
+    const int r = e / nh;
+    const int T = sT[e];
+    const int Pe = sX[e] - sX[r * nh];                 // position in r's home stream
+    const int h = consistent ? min(max(SK - Pe, 0), T) : 0;
+    sH[e] = h;
+    sO[e] = consistent ? T - h : 0;
+    atomicMax(&sStat[0], T);
+    if (T - h > 0) atomicAdd(&sStat[3], 1);
+  }
+  for (int r = tid; r < R; r += kPlanThreads) {
+    const int L = sX[(r + 1) * nh] - sX[r * nh];
+    const int def = consistent ? SK - min(L, SK) : 0;
+    sL[r] = L;
+    sDef[r] = def;
+    sD[r] = def;
+    sCidx[r] = def > 0;
+    sRep[r] = 0;
+    atomicMax(&sStat[1], L);
+    if (L > SK) atomicAdd(&sStat[2], 1);
+  }
+  __syncthreads();
+  const int totOv = block_excl_scan<kPlanThreads, 1>(sO, E, tmp);
+  block_excl_scan<kPlanThreads, 1>(sD, R, tmp);
+  block_excl_scan<kPlanThreads, 1>(sCidx, R, tmp);
+
+  // pieces per overflowing expert: the deficit ranks its interval overlaps
+  for (int r = tid; r < R; r += kPlanThreads)
+    if (sDef[r] > 0) sDl[sCidx[r]] = r;
+  for (int e = tid; e < E; e += kPlanThreads) {
+    const int o = sT[e] - sH[e];
+    int np = 0;
+    if (consistent && o > 0) {
+      const int Oe = sO[e];
+      // last rank with D <= x is the deficit rank holding x (empty
+      // intervals of ranks without deficit never end up last)
+      const int dlo = upper_bound(sD, R, Oe) - 1;
+      const int dhi = upper_bound(sD, R, Oe + o - 1) - 1;
+      np = sCidx[dhi] - sCidx[dlo] + 1;
+      sDlo[e] = sCidx[dlo];
+    }
+    sNp[e] = np;
+  }
+  __syncthreads();
+  const int nP = block_excl_scan<kPlanThreads, 1>(sNp, E, tmp);
+
+  for (int g = tid; g < nP; g += kPlanThreads) {
+    const int e = upper_bound(sNp, E, g) - 1;
+    const int jj = g - sNp[e];
+    const int dd = sDl[sDlo[e] + jj];
+    const int Oe = sO[e], o = sT[e] - sH[e];
+    const int lo = max(Oe, sD[dd]);
+    const int hi = min(Oe + o, sD[dd] + sDef[dd]);
+    sPe[g] = e;
+    sPd[g] = dd;
+    sPc[g] = hi - lo;
+    sPl[g] = lo;
+    atomicAdd(&sRep[dd], 1);
+  }
+  __syncthreads();
+  block_excl_scan<kPlanThreads, 1>(sRep, R, tmp);   // first piece of each rank
+
+  // flat segment list: rank r's E/R home experts, then its pieces
+  for (int g = tid; g < nP; g += kPlanThreads) {
+    const int dd = sPd[g];
+    const int jj = g - sRep[dd];
+    sPj[g] = jj;
+    sF[dd * nh + sRep[dd] + nh + jj] = pad_to(sPc[g], blk);
+  }
+  for (int e = tid; e < E; e += kPlanThreads) {
+    const int r = e / nh;
+    sF[r * nh + sRep[r] + (e - r * nh)] = pad_to(sH[e], blk);
+  }
+  __syncthreads();
+  block_excl_scan<kPlanThreads, 2>(sF, E + nP, tmp);
+  // rank r's flat entries are [fb(r), fb(r+1)) with fb(r) = r*nh + sRep[r]
+
+  int32_t* P = plan;
+  for (int e = tid; e < E; e += kPlanThreads) {
+    const int r = e / nh;
+    const int fb = r * nh + sRep[r];
+    P[pl.T + e] = sT[e];
+    P[pl.h + e] = sH[e];
+    P[pl.O + e] = sO[e];
+    P[pl.home_row + e] = sF[fb + (e - r * nh)] - sF[fb];
+  }
+  for (int r = tid; r < R; r += kPlanThreads) {
+    const int fb = r * nh + sRep[r];
+    const int fe = (r + 1) * nh + sRep[r + 1];
+    const int nrep = sRep[r + 1] - sRep[r];
+    const int nrp = sF[fe] - sF[fb];
+    P[pl.L + r] = sL[r];
+    P[pl.def + r] = sDef[r];
+    P[pl.D + r] = sD[r];
+    P[pl.n_seg + r] = nh + nrep;
+    P[pl.n_rows_padded + r] = nrp;
+    P[pl.n_slots + r] = min(nrep, B);
+    P[pl.n_remote + r] = nrep - min(nrep, B);
+    if (nrp > C) atomicOr(&sStat[4], LBT_ST_CAPACITY);
+  }
+  if (tid == 0) P[pl.D + R] = sD[R];
+  for (int idx = tid; idx < R * ms; idx += kPlanThreads) {
+    const int r = idx / ms, s = idx - r * ms;
+    const int nrep = sRep[r + 1] - sRep[r];
+    int ex = -1, wr = -1, cnt = 0;
+    if (s < nh) {
+      ex = r * nh + s;
+      wr = ex;
+      cnt = sH[ex];
+    } else if (s < nh + nrep) {
+      const int g = sRep[r] + (s - nh);
+      ex = sPe[g];
+      cnt = sPc[g];
+      wr = (s - nh < B) ? E + (s - nh) : ex;
+    }
+    P[pl.seg_expert + idx] = ex;
+    P[pl.seg_wrow + idx] = wr;
+    P[pl.seg_count + idx] = cnt;
+  }
+  for (int idx = tid; idx < R * (ms + 1); idx += kPlanThreads) {
+    const int r = idx / (ms + 1), s = idx - r * (ms + 1);
+    const int fb = r * nh + sRep[r];
+    const int nseg = nh + sRep[r + 1] - sRep[r];
+    const int fe = fb + nseg;
+    P[pl.seg_start + idx] = (s < nseg ? sF[fb + s] : sF[fe]) - sF[fb];
+  }
+  for (int g = tid; g < pl.max_pieces; g += kPlanThreads) {
+    int ex = -1, dd = -1, cnt = 0, line = -1, row = -1;
+    if (g < nP) {
+      ex = sPe[g];
+      dd = sPd[g];
+      cnt = sPc[g];
+      line = sPl[g];
+      const int fb = dd * nh + sRep[dd];
+      row = sF[fb + nh + sPj[g]] - sF[fb];
+    }
+    P[pl.piece_expert + g] = ex;
+    P[pl.piece_rank + g] = dd;
+    P[pl.piece_count + g] = cnt;
+    P[pl.piece_line + g] = line;
+    P[pl.piece_row + g] = row;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int st = sStat[4] | (consistent ? 0 : LBT_ST_BADCOUNT);
+    P[pl.hdr + LBT_HDR_N_PIECES] = nP;
+    P[pl.hdr + LBT_HDR_MAX_T] = sStat[0];
+    P[pl.hdr + LBT_HDR_MAX_L] = sStat[1];
+    P[pl.hdr + LBT_HDR_TOTAL_OVERFLOW] = totOv;
+    P[pl.hdr + LBT_HDR_N_DEFICIT_RANKS] = sCidx[R];
+    P[pl.hdr + LBT_HDR_N_OVERFLOW_RANKS] = sStat[2];
+    P[pl.hdr + LBT_HDR_N_OVERFLOW_EXPERTS] = sStat[3];
+    P[pl.hdr + LBT_HDR_STATUS] = st;
+    P[pl.hdr + LBT_HDR_P] = Ptot;
+    for (int i = LBT_HDR_P + 1; i < LBT_HDR_WORDS; ++i) P[pl.hdr + i] = 0;
+    if (status != nullptr) *status = st;
+  }
+}
+
+hipError_t launch_plan(const Dims& d, const int32_t* counts, int32_t* plan, int32_t* status,
+                       hipStream_t st) {
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, st, counts, d, plan, status);
+  return hipGetLastError();
+}
+
+}  // namespace lbt

@@ -1,0 +1,380 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element
+by element on the same seeded inputs.  Integer outputs must be bit-exact;
+gates within 1e-6 relative of the fp64 oracle; combine within
+1e-6 * sum_k |g * out| (fp32 accumulation of K terms)."""
+import glob
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import (WORKLOADS, router_logits, activations, activation_rows,
+                       random_expert_out, f32_to_bf16_bits)
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = sorted(glob.glob(os.path.join(os.path.dirname(__file__), "golden", "W*.json")))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# --------------------------------------------------------------------------- golden
+@pytest.mark.parametrize("path", GOLDEN, ids=[os.path.basename(p) for p in GOLDEN])
+def test_gpu_matches_hand_examples(path):
+    g = json.load(open(path))
+    sh = g["shape"]
+    import load_balanced_token_amd as lbt
+    shape = lbt.Shape(E=sh["E"], K=sh["K"], R=sh["R"], S=sh["S"], H=8, B=sh["B"], blk=sh["blk"])
+    res = gu.run_front(shape, np.array(g["logits"], np.float32))
+    assert res["ids"].tolist() == g["ids"]
+    assert res["counts"].tolist() == g["counts"]
+    pf = res["plan_fields"]
+    for key in ("T", "h", "O", "L", "D", "n_rows_padded", "n_slots", "n_remote", "home_row"):
+        assert pf[key].tolist() == g[key], key
+    assert pf["def"].tolist() == g["deficit"]
+    assert res["sizes"]["C"] == g["C"]
+    assert res["slot"].tolist() == g["slot"]
+    C = g["C"]
+    for r in range(sh["R"]):
+        for want, got in zip(g["sorted_ids"][r], res["sorted_ids"][r * C:(r + 1) * C].tolist()):
+            if want is not None:
+                assert got == want
+    assert res["block_wrow"].tolist() == g["block_wrow"]
+    assert res["block_expert"].tolist() == g["block_expert"]
+
+
+# --------------------------------------------------------------------------- configs
+FRONT_CONFIGS = ["tiny", "dsv3", "wideep", "decode1", "decode16", "decode128", "kimi"]
+
+
+@pytest.mark.parametrize("name", FRONT_CONFIGS)
+def test_route_plan_align_parity(name):
+    """Full-size route + plan + align against the oracle: ids, counts, the
+    whole plan, slot, sorted_ids and block tables bit-exact."""
+    w = WORKLOADS[name]
+    print(f"[parity] {name} E={w.E} K={w.K} R={w.R} S={w.S}", flush=True)
+    logits = router_logits(w, 0)
+    res = gu.run_front(gu.shape_of(w), logits)
+    ref = gu.run_oracle(w, logits)
+    gu.check_route(res, ref)
+    gu.check_plan(res["plan_fields"], ref["plan"], w.P)
+    gu.check_align(res, ref, w.R, res["sizes"]["C"])
+
+
+@pytest.mark.parametrize("name", ["dsv3", "decode128"])
+def test_route_plan_align_parity_more_layers(name):
+    w = WORKLOADS[name]
+    for layer in (1, 2, 3):
+        logits = router_logits(w, layer)
+        res = gu.run_front(gu.shape_of(w), logits)
+        ref = gu.run_oracle(w, logits)
+        gu.check_route(res, ref)
+        gu.check_plan(res["plan_fields"], ref["plan"], w.P)
+        gu.check_align(res, ref, w.R, res["sizes"]["C"])
+
+
+def _full_move_check(w, res, ref, x_bits, out_bits=None):
+    """Dispatch + combine with every row compared (sizes that fit the host)."""
+    t = gu.torch()
+    path = res["path"]
+    C = res["sizes"]["C"]
+    recv = t.full((w.R * C, w.H), 0x7F7F, dtype=t.int16, device="cuda")   # sentinel fill
+    x = gu.h2d(x_bits)
+    path.dispatch(x, res["dev"]["slot"], recv)
+    slot = ref["align"]["slot"]
+    recv_h = gu.d2h(recv)
+    want = oracle.dispatch(x_bits, slot, w.K, w.R, C)
+    used = np.zeros(w.R * C, bool)
+    used[slot] = True
+    assert np.array_equal(recv_h[used], want[used]), "dispatched rows differ"
+    assert (recv_h[~used] == 0x7F7F).all(), "dispatch touched rows it does not own"
+    # combine of the identity expert and of a random expert output
+    gates32 = ref["gates"].astype(np.float32)
+    for src in ("identity", "random"):
+        if src == "identity":
+            out_d, out_h = recv, want
+        else:
+            out_h = random_expert_out(w, w.R * C) if out_bits is None else out_bits
+            out_d = gu.h2d(out_h)
+        y = t.empty((w.N, w.H), dtype=t.float32, device="cuda")
+        path.combine(out_d, res["dev"]["slot"], gu.h2d(gates32), y)
+        yref, mag = oracle.combine(lambda rows: out_h[rows], slot, gates32, w.K)
+        err = np.abs(y.cpu().numpy().astype(np.float64) - yref)
+        assert (err <= gu.COMBINE_RTOL * mag + 1e-30).all(), \
+            f"combine ({src}) max err/mag {(err / np.maximum(mag, 1e-30)).max()}"
+        if src == "identity":
+            xs = oracle.bf16_to_f64(x_bits) * gates32.astype(np.float64).sum(axis=1)[:, None]
+            assert (np.abs(y.cpu().numpy() - xs) <= gu.COMBINE_RTOL * np.abs(xs) + 1e-30).all()
+    # bf16 output is the round-to-nearest-even of the fp32 accumulator
+    yb = t.empty((w.N, w.H), dtype=t.int16, device="cuda")
+    yf = t.empty((w.N, w.H), dtype=t.float32, device="cuda")
+    path.combine(recv, res["dev"]["slot"], gu.h2d(gates32), yb)
+    path.combine(recv, res["dev"]["slot"], gu.h2d(gates32), yf)
+    assert np.array_equal(gu.d2h(yb), f32_to_bf16_bits(yf.cpu().numpy()))
+
+
+@pytest.mark.parametrize("name,S", [("tiny", None), ("dsv3", 256), ("wideep", 64), ("kimi", 64)])
+def test_dispatch_combine_parity_full_rows(name, S):
+    w = WORKLOADS[name]
+    if S is not None:
+        w = w.with_(S=S)
+    print(f"[parity] move {name} S={w.S} H={w.H}", flush=True)
+    logits = router_logits(w, 0)
+    res = gu.run_front(gu.shape_of(w), logits)
+    ref = gu.run_oracle(w, logits)
+    gu.check_align(res, ref, w.R, res["sizes"]["C"])
+    _full_move_check(w, res, ref, activations(w, 0))
+
+
+@pytest.mark.parametrize("name", ["dsv3", "wideep", "kimi"])
+def test_dispatch_combine_full_size_sampled(name):
+    """Full-size dispatch + combine in the launch configuration the benchmark
+    times; the oracle recomputes sampled rows one by one."""
+    t = gu.torch()
+    w = WORKLOADS[name]
+    print(f"[parity] sampled move {name}", flush=True)
+    logits = router_logits(w, 0)
+    res = gu.run_front(gu.shape_of(w), logits)
+    ref = gu.run_oracle(w, logits)
+    gu.check_align(res, ref, w.R, res["sizes"]["C"])
+    path, C = res["path"], res["sizes"]["C"]
+    x = t.empty((w.N, w.H), dtype=t.int16, device="cuda")
+    from workloads.gen import X_CHUNK, x_chunk
+    for c in range((w.N + X_CHUNK - 1) // X_CHUNK):
+        blk = x_chunk(w, 0, c)
+        x[c * X_CHUNK: c * X_CHUNK + blk.shape[0]] = gu.h2d(blk)
+    recv = t.full((w.R * C, w.H), 0x7F7F, dtype=t.int16, device="cuda")
+    path.dispatch(x, res["dev"]["slot"], recv)
+    y = t.empty((w.N, w.H), dtype=t.float32, device="cuda")
+    gates32 = ref["gates"].astype(np.float32)
+    path.combine(recv, res["dev"]["slot"], gu.h2d(gates32), y)
+    t.cuda.synchronize()
+    rng = np.random.default_rng(123)
+    tokens = np.sort(rng.choice(w.N, size=256, replace=False))
+    xs = activation_rows(w, tokens, 0)
+    slot = ref["align"]["slot"]
+    for i, tok in enumerate(tokens):
+        rows = slot[tok * w.K:(tok + 1) * w.K]
+        got = gu.d2h(recv[t.from_numpy(rows).cuda()])
+        assert (got == xs[i][None, :]).all(), f"token {tok}"
+    # padding rows keep the sentinel
+    nrp = ref["plan"]["n_rows_padded"]
+    sid = ref["align"]["sorted_ids"]
+    pad_rows = np.nonzero(sid == w.P)[0]
+    if pad_rows.size:
+        pick = rng.choice(pad_rows, size=min(256, pad_rows.size), replace=False)
+        assert (gu.d2h(recv[t.from_numpy(pick).cuda()]) == 0x7F7F).all()
+    assert (nrp <= C).all()
+    yh = y[t.from_numpy(tokens).cuda()].cpu().numpy().astype(np.float64)
+    want = oracle.bf16_to_f64(xs) * gates32[tokens].astype(np.float64).sum(axis=1)[:, None]
+    assert (np.abs(yh - want) <= gu.COMBINE_RTOL * np.abs(want) + 1e-30).all()
+
+
+# --------------------------------------------------------------------------- edge cases
+def _edge(w, logits=None, sel_bias=None, cap=0, renorm=0, move=True):
+    logits = router_logits(w, 0) if logits is None else logits
+    res = gu.run_front(gu.shape_of(w, cap=cap, renorm=renorm), logits, sel_bias=sel_bias)
+    ref = gu.run_oracle(w, logits, sel_bias=sel_bias, cap=cap, renorm=bool(renorm))
+    gu.check_route(res, ref)
+    gu.check_plan(res["plan_fields"], ref["plan"], w.P)
+    gu.check_align(res, ref, w.R, res["sizes"]["C"])
+    if move:
+        _full_move_check(w, res, ref, activations(w, 0))
+    return res, ref
+
+
+TINY = WORKLOADS["tiny"]
+
+
+@pytest.mark.parametrize("case", [
+    "S1", "S300_ragged", "K1", "KeqE", "B0", "E_eq_R", "H_ragged", "H8", "renorm",
+    "softmax_big_E", "sel_bias"])
+def test_edge_cases(case):
+    print(f"[parity] edge {case}", flush=True)
+    w = TINY
+    kw = {}
+    if case == "S1":
+        w = w.with_(S=1)
+    elif case == "S300_ragged":
+        w = w.with_(S=300, H=64)
+    elif case == "K1":
+        w = w.with_(K=1)
+    elif case == "KeqE":
+        w = w.with_(K=w.E)
+    elif case == "B0":
+        w = WORKLOADS["wideep"].with_(S=16, H=64, B=0)
+    elif case == "E_eq_R":
+        w = w.with_(E=8, R=8, S=16)
+    elif case == "H_ragged":
+        w = w.with_(H=7176, S=8)
+    elif case == "H8":
+        w = w.with_(H=8)
+    elif case == "renorm":
+        kw["renorm"] = 1
+    elif case == "softmax_big_E":
+        w = WORKLOADS["dsv3"].with_(S=64, H=64, score="softmax")
+    elif case == "sel_bias":
+        kw["sel_bias"] = np.linspace(-1, 1, w.E).astype(np.float32)
+    _edge(w, **kw)
+
+
+def test_ties_and_signed_zero():
+    w = TINY.with_(S=16)
+    rng = np.random.default_rng(4)
+    logits = (rng.integers(-2, 3, size=(w.N, w.E)) * 0.5).astype(np.float32)
+    logits[rng.random(logits.shape) < 0.2] = np.float32(-0.0)
+    logits[0] = 0.0
+    _edge(w, logits=logits)
+
+
+def test_all_equal_logits():
+    w = TINY.with_(S=32)
+    _edge(w, logits=np.zeros((w.N, w.E), np.float32))
+
+
+def test_balanced_routing_no_replicas():
+    w = TINY.with_(S=32, H=64)
+    # token t of rank r picks rank r's two home experts with the largest keys
+    logits = np.full((w.N, w.E), -5.0, np.float32)
+    nh = w.E // w.R
+    for t_ in range(w.N):
+        r = t_ // w.S
+        logits[t_, r * nh:(r + 1) * nh] = [1.0, 0.5]
+    res, ref = _edge(w, logits=logits)
+    assert ref["plan"]["replicas"] == []
+    assert res["plan_fields"]["hdr"][0] == 0
+
+
+def test_one_overloaded_rank():
+    w = TINY.with_(S=32, H=64, B=1)
+    logits = router_logits(w, 0)
+    logits[:, 0] += 10.0   # expert 0 (rank 0) chosen by every token
+    res, ref = _edge(w, logits=logits)
+    assert ref["plan"]["over"][0] > 0
+
+
+def test_empty_input():
+    import load_balanced_token_amd as lbt
+    t = gu.torch()
+    shape = lbt.Shape(E=8, K=2, R=4, S=0, H=64, B=2, blk=16)
+    path = lbt.Path(shape)
+    buf = path.alloc()
+    lg = t.empty((0, 8), dtype=t.float32, device="cuda")
+    path.route_topk(lg, buf["ids"], buf["gates"], buf["counts"], buf["work"])
+    path.plan_balance(buf["counts"], buf["plan"], buf["status"])
+    path.align_sort(buf["ids"], buf["work"], buf["plan"], buf["slot"], buf["sorted_ids"],
+                    buf["block_wrow"], buf["block_expert"], buf["status"])
+    t.cuda.synchronize()
+    pf = lbt.plan_fields(buf["plan"].cpu().numpy(), path.sizes, 4, 8)
+    assert (buf["counts"].cpu().numpy() == 0).all()
+    assert (pf["n_rows_padded"] == 0).all() and pf["hdr"][0] == 0
+    assert (buf["block_wrow"].cpu().numpy() == -1).all()
+    assert buf["status"].item() == 0
+
+
+def test_capacity_too_small_sets_status():
+    import load_balanced_token_amd as lbt
+    t = gu.torch()
+    w = WORKLOADS["dsv3"].with_(S=64, H=64)
+    logits = router_logits(w, 0)
+    ref = gu.run_oracle(w, logits)
+    need = int(ref["plan"]["n_rows_padded"].max())
+    cap = (need // w.blk - 1) * w.blk
+    res = gu.run_front(gu.shape_of(w, cap=cap), logits)
+    assert res["status"][0] & lbt.ST_CAPACITY
+    assert res["plan_fields"]["hdr"][7] & lbt.ST_CAPACITY
+    ok = res["slot"] >= 0
+    assert (~ok).any()
+    # pairs that fit land where the uncapped plan puts them (same rows, new C)
+    full = ref["align"]["slot"]
+    C0 = ref["plan"]["C"]
+    assert np.array_equal(res["slot"][ok], (full[ok] // C0) * cap + full[ok] % C0)
+
+
+def test_histogram_of_caller_ids_and_bad_ids():
+    import load_balanced_token_amd as lbt
+    t = gu.torch()
+    w = TINY
+    ids, _ = oracle.route_topk(router_logits(w, 0), w.K, oracle.SOFTMAX)
+    path = lbt.Path(gu.shape_of(w))
+    buf = path.alloc()
+    buf["status"].zero_()
+    path.histogram(gu.h2d(ids.astype(np.int32)), buf["counts"], buf["work"], buf["status"])
+    t.cuda.synchronize()
+    assert np.array_equal(buf["counts"].cpu().numpy(), oracle.load_matrix(ids, w.R, w.S, w.E))
+    assert buf["status"].item() == 0
+    bad = ids.astype(np.int32).copy()
+    bad[3, 1] = w.E + 5
+    path.histogram(gu.h2d(bad), buf["counts"], buf["work"], buf["status"])
+    t.cuda.synchronize()
+    assert buf["status"].item() & lbt.ST_BADID
+
+
+def test_duplicate_ids_flagged():
+    import load_balanced_token_amd as lbt
+    t = gu.torch()
+    w = TINY
+    ids, _ = oracle.route_topk(router_logits(w, 0), w.K, oracle.SOFTMAX)
+    dup = ids.astype(np.int32).copy()
+    dup[5, 1] = dup[5, 0]
+    path = lbt.Path(gu.shape_of(w))
+    buf = path.alloc()
+    buf["status"].zero_()
+    d = gu.h2d(dup)
+    path.histogram(d, buf["counts"], buf["work"], buf["status"])
+    path.plan_balance(buf["counts"], buf["plan"], buf["status"])
+    path.align_sort(d, buf["work"], buf["plan"], buf["slot"], buf["sorted_ids"],
+                    buf["block_wrow"], buf["block_expert"], buf["status"])
+    t.cuda.synchronize()
+    assert buf["status"].item() & lbt.ST_DUPID
+
+
+def test_inconsistent_counts_flagged():
+    import load_balanced_token_amd as lbt
+    t = gu.torch()
+    w = TINY
+    path = lbt.Path(gu.shape_of(w))
+    buf = path.alloc()
+    counts = np.ones((w.R, w.E), np.int32)
+    path.plan_balance(gu.h2d(counts), buf["plan"], buf["status"])
+    t.cuda.synchronize()
+    assert buf["status"].item() & lbt.ST_BADCOUNT
+
+
+def test_bad_arguments_rejected():
+    import load_balanced_token_amd as lbt
+    t = gu.torch()
+    with pytest.raises(lbt.LbtError):
+        lbt.Path(lbt.Shape(E=10, K=2, R=4, S=8, H=64, B=1, blk=16))   # E % R != 0
+    with pytest.raises(lbt.LbtError):
+        lbt.Path(lbt.Shape(E=8, K=9, R=4, S=8, H=64, B=1, blk=16))    # K > E
+    with pytest.raises(lbt.LbtError):
+        lbt.Path(lbt.Shape(E=8, K=2, R=4, S=8, H=60, B=1, blk=16))    # H % 8
+    path = lbt.Path(lbt.Shape(E=8, K=2, R=4, S=8, H=64, B=1, blk=16))
+    buf = path.alloc()
+    xs = t.zeros(32 * 64 + 1, dtype=t.int16, device="cuda")[1:]        # misaligned
+    with pytest.raises(lbt.LbtError):
+        path.dispatch(xs, buf["slot"], buf["recv"])
+
+
+def test_deterministic_rerun():
+    t = gu.torch()
+    w = WORKLOADS["wideep"]
+    logits = router_logits(w, 0)
+    a = gu.run_front(gu.shape_of(w), logits)
+    b = gu.run_front(gu.shape_of(w), logits)
+    for k in ("ids", "gates", "counts", "plan", "slot", "block_wrow", "block_expert"):
+        assert np.array_equal(a[k], b[k]), k
+    C = a["sizes"]["C"]
+    nrp = a["plan_fields"]["n_rows_padded"]
+    for r in range(w.R):
+        assert np.array_equal(a["sorted_ids"][r * C: r * C + nrp[r]],
+                              b["sorted_ids"][r * C: r * C + nrp[r]])

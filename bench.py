@@ -1,0 +1,254 @@
+"""Benchmark of the load-balanced MoE token path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload dsv3]
+
+One step = route_topk (+ load histogram) -> plan_balance -> align_sort ->
+dispatch -> combine over one batch of synthetic router logits and bf16
+activations already resident in HBM (identity expert: combine reads the
+dispatched rows).  Prints one JSON line: token-slots/s of the whole step,
+per-kernel device times from HIP events recorded on the launch stream, the
+HBM roofline of the dominant kernel (combine), and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, vendor figure
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def algorithmic_bytes(w, C):
+    """Bytes each step must move (padding rows excluded; fp32 y).  Route:
+    logits read, ids + gates written.  Align: ids read, slot and sorted_ids
+    written.  Dispatch: x read once, K copies written, slot read.  Combine:
+    K rows read, slot + gate read, fp32 y written."""
+    N, P, E, H = w.N, w.P, w.E, w.H
+    return {
+        "route": N * E * 4 + P * 8,
+        "align": P * 12,
+        "dispatch": N * H * 2 + P * H * 2 + P * 4,
+        "combine": P * H * 2 + P * 8 + N * H * 4,
+    }
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "load_balanced_token_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"source_hash:\s*(\w+)", txt)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m or not b or m.group(1) != source_hash("move.hip", "lbt_internal.h"):
+        return None
+    return float(b.group(1))
+
+
+def cpu_baseline(name, sample_S):
+    """The oracle, as it stands, on a bounded sample of the workload: the same
+    generator and shapes with S reduced to ``sample_S`` tokens per rank."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    import oracle
+    from workloads import WORKLOADS, router_logits, activations
+
+    w = WORKLOADS[name].with_(S=sample_S)
+    logits = router_logits(w, 0)
+    x = activations(w, 0)
+    score = oracle.SOFTMAX if w.score == "softmax" else oracle.SIGMOID
+    t0 = time.perf_counter()
+    ids, gates = oracle.route_topk(logits, w.K, score)
+    counts = oracle.load_matrix(ids, w.R, w.S, w.E)
+    plan = oracle.plan_balance(counts, w.K, w.S, w.B, w.blk)
+    al = oracle.align_sort(ids, plan)
+    rows, data = oracle.dispatch_rows(x, al["slot"], w.K)
+    order = np.argsort(rows)
+    srt = rows[order]
+    y, _ = oracle.combine(lambda r: data[order[np.searchsorted(srt, r)]], al["slot"],
+                          gates.astype(np.float32), w.K)
+    dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    return {
+        "value": w.P / dt,
+        "unit": "token-slots/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{name} shape with S={sample_S} tokens/rank (N={w.N}, P={w.P} token-slots, "
+                  f"H={w.H}), layer 0; oracle route, histogram, plan, align, dispatch, combine "
+                  f"end to end on one host thread in {dt:.2f} s",
+        "host_cpu": platform.processor() or platform.machine(),
+        "host_logical_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--cpu-sample-S", type=int, default=0,
+                    help="tokens per rank of the oracle sample (default: up to 32768 tokens in all)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after timing, run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: every expert-parallel rank of the workload is a "
+              "logical partition of that GPU's memory, so --gpus must be 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import load_balanced_token_amd as lbt
+    from workloads import WORKLOADS, router_logits
+    from workloads.gen import X_CHUNK, x_chunk
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[args.workload]
+    shape = lbt.Shape(E=w.E, K=w.K, R=w.R, S=w.S, H=w.H, B=w.B, blk=w.blk,
+                      score_fn=lbt.SOFTMAX if w.score == "softmax" else lbt.SIGMOID)
+    path = lbt.Path(shape)
+    C = path.sizes["C"]
+    buf = path.alloc(dev)
+    print(f"[bench] {w.name}: E={w.E} K={w.K} R={w.R} S={w.S} H={w.H} B={w.B} blk={w.blk} "
+          f"C={C}; generating inputs", file=sys.stderr, flush=True)
+
+    # inputs resident in HBM before timing
+    logits = torch.from_numpy(router_logits(w, 0)).to(dev)
+    x = torch.empty((w.N, w.H), dtype=torch.int16, device=dev)
+    for c in range((w.N + X_CHUNK - 1) // X_CHUNK):
+        blk = x_chunk(w, 0, c)
+        x[c * X_CHUNK: c * X_CHUNK + blk.shape[0]] = torch.from_numpy(blk.view(np.int16)).to(dev)
+    buf["status"].zero_()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    names = ["route", "plan", "align", "dispatch", "combine"]
+
+    def step(evs=None):
+        rec = (lambda i: evs[i].record(stream)) if evs is not None else (lambda i: None)
+        rec(0)
+        path.route_topk(logits, buf["ids"], buf["gates"], buf["counts"], buf["work"])
+        rec(1)
+        path.plan_balance(buf["counts"], buf["plan"], buf["status"])
+        rec(2)
+        path.align_sort(buf["ids"], buf["work"], buf["plan"], buf["slot"], buf["sorted_ids"],
+                        buf["block_wrow"], buf["block_expert"], buf["status"])
+        rec(3)
+        path.dispatch(x, buf["slot"], buf["recv"])
+        rec(4)
+        path.combine(buf["recv"], buf["slot"], buf["gates"], buf["y"])
+        rec(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps}", file=sys.stderr,
+          flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: [] for n in names}
+    for e in evs:
+        for j, n in enumerate(names):
+            per[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)   # microseconds
+    avg_us = {n: float(np.mean(v)) for n, v in per.items()}
+    step_dev_us = [e[0].elapsed_time(e[5]) * 1e3 for e in evs]
+
+    status = int(buf["status"].item())
+    hdr = buf["plan"][:16].cpu().numpy()
+    if args.calib_copy:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    ab = algorithmic_bytes(w, C)
+    step_bytes = sum(ab.values())
+    ms_per_step = wall / args.steps * 1e3
+    slots_per_s = w.P * args.steps / wall
+    comb_gbps = ab["combine"] / (avg_us["combine"] * 1e-6) / 1e9
+    disp_gbps = ab["dispatch"] / (avg_us["dispatch"] * 1e-6) / 1e9
+    dc_gbps = (ab["dispatch"] + ab["combine"]) / ((avg_us["dispatch"] + avg_us["combine"]) * 1e-6) / 1e9
+    traffic = measured_traffic("combine", w.name)
+    result = {
+        "metric": "token-slots/s",
+        "value": slots_per_s,
+        "unit": "token-slots/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "E": w.E, "K": w.K, "R": w.R, "S": w.S, "H": w.H,
+                   "B": w.B, "blk": w.blk, "C": C, "token_slots_per_step": w.P,
+                   "gate": w.score, "combine_accumulate": "fp32", "y": "fp32",
+                   "expert": "identity (out = recv)"},
+        "roofline": {"bound": "hbm", "kernel": "k_combine",
+                     "achieved": comb_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": comb_gbps / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": ab["combine"]},
+        "step_hbm_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_pct_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "dispatch_combine_gbps": dc_gbps,
+        "dispatch_combine_frac_peak": dc_gbps / HBM_PEAK_GBPS,
+        "dispatch_gbps": disp_gbps,
+        "kernel_us": avg_us,
+        "plan_us": avg_us["plan"],
+        "step_device_us_median": float(np.median(step_dev_us)),
+        "max_vio": float(hdr[1]) * w.E / w.P - 1.0,
+        "rank_imbalance_before": float(hdr[2]) / w.SK - 1.0,
+        "replica_segments": int(hdr[0]),
+        "status": status,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        sample_S = args.cpu_sample_S or max(1, min(w.S, 32768 // w.R))
+        result["cpu_baseline"] = cpu_baseline(w.name, sample_S)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -14,7 +14,7 @@
 
 namespace lbt {
 
-constexpr int kRouteThreads = 512;
+constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 
 // Order-preserving map of a finite fp32 value to u32; -0.0 maps like +0.0 so
@@ -25,16 +25,44 @@ __device__ __forceinline__ uint32_t ordered_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// DPP lane permutations inside a 16-lane row.
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i inside each 8 lanes
+constexpr int kDppRowMirror = 0x140;   // lane i <-> 15-i inside each 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+
+// Wave-wide max of a u32, returned as a wave-uniform value: four DPP steps
+// leave every lane of a 16-lane row holding the row's max, and the four
+// row maxima are combined from lanes 0, 16, 32, 48.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o, kWave));
-  return x;
+  int v = (int)x;
+  v = (int)max((uint32_t)v, (uint32_t)dpp<kDppQuadXor1>(v));
+  v = (int)max((uint32_t)v, (uint32_t)dpp<kDppQuadXor2>(v));
+  v = (int)max((uint32_t)v, (uint32_t)dpp<kDppHalfMirror>(v));
+  v = (int)max((uint32_t)v, (uint32_t)dpp<kDppRowMirror>(v));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane(v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane(v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
 }
 
 __device__ __forceinline__ float wave_max_f32(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
-  return x;
+  int v = __float_as_int(x);
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp<kDppQuadXor1>(v))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp<kDppQuadXor2>(v))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp<kDppHalfMirror>(v))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp<kDppRowMirror>(v))));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(v, 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(v, 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(v, 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(v, 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
 __device__ __forceinline__ double wave_sum_f64(double x) {
@@ -95,10 +123,21 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict
 #pragma unroll
   for (int v = 0; v < V; ++v) b[v] = (bias != nullptr && e0 + v < E) ? bias[e0 + v] : 0.f;
 
-  for (int i = wave_id(); i < len; i += kRouteWaves) {
+  // every wave loads all of its tokens' rows first (one latency for all),
+  // then routes them one after the other
+  constexpr int TPW = kTileTokens / kRouteWaves;
+  float rows[TPW][V];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int i = wave_id() + u * kRouteWaves;
+    if (i < len) load_row<V>(logits + ((long long)t0 + i) * E, E, lane, vec, rows[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int i = wave_id() + u * kRouteWaves;
+    if (i >= len) break;
     const long long t = (long long)t0 + i;
-    float raw[V];
-    load_row<V>(logits + t * E, E, lane, vec, raw);
+    float (&raw)[V] = rows[u];
     uint32_t key[V];
 #pragma unroll
     for (int v = 0; v < V; ++v)

@@ -5,10 +5,11 @@
 // Top-K: [AlignSort] -- the MoE layer routes each token to its Top-K experts
 // by gate score (DeepSeek V3/R1 add a per-expert gating bias that penalises
 // hot experts); the article names warp-shuffle sorting in thread-local
-// registers as the faster alternative to a shared-memory radix sort.  Here
-// one wave64 owns one token: lane l holds experts [l*V, l*V+V) of the row,
-// and K rounds of a wave-wide max over order-preserving 32-bit keys pick
-// the experts, lowest lane (= lowest expert index) winning ties.
+// registers as the faster alternative to a shared-memory radix sort.  Here a
+// token belongs to one 16-lane DPP row of a wave64 (four tokens per wave):
+// lane j of the row holds experts [j*V, j*V+V); each of the K rounds takes
+// the row-wide max of order-preserving 32-bit keys with four DPP steps and
+// the lowest lane holding it (= the lowest expert index) wins.
 // Load matrix: [UltraEP] section "その仕組みは高速なエキスパート複製に依存する".
 #include "lbt_internal.h"
 
@@ -16,6 +17,9 @@ namespace lbt {
 
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / kWave;
+constexpr int kRowLanes = 16;                        // lanes per token
+constexpr int kRowsPerWave = kWave / kRowLanes;      // tokens per wave
+constexpr int kRoutePasses = kTileTokens / (kRouteWaves * kRowsPerWave);
 
 // Order-preserving map of a finite fp32 value to u32; -0.0 maps like +0.0 so
 // the two tie (IEEE equality).  Every finite value maps above 0x007FFFFF.
@@ -36,46 +40,46 @@ __device__ __forceinline__ int dpp(int v) {
   return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
 }
 
-// Wave-wide max of a u32, returned as a wave-uniform value: four DPP steps
-// leave every lane of a 16-lane row holding the row's max, and the four
-// row maxima are combined from lanes 0, 16, 32, 48.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+// Row-wide (16-lane) reductions; every lane of the row receives the result.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t x) {
   int v = (int)x;
   v = (int)max((uint32_t)v, (uint32_t)dpp<kDppQuadXor1>(v));
   v = (int)max((uint32_t)v, (uint32_t)dpp<kDppQuadXor2>(v));
   v = (int)max((uint32_t)v, (uint32_t)dpp<kDppHalfMirror>(v));
   v = (int)max((uint32_t)v, (uint32_t)dpp<kDppRowMirror>(v));
-  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane(v, 0);
-  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane(v, 16);
-  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane(v, 32);
-  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane(v, 48);
-  return max(max(a, b), max(c, d));
+  return (uint32_t)v;
 }
 
-__device__ __forceinline__ float wave_max_f32(float x) {
+__device__ __forceinline__ float row_max_f32(float x) {
   int v = __float_as_int(x);
   v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp<kDppQuadXor1>(v))));
   v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp<kDppQuadXor2>(v))));
   v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp<kDppHalfMirror>(v))));
   v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp<kDppRowMirror>(v))));
-  const float a = __int_as_float(__builtin_amdgcn_readlane(v, 0));
-  const float b = __int_as_float(__builtin_amdgcn_readlane(v, 16));
-  const float c = __int_as_float(__builtin_amdgcn_readlane(v, 32));
-  const float d = __int_as_float(__builtin_amdgcn_readlane(v, 48));
-  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+  return __int_as_float(v);
 }
 
-__device__ __forceinline__ double wave_sum_f64(double x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const long long b = __double_as_longlong(x);
+  const int lo = dpp<CTRL>((int)(b & 0xFFFFFFFFll));
+  const int hi = dpp<CTRL>((int)(b >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ double row_sum_f64(double x) {
+  x += dpp_f64<kDppQuadXor1>(x);
+  x += dpp_f64<kDppQuadXor2>(x);
+  x += dpp_f64<kDppHalfMirror>(x);
+  x += dpp_f64<kDppRowMirror>(x);
   return x;
 }
 
-// Load lane's V logits [lane*V, lane*V+V) of one row; vec = 4, 2 or 1.
+// Load lane's V logits [j*V, j*V+V) of one row (j = lane within its
+// 16-lane row); vec = 4, 2 or 1 is the widest aligned load.
 template <int V>
-__device__ __forceinline__ void load_row(const float* __restrict__ row, int E, int lane, int vec,
+__device__ __forceinline__ void load_row(const float* __restrict__ row, int E, int e0, int vec,
                                          float (&raw)[V]) {
-  const int e0 = lane * V;
   if constexpr (V % 4 == 0) {
     if (vec == 4) {
 #pragma unroll
@@ -109,43 +113,48 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict
                                                          float* __restrict__ gates,
                                                          int32_t* __restrict__ tile_counts) {
   __shared__ int hist[kMaxE];
+  // winners of each round: expert and raw logit, per wave, token row and k
+  __shared__ int s_id[kRouteWaves][kRowsPerWave][kMaxK];
+  __shared__ float s_raw[kRouteWaves][kRowsPerWave][kMaxK];
   const int E = d.E, K = d.K;
   const int tile = blockIdx.x;
   const int r = tile / d.tpr, j = tile - r * d.tpr;
   const int t0 = r * d.S + j * kTileTokens;
   const int len = min(kTileTokens, d.S - j * kTileTokens);
   for (int e = threadIdx.x; e < E; e += kRouteThreads) hist[e] = 0;
-  __syncthreads();
 
-  const int lane = lane_id();
-  const int e0 = lane * V;
+  const int lane = lane_id(), wv = wave_id();
+  const int row = lane / kRowLanes, rl = lane % kRowLanes;
+  const int e0 = rl * V;
   float b[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) b[v] = (bias != nullptr && e0 + v < E) ? bias[e0 + v] : 0.f;
 
-  // every wave loads all of its tokens' rows first (one latency for all),
-  // then routes them one after the other
-  constexpr int TPW = kTileTokens / kRouteWaves;
-  float rows[TPW][V];
+  // all rows of this wave first (one memory latency), then the rounds
+  float rows[kRoutePasses][V];
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int i = wave_id() + u * kRouteWaves;
-    if (i < len) load_row<V>(logits + ((long long)t0 + i) * E, E, lane, vec, rows[u]);
+  for (int u = 0; u < kRoutePasses; ++u) {
+    const int i = (u * kRouteWaves + wv) * kRowsPerWave + row;
+    if (i < len) {
+      load_row<V>(logits + ((long long)t0 + i) * E, E, e0, vec, rows[u]);
+    } else {
+#pragma unroll
+      for (int v = 0; v < V; ++v) rows[u][v] = 0.f;
+    }
   }
+  __syncthreads();   // hist zeroed
+
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int i = wave_id() + u * kRouteWaves;
-    if (i >= len) break;
-    const long long t = (long long)t0 + i;
-    float (&raw)[V] = rows[u];
+  for (int u = 0; u < kRoutePasses; ++u) {
+    const int i = (u * kRouteWaves + wv) * kRowsPerWave + row;
+    const bool valid = i < len;
+    if (!__any(valid)) continue;
+    const float(&raw)[V] = rows[u];
     uint32_t key[V];
 #pragma unroll
     for (int v = 0; v < V; ++v)
-      key[v] = (e0 + v < E) ? ordered_key(bias != nullptr ? raw[v] + b[v] : raw[v]) : 0u;
-
+      key[v] = (valid && e0 + v < E) ? ordered_key(bias != nullptr ? raw[v] + b[v] : raw[v]) : 0u;
     uint32_t taken = 0;
-    int my_id = 0;
-    float my_logit = 0.f;
     for (int k = 0; k < K; ++k) {
       // lane-local best untaken key; strict '>' keeps the lower expert on ties
       uint32_t best = 0;
@@ -158,43 +167,58 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict
         bv = ok ? v : bv;
         braw = ok ? raw[v] : braw;
       }
-      const uint32_t wmax = wave_max_u32(best);
-      const unsigned long long m = __ballot(best == wmax);
-      const int win = __ffsll((long long)m) - 1;          // lowest lane = lowest expert
-      const int wbv = __builtin_amdgcn_readlane(bv, win);
-      const float wraw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(braw), win));
-      if (lane == win) taken |= 1u << bv;
-      if (lane == k) {
-        my_id = win * V + wbv;
-        my_logit = wraw;
+      const uint32_t rmax = row_max_u32(best);
+      const bool cand = valid && best == rmax;
+      const unsigned long long m = __ballot(cand);
+      // candidates below this lane in the wave, minus those in lower rows
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const int p1 = __popcll(m & 0xFFFFull), p2 = __popcll(m & 0xFFFFFFFFull),
+                p3 = __popcll(m & 0xFFFFFFFFFFFFull);
+      const int lower = row == 0 ? 0 : row == 1 ? p1 : row == 2 ? p2 : p3;
+      if (cand && below == lower) {        // lowest lane of the row = lowest expert
+        taken |= 1u << bv;
+        s_id[wv][row][k] = e0 + bv;
+        s_raw[wv][row][k] = braw;
       }
     }
+    __builtin_amdgcn_wave_barrier();
 
-    double g;
-    if (d.score_fn == LBT_SIGMOID) {
-      g = 1.0 / (1.0 + exp(-(double)my_logit));
-    } else {
-      float mx = -INFINITY;
+    const long long t = (long long)t0 + i;
+    double mx = 0.0, denom = 1.0;
+    if (d.score_fn == LBT_SOFTMAX) {
+      float m = -INFINITY;
 #pragma unroll
       for (int v = 0; v < V; ++v)
-        if (e0 + v < E) mx = fmaxf(mx, raw[v]);
-      mx = wave_max_f32(mx);
+        if (e0 + v < E) m = fmaxf(m, raw[v]);
+      mx = (double)row_max_f32(m);
       double s = 0.0;
 #pragma unroll
       for (int v = 0; v < V; ++v)
-        if (e0 + v < E) s += exp((double)raw[v] - (double)mx);
-      s = wave_sum_f64(s);
-      g = exp((double)my_logit - (double)mx) / s;
+        if (e0 + v < E) s += exp((double)raw[v] - mx);
+      denom = row_sum_f64(s);
     }
+    double gsum = 1.0;
     if (d.renorm) {
-      const double gs = wave_sum_f64(lane < K ? g : 0.0);
-      g = g / gs;
+      double part = 0.0;
+      for (int kk = rl; kk < K; kk += kRowLanes) {
+        const double lg = (double)s_raw[wv][row][kk];
+        part += d.score_fn == LBT_SIGMOID ? 1.0 / (1.0 + exp(-lg)) : exp(lg - mx) / denom;
+      }
+      gsum = row_sum_f64(part);
     }
-    if (lane < K) {
-      ids[t * K + lane] = my_id;
-      gates[t * K + lane] = (float)g;
-      atomicAdd(&hist[my_id], 1);
+    if (valid) {
+      for (int kk = rl; kk < K; kk += kRowLanes) {
+        const int id = s_id[wv][row][kk];
+        const double lg = (double)s_raw[wv][row][kk];
+        double g = d.score_fn == LBT_SIGMOID ? 1.0 / (1.0 + exp(-lg)) : exp(lg - mx) / denom;
+        if (d.renorm) g = g / gsum;
+        ids[t * K + kk] = id;
+        gates[t * K + kk] = (float)g;
+        atomicAdd(&hist[id], 1);
+      }
     }
+    __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kRouteThreads)
@@ -266,12 +290,14 @@ hipError_t launch_route(const Dims& d, const float* logits, const float* bias, i
   if (d.n_tiles == 0 || d.S == 0) return hipSuccess;
   const int vec = route_vec(logits, d.E);
   const dim3 grid(d.n_tiles), block(kRouteThreads);
-  const int V = (d.E + kWave - 1) / kWave;
+  const int V = (d.E + kRowLanes - 1) / kRowLanes;
   if (V <= 1) hipLaunchKernelGGL(k_route<1>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
   else if (V <= 2) hipLaunchKernelGGL(k_route<2>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
   else if (V <= 4) hipLaunchKernelGGL(k_route<4>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
-  else if (V <= 6) hipLaunchKernelGGL(k_route<6>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
-  else hipLaunchKernelGGL(k_route<8>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
+  else if (V <= 8) hipLaunchKernelGGL(k_route<8>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
+  else if (V <= 16) hipLaunchKernelGGL(k_route<16>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
+  else if (V <= 24) hipLaunchKernelGGL(k_route<24>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
+  else hipLaunchKernelGGL(k_route<32>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
   return hipGetLastError();
 }
 

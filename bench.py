@@ -106,6 +106,57 @@ def cpu_baseline(name, sample_S):
     }
 
 
+def decode_latency(path, buf, w, x, n_steps, dev):
+    """p50/p99 latency of one whole step over ``n_steps`` fresh routings.
+
+    Every routing is resident in HBM; the step (route -> plan -> align ->
+    dispatch -> combine) is captured once in a HIP graph whose first node
+    gathers routing number ``idx`` (a device counter the graph advances), so
+    each replay runs on new router logits with no host work in between."""
+    import numpy as np
+    import torch
+    from workloads import router_logits
+
+    all_logits = torch.empty((n_steps, w.N, w.E), dtype=torch.float32, device=dev)
+    for i in range(n_steps):
+        all_logits[i] = torch.from_numpy(router_logits(w, i)).to(dev)
+    idx = torch.zeros(1, dtype=torch.int64, device=dev)
+    cur = torch.empty((1, w.N, w.E), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+
+    def body():
+        torch.index_select(all_logits, 0, idx, out=cur)
+        path.step(cur[0], x, buf)
+        idx.add_(1)
+
+    with torch.cuda.stream(stream):        # warm up outside the graph
+        for _ in range(3):
+            body()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        body()
+    idx.zero_()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lat = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    # the last replay's routing, checked for a clean status
+    status = int(buf["status"].item())
+    return {"p50_us": float(np.percentile(lat, 50)), "p99_us": float(np.percentile(lat, 99)),
+            "mean_us": float(lat.mean()), "steps": n_steps, "wall_s": wall, "status": status,
+            "note": "graph replay incl. the gather of fresh router logits"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +166,8 @@ def main():
     ap.add_argument("--cpu-sample-S", type=int, default=0,
                     help="tokens per rank of the oracle sample (default: up to 32768 tokens in all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=1000,
+                    help="fresh-routing graph replays for the decode workloads")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -243,6 +296,10 @@ def main():
         "status": status,
         "device": torch.cuda.get_device_name(0),
     }
+    if w.name.startswith("decode"):
+        print(f"[bench] decode latency over {args.decode_steps} fresh routings (HIP graph)",
+              file=sys.stderr, flush=True)
+        result["decode_latency"] = decode_latency(path, buf, w, x, args.decode_steps, dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         sample_S = args.cpu_sample_S or max(1, min(w.S, 32768 // w.R))

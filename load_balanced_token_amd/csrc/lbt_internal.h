@@ -132,6 +132,42 @@ __device__ int block_excl_scan(int* arr, int n, int* tmp) {
   return total;
 }
 
+// Inclusive prefix sum across a wave64 with DPP: Hillis-Steele steps inside
+// each 16-lane row (row_shr 1, 2, 4, 8; lanes without a source add 0), then
+// row_bcast:15 carries rows 0 and 2 into rows 1 and 3, and row_bcast:31
+// carries rows 0-1 into rows 2-3.
+__device__ __forceinline__ int wave_incl_scan_dpp(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+// Exclusive prefix sum of a[0..n) in LDS by ONE wave (lane l takes the
+// contiguous chunk [l*c, l*c + c), c = ceil(n/64)); a[n] receives the total,
+// which every lane returns.  No workgroup barrier.
+__device__ __forceinline__ int wave_excl_scan_lds(int* a, int n) {
+  const int lane = lane_id();
+  const int c = (n + kWave - 1) / kWave;
+  const int lo = min(n, lane * c), hi = min(n, lo + c);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += a[i];
+  const int incl = wave_incl_scan_dpp(s);
+  int run = incl - s;
+  for (int i = lo; i < hi; ++i) {
+    const int v = a[i];
+    a[i] = run;
+    run += v;
+  }
+  const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+  if (lane == 0) a[n] = total;
+  __builtin_amdgcn_wave_barrier();
+  return total;
+}
+
 // First index in a[0..n) whose value is > x (a non-decreasing).
 __device__ __forceinline__ int upper_bound(const int* a, int n, int x) {
   int lo = 0, hi = n;

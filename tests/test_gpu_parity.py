@@ -195,7 +195,7 @@ TINY = WORKLOADS["tiny"]
 
 
 @pytest.mark.parametrize("case", [
-    "S1", "S300_ragged", "K1", "KeqE", "B0", "E_eq_R", "H_ragged", "H8", "renorm",
+    "S1", "S300_ragged", "K1", "K3", "KeqE", "B0", "E_eq_R", "H_ragged", "H8", "renorm",
     "softmax_big_E", "sel_bias"])
 def test_edge_cases(case):
     print(f"[parity] edge {case}", flush=True)
@@ -207,6 +207,8 @@ def test_edge_cases(case):
         w = w.with_(S=300, H=64)
     elif case == "K1":
         w = w.with_(K=1)
+    elif case == "K3":
+        w = w.with_(K=3)
     elif case == "KeqE":
         w = w.with_(K=w.E)
     elif case == "B0":
@@ -378,3 +380,80 @@ def test_deterministic_rerun():
     for r in range(w.R):
         assert np.array_equal(a["sorted_ids"][r * C: r * C + nrp[r]],
                               b["sorted_ids"][r * C: r * C + nrp[r]])
+
+
+def test_graph_capture_replays_match_eager():
+    """The whole step captured in a HIP graph: every replay (fresh routing
+    each time, eager work and syncs in between) equals the eager run."""
+    import load_balanced_token_amd as lbt
+    t = gu.torch()
+    w = WORKLOADS["decode16"].with_(H=512)
+    path = lbt.Path(gu.shape_of(w))
+    buf = path.alloc()
+    buf["status"].zero_()
+    n = 4
+    all_logits = t.stack([gu.h2d(router_logits(w, i)) for i in range(n)])
+    x = gu.h2d(activations(w, 0))
+    idx = t.zeros(1, dtype=t.int64, device="cuda")
+    cur = t.empty((1, w.N, w.E), dtype=t.float32, device="cuda")
+    keys = ("ids", "gates", "counts", "plan", "slot", "block_wrow", "y")
+
+    def body():
+        t.index_select(all_logits, 0, idx, out=cur)
+        path.step(cur[0], x, buf)
+        idx.add_(1)
+
+    s = t.cuda.Stream()
+    s.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(s):
+        body()
+    t.cuda.current_stream().wait_stream(s)
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g, stream=s):
+        body()
+    idx.zero_()
+    t.cuda.synchronize()
+    ref_path = lbt.Path(gu.shape_of(w))
+    for i in range(n):
+        g.replay()
+        t.cuda.synchronize()
+        got = {k: buf[k].clone() for k in keys}
+        ref = ref_path.alloc()
+        ref["status"].zero_()
+        ref_path.step(all_logits[i], x, ref)            # eager work between replays
+        t.cuda.synchronize()
+        for k in keys:
+            assert t.equal(got[k], ref[k]), f"replay {i}: {k}"
+        assert buf["status"].item() == 0
+
+
+@pytest.mark.parametrize("H", [7168, 512])
+def test_dispatch_combine_with_dropped_pairs(H):
+    """A capacity below the plan's need drops pairs (slot -1): dispatch skips
+    them and combine sums only the pairs that fit (both row-width paths)."""
+    t = gu.torch()
+    w = WORKLOADS["dsv3"].with_(S=32, H=H)
+    logits = router_logits(w, 0)
+    ref = gu.run_oracle(w, logits)
+    need = int(ref["plan"]["n_rows_padded"].max())
+    cap = (need // w.blk - 1) * w.blk
+    res = gu.run_front(gu.shape_of(w, cap=cap), logits)
+    slot = res["slot"]
+    assert (slot < 0).any() and (slot >= 0).any()
+    path = res["path"]
+    x_bits = activations(w, 0)
+    recv = t.zeros((w.R * cap, w.H), dtype=t.int16, device="cuda")
+    path.dispatch(gu.h2d(x_bits), res["dev"]["slot"], recv)
+    gates32 = ref["gates"].astype(np.float32)
+    y = t.empty((w.N, w.H), dtype=t.float32, device="cuda")
+    path.combine(recv, res["dev"]["slot"], gu.h2d(gates32), y)
+    t.cuda.synchronize()
+    recv_h = gu.d2h(recv)
+    ok = slot >= 0
+    f = np.nonzero(ok)[0]
+    assert np.array_equal(recv_h[slot[f]], x_bits[f // w.K])
+    g_fit = np.where(ok.reshape(w.N, w.K), gates32, 0).astype(np.float64)
+    want = oracle.bf16_to_f64(x_bits) * g_fit.sum(axis=1)[:, None]
+    got = y.cpu().numpy().astype(np.float64)
+    assert (np.abs(got - want) <= gu.COMBINE_RTOL * np.abs(want) + 1e-30).all()

@@ -230,7 +230,8 @@ def main():
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps}", file=sys.stderr,
           flush=True)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -242,7 +243,20 @@ def main():
         for j, n in enumerate(names):
             per[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)   # microseconds
     avg_us = {n: float(np.mean(v)) for n, v in per.items()}
-    step_dev_us = [e[0].elapsed_time(e[5]) * 1e3 for e in evs]
+    step_dev_us = [e[0].elapsed_time(e[-1]) * 1e3 for e in evs]
+
+    # the planner alone (back-to-back launches on the same load matrix)
+    plan2 = torch.empty_like(buf["plan"])
+    pev = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
+    for _ in range(3):
+        path.plan_balance(buf["counts"], plan2)
+    pev[0].record(stream)
+    for i in range(20):
+        path.plan_balance(buf["counts"], plan2)
+        pev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    plan_alone_us = float(np.median([pev[i].elapsed_time(pev[i + 1]) * 1e3 for i in range(20)]))
+    assert torch.equal(plan2, buf["plan"]), "standalone plan differs from the fused one"
 
     status = int(buf["status"].item())
     hdr = buf["plan"][:16].cpu().numpy()
@@ -288,7 +302,8 @@ def main():
         "dispatch_combine_frac_peak": dc_gbps / HBM_PEAK_GBPS,
         "dispatch_gbps": disp_gbps,
         "kernel_us": avg_us,
-        "plan_us": avg_us["plan"],
+        "plan_us": plan_alone_us,
+        "plan_in_step_us": avg_us["plan"],
         "step_device_us_median": float(np.median(step_dev_us)),
         "max_vio": float(hdr[1]) * w.E / w.P - 1.0,
         "rank_imbalance_before": float(hdr[2]) / w.SK - 1.0,

@@ -147,20 +147,27 @@ __device__ __forceinline__ int wave_incl_scan_dpp(int x) {
 }
 
 // Exclusive prefix sum of a[0..n) in LDS by ONE wave (lane l takes the
-// contiguous chunk [l*c, l*c + c), c = ceil(n/64)); a[n] receives the total,
-// which every lane returns.  No workgroup barrier.
+// contiguous chunk [l*c, l*c + c), c = ceil(n/64) <= CMAX); a[n] receives the
+// total, which every lane returns.  The chunk is read with independent loads
+// (no dependent LDS round trips) and scanned in registers.  No workgroup
+// barrier.
+template <int CMAX>
 __device__ __forceinline__ int wave_excl_scan_lds(int* a, int n) {
   const int lane = lane_id();
   const int c = (n + kWave - 1) / kWave;
-  const int lo = min(n, lane * c), hi = min(n, lo + c);
+  const int lo = lane * c;
+  int v[CMAX];
+#pragma unroll
+  for (int i = 0; i < CMAX; ++i) v[i] = (i < c && lo + i < n) ? a[lo + i] : 0;
   int s = 0;
-  for (int i = lo; i < hi; ++i) s += a[i];
+#pragma unroll
+  for (int i = 0; i < CMAX; ++i) s += v[i];
   const int incl = wave_incl_scan_dpp(s);
   int run = incl - s;
-  for (int i = lo; i < hi; ++i) {
-    const int v = a[i];
-    a[i] = run;
-    run += v;
+#pragma unroll
+  for (int i = 0; i < CMAX; ++i) {
+    if (i < c && lo + i < n) a[lo + i] = run;
+    run += v[i];
   }
   const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
   if (lane == 0) a[n] = total;

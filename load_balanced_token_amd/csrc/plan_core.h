@@ -1,0 +1,256 @@
+// The online balancing plan: one workgroup turns the per-expert loads into
+// the replica segments and per-rank segment tables, entirely on the device.
+// The plan body as a device function; the plan kernel wraps it.
+//
+// [MoonEP-GR] sections "Η βασική υπόσχεση του MoonEP: σταθερό φορτίο S × K"
+// (each rank receives exactly S*K; a few temporary expert copies, planned
+// online from the current router output) and "Το memory contract ..."
+// (weight rows 0..E-1 are the ranks' experts, E..E+B-1 local prefetch
+// slots, the grouped GEMM finds experts by row index and consumes the
+// planner's cu_seqlens; replicas beyond the slots are read from home).
+// [UltraEP] section "その仕組みは高速なエキスパート複製に依存する" (the
+// planner runs fully on the GPU, no host round trip inside a layer;
+// replicas exist only when given work).
+//
+// The rule: rank r keeps min(L_r, S*K) of its pairs, the first ones of its
+// home stream; the overflow of every expert (experts ascending) and the
+// deficit of every rank (ranks ascending) are laid on one line, and each
+// non-empty overlap is a replica segment ("piece").  The workgroup sums the
+// load matrix, one wave then builds the whole plan in LDS with DPP prefix
+// sums and binary searches (no workgroup barriers on the critical path),
+// and the workgroup writes the blob.  E <= 512 experts, R <= 512 ranks.
+#pragma once
+#include "lbt_internal.h"
+
+namespace lbt {
+
+constexpr int kPlanThreads = 1024;
+
+__device__ __forceinline__ int pad_to(int c, int blk) { return ((c + blk - 1) / blk) * blk; }
+
+// LDS of the plan.
+struct PlanSmem {
+  int sT[kMaxE + 1];      // T_e
+  int sX[kMaxE + 1];      // exclusive prefix of T over e
+  int sH[kMaxE];          // h_e
+  int sO[kMaxE + 1];      // o_e, then exclusive prefix O_e
+  int sNp[kMaxE + 1];     // pieces of expert e, then exclusive prefix
+  int sDlo[kMaxE];        // compact index of e's first deficit rank
+  int sL[kMaxR];          // L_r
+  int sDef[kMaxR];        // def_r
+  int sD[kMaxR + 1];      // exclusive prefix D_r
+  int sCidx[kMaxR + 1];   // compact index among deficit ranks
+  int sDl[kMaxR];         // compact index -> rank
+  int sRep[kMaxR + 1];    // replicas per rank, then first piece of rank
+  int sPe[kMaxPieces], sPd[kMaxPieces], sPc[kMaxPieces], sPl[kMaxPieces],
+      sPj[kMaxPieces];
+  int sF[kMaxE + kMaxPieces + 1];  // flat segment padded lengths -> starts
+  int sStat[8];  // max_T, max_L, over ranks, over experts, status, nP, totOv, Ptot
+
+};
+
+// The plan from T_e (in m.sT and m.sX, written and made visible by a
+// workgroup barrier before the call); 1024 threads; writes the whole blob
+// and *status.
+__device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, int32_t* __restrict__ plan,
+                                          int32_t* __restrict__ status) {
+  auto& sT = m.sT; auto& sX = m.sX; auto& sH = m.sH; auto& sO = m.sO; auto& sNp = m.sNp;
+  auto& sDlo = m.sDlo; auto& sL = m.sL; auto& sDef = m.sDef; auto& sD = m.sD;
+  auto& sCidx = m.sCidx; auto& sDl = m.sDl; auto& sRep = m.sRep; auto& sPe = m.sPe;
+  auto& sPd = m.sPd; auto& sPc = m.sPc; auto& sPl = m.sPl; auto& sPj = m.sPj; auto& sF = m.sF;
+  auto& sStat = m.sStat;
+  const int tid = threadIdx.x;
+  const int E = d.E, R = d.R, nh = d.nh, SK = d.SK, B = d.B, blk = d.blk, C = d.C;
+  const PlanLayout pl = d.pl;
+  const int ms = pl.max_seg;
+
+  // 2. wave 0 alone: the plan, with wave-level scans and no barriers
+  if (tid < kWave) {
+    const int lane = tid;
+    const int Ptot = wave_excl_scan_lds<kMaxE / kWave>(sX, E);
+    const bool consistent = (long long)Ptot == (long long)R * SK;
+    int maxT = 0, nOverE = 0;
+    for (int e = lane; e < E; e += kWave) {
+      const int r = e / nh;
+      const int T = sT[e];
+      const int Pe = sX[e] - sX[r * nh];        // position in r's home stream
+      const int h = consistent ? min(max(SK - Pe, 0), T) : 0;
+      sH[e] = h;
+      sO[e] = consistent ? T - h : 0;
+      maxT = max(maxT, T);
+      nOverE += (consistent && T - h > 0);
+    }
+    int maxL = 0, nOverR = 0;
+    for (int r = lane; r < R; r += kWave) {
+      const int L = sX[(r + 1) * nh] - sX[r * nh];
+      const int def = consistent ? SK - min(L, SK) : 0;
+      sL[r] = L;
+      sDef[r] = def;
+      sD[r] = def;
+      sCidx[r] = def > 0;
+      sRep[r] = 0;
+      maxL = max(maxL, L);
+      nOverR += (L > SK);
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int totOv = wave_excl_scan_lds<kMaxE / kWave>(sO, E);
+    wave_excl_scan_lds<kMaxR / kWave>(sD, R);
+    wave_excl_scan_lds<kMaxR / kWave>(sCidx, R);
+    for (int r = lane; r < R; r += kWave)
+      if (sDef[r] > 0) sDl[sCidx[r]] = r;
+    for (int e = lane; e < E; e += kWave) {
+      const int o = sT[e] - sH[e];
+      int np = 0;
+      if (consistent && o > 0) {
+        const int Oe = sO[e];
+        // the last rank with D <= x is the deficit rank holding x (ranks
+        // without deficit have empty intervals and never end up last)
+        const int dlo = upper_bound(sD, R, Oe) - 1;
+        const int dhi = upper_bound(sD, R, Oe + o - 1) - 1;
+        np = sCidx[dhi] - sCidx[dlo] + 1;
+        sDlo[e] = sCidx[dlo];
+      }
+      sNp[e] = np;
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int nP = wave_excl_scan_lds<kMaxE / kWave>(sNp, E);
+    // one lane per replica segment ("piece"), in line order
+    for (int g = lane; g < nP; g += kWave) {
+      const int e = upper_bound(sNp, E, g) - 1;
+      const int jj = g - sNp[e];
+      const int dd = sDl[sDlo[e] + jj];
+      const int Oe = sO[e], o = sT[e] - sH[e];
+      const int lo = max(Oe, sD[dd]);
+      const int hi = min(Oe + o, sD[dd] + sDef[dd]);
+      sPe[g] = e;
+      sPd[g] = dd;
+      sPc[g] = hi - lo;
+      sPl[g] = lo;
+      atomicAdd(&sRep[dd], 1);
+    }
+    __builtin_amdgcn_wave_barrier();
+    wave_excl_scan_lds<kMaxR / kWave>(sRep, R);   // first piece of each rank
+    // flat segment list: rank r's E/R home experts, then its pieces
+    for (int g = lane; g < nP; g += kWave) {
+      const int dd = sPd[g];
+      const int jj = g - sRep[dd];
+      sPj[g] = jj;
+      sF[dd * nh + sRep[dd] + nh + jj] = pad_to(sPc[g], blk);
+    }
+    for (int e = lane; e < E; e += kWave) {
+      const int r = e / nh;
+      sF[r * nh + sRep[r] + (e - r * nh)] = pad_to(sH[e], blk);
+    }
+    __builtin_amdgcn_wave_barrier();
+    wave_excl_scan_lds<(kMaxE + kMaxPieces) / kWave>(sF, E + nP);
+    // wave-wide reductions of the statistics
+    for (int o = 32; o > 0; o >>= 1) {
+      maxT = max(maxT, __shfl_xor(maxT, o, kWave));
+      maxL = max(maxL, __shfl_xor(maxL, o, kWave));
+      nOverE += __shfl_xor(nOverE, o, kWave);
+      nOverR += __shfl_xor(nOverR, o, kWave);
+    }
+    if (lane == 0) {
+      sStat[0] = maxT;
+      sStat[1] = maxL;
+      sStat[2] = nOverR;
+      sStat[3] = nOverE;
+      sStat[4] = consistent ? 0 : LBT_ST_BADCOUNT;
+      sStat[5] = nP;
+      sStat[6] = totOv;
+      sStat[7] = Ptot;
+    }
+  }
+  __syncthreads();
+  // rank r's flat entries are [fb(r), fb(r+1)) with fb(r) = r*nh + sRep[r]
+  const int nP = sStat[5];
+
+  // 3. every wave: write the blob from LDS
+  int32_t* P = plan;
+  for (int e = tid; e < E; e += kPlanThreads) {
+    const int r = e / nh;
+    const int fb = r * nh + sRep[r];
+    P[pl.T + e] = sT[e];
+    P[pl.h + e] = sH[e];
+    P[pl.O + e] = sO[e];
+    P[pl.home_row + e] = sF[fb + (e - r * nh)] - sF[fb];
+  }
+  int capflag = 0;
+  for (int r = tid; r < R; r += kPlanThreads) {
+    const int fb = r * nh + sRep[r];
+    const int fe = (r + 1) * nh + sRep[r + 1];
+    const int nrep = sRep[r + 1] - sRep[r];
+    const int nrp = sF[fe] - sF[fb];
+    P[pl.L + r] = sL[r];
+    P[pl.def + r] = sDef[r];
+    P[pl.D + r] = sD[r];
+    P[pl.n_seg + r] = nh + nrep;
+    P[pl.n_rows_padded + r] = nrp;
+    P[pl.n_slots + r] = min(nrep, B);
+    P[pl.n_remote + r] = nrep - min(nrep, B);
+    if (nrp > C) capflag = LBT_ST_CAPACITY;
+  }
+  if (capflag) atomicOr(&sStat[4], capflag);
+  if (tid == 0) P[pl.D + R] = sD[R];
+  // segment tables, one rank per wave at a time, entries across the lanes
+  constexpr int kPlanWaves = kPlanThreads / kWave;
+  for (int r = wave_id(); r < R; r += kPlanWaves) {
+    const int rep0 = sRep[r], nrep = sRep[r + 1] - rep0;
+    const int fb = r * nh + rep0;
+    const int nseg = nh + nrep;
+    const int f0 = sF[fb];
+    const long long row = (long long)r * ms;
+    for (int s = lane_id(); s < ms; s += kWave) {
+      int ex = -1, wr = -1, cnt = 0;
+      if (s < nh) {
+        ex = r * nh + s;
+        wr = ex;
+        cnt = sH[ex];
+      } else if (s < nseg) {
+        const int g = rep0 + (s - nh);
+        ex = sPe[g];
+        cnt = sPc[g];
+        wr = (s - nh < B) ? E + (s - nh) : ex;
+      }
+      P[pl.seg_expert + row + s] = ex;
+      P[pl.seg_wrow + row + s] = wr;
+      P[pl.seg_count + row + s] = cnt;
+    }
+    const long long row1 = (long long)r * (ms + 1);
+    for (int s = lane_id(); s <= ms; s += kWave)
+      P[pl.seg_start + row1 + s] = (s < nseg ? sF[fb + s] : sF[fb + nseg]) - f0;
+  }
+  for (int g = tid; g < pl.max_pieces; g += kPlanThreads) {
+    int ex = -1, dd = -1, cnt = 0, line = -1, row = -1;
+    if (g < nP) {
+      ex = sPe[g];
+      dd = sPd[g];
+      cnt = sPc[g];
+      line = sPl[g];
+      const int fb = dd * nh + sRep[dd];
+      row = sF[fb + nh + sPj[g]] - sF[fb];
+    }
+    P[pl.piece_expert + g] = ex;
+    P[pl.piece_rank + g] = dd;
+    P[pl.piece_count + g] = cnt;
+    P[pl.piece_line + g] = line;
+    P[pl.piece_row + g] = row;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int st = sStat[4];
+    P[pl.hdr + LBT_HDR_N_PIECES] = nP;
+    P[pl.hdr + LBT_HDR_MAX_T] = sStat[0];
+    P[pl.hdr + LBT_HDR_MAX_L] = sStat[1];
+    P[pl.hdr + LBT_HDR_TOTAL_OVERFLOW] = sStat[6];
+    P[pl.hdr + LBT_HDR_N_DEFICIT_RANKS] = sCidx[R];
+    P[pl.hdr + LBT_HDR_N_OVERFLOW_RANKS] = sStat[2];
+    P[pl.hdr + LBT_HDR_N_OVERFLOW_EXPERTS] = sStat[3];
+    P[pl.hdr + LBT_HDR_STATUS] = st;
+    P[pl.hdr + LBT_HDR_P] = sStat[7];
+    for (int i = LBT_HDR_P + 1; i < LBT_HDR_WORDS; ++i) P[pl.hdr + i] = 0;
+    if (status != nullptr) *status = st;
+  }
+}
+
+}  // namespace lbt

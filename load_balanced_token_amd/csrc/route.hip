@@ -2,109 +2,10 @@
 // caller-supplied ids, and the column scan that turns per-tile counts into
 // per-tile prefix offsets and the per-rank load matrix.
 //
-// Top-K: [AlignSort] -- the MoE layer routes each token to its Top-K experts
-// by gate score (DeepSeek V3/R1 add a per-expert gating bias that penalises
-// hot experts); the article names warp-shuffle sorting in thread-local
-// registers as the faster alternative to a shared-memory radix sort.  Here a
-// token belongs to one 16-lane DPP row of a wave64 (four tokens per wave):
-// lane j of the row holds experts [j*V, j*V+V); each of the K rounds takes
-// the row-wide max of order-preserving 32-bit keys with four DPP steps and
-// the lowest lane holding it (= the lowest expert index) wins.
-// Load matrix: [UltraEP] section "その仕組みは高速なエキスパート複製に依存する".
-#include "lbt_internal.h"
+// The top-K itself is in route_core.h.
+#include "route_core.h"
 
 namespace lbt {
-
-constexpr int kRouteThreads = 1024;
-constexpr int kRouteWaves = kRouteThreads / kWave;
-constexpr int kRowLanes = 16;                        // lanes per token
-constexpr int kRowsPerWave = kWave / kRowLanes;      // tokens per wave
-constexpr int kRoutePasses = kTileTokens / (kRouteWaves * kRowsPerWave);
-
-// Order-preserving map of a finite fp32 value to u32; -0.0 maps like +0.0 so
-// the two tie (IEEE equality).  Every finite value maps above 0x007FFFFF.
-__device__ __forceinline__ uint32_t ordered_key(float v) {
-  uint32_t u = __float_as_uint(v);
-  if (v == 0.0f) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// DPP lane permutations inside a 16-lane row.
-constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i inside each 8 lanes
-constexpr int kDppRowMirror = 0x140;   // lane i <-> 15-i inside each 16 lanes
-
-template <int CTRL>
-__device__ __forceinline__ int dpp(int v) {
-  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
-}
-
-// Row-wide (16-lane) reductions; every lane of the row receives the result.
-__device__ __forceinline__ uint32_t row_max_u32(uint32_t x) {
-  int v = (int)x;
-  v = (int)max((uint32_t)v, (uint32_t)dpp<kDppQuadXor1>(v));
-  v = (int)max((uint32_t)v, (uint32_t)dpp<kDppQuadXor2>(v));
-  v = (int)max((uint32_t)v, (uint32_t)dpp<kDppHalfMirror>(v));
-  v = (int)max((uint32_t)v, (uint32_t)dpp<kDppRowMirror>(v));
-  return (uint32_t)v;
-}
-
-__device__ __forceinline__ float row_max_f32(float x) {
-  int v = __float_as_int(x);
-  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp<kDppQuadXor1>(v))));
-  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp<kDppQuadXor2>(v))));
-  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp<kDppHalfMirror>(v))));
-  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp<kDppRowMirror>(v))));
-  return __int_as_float(v);
-}
-
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double x) {
-  const long long b = __double_as_longlong(x);
-  const int lo = dpp<CTRL>((int)(b & 0xFFFFFFFFll));
-  const int hi = dpp<CTRL>((int)(b >> 32));
-  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
-
-__device__ __forceinline__ double row_sum_f64(double x) {
-  x += dpp_f64<kDppQuadXor1>(x);
-  x += dpp_f64<kDppQuadXor2>(x);
-  x += dpp_f64<kDppHalfMirror>(x);
-  x += dpp_f64<kDppRowMirror>(x);
-  return x;
-}
-
-// Load lane's V logits [j*V, j*V+V) of one row (j = lane within its
-// 16-lane row); vec = 4, 2 or 1 is the widest aligned load.
-template <int V>
-__device__ __forceinline__ void load_row(const float* __restrict__ row, int E, int e0, int vec,
-                                         float (&raw)[V]) {
-  if constexpr (V % 4 == 0) {
-    if (vec == 4) {
-#pragma unroll
-      for (int v = 0; v < V; v += 4) {
-        float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (e0 + v < E) q = *reinterpret_cast<const float4*>(row + e0 + v);
-        raw[v] = q.x; raw[v + 1] = q.y; raw[v + 2] = q.z; raw[v + 3] = q.w;
-      }
-      return;
-    }
-  }
-  if constexpr (V % 2 == 0) {
-    if (vec >= 2) {
-#pragma unroll
-      for (int v = 0; v < V; v += 2) {
-        float2 q = make_float2(0.f, 0.f);
-        if (e0 + v < E) q = *reinterpret_cast<const float2*>(row + e0 + v);
-        raw[v] = q.x; raw[v + 1] = q.y;
-      }
-      return;
-    }
-  }
-#pragma unroll
-  for (int v = 0; v < V; ++v) raw[v] = (e0 + v < E) ? row[e0 + v] : 0.f;
-}
 
 template <int V>
 __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict__ logits,
@@ -112,117 +13,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict
                                                          int vec, int32_t* __restrict__ ids,
                                                          float* __restrict__ gates,
                                                          int32_t* __restrict__ tile_counts) {
-  __shared__ int hist[kMaxE];
-  // winners of each round: expert and raw logit, per wave, token row and k
-  __shared__ int s_id[kRouteWaves][kRowsPerWave][kMaxK];
-  __shared__ float s_raw[kRouteWaves][kRowsPerWave][kMaxK];
-  const int E = d.E, K = d.K;
-  const int tile = blockIdx.x;
-  const int r = tile / d.tpr, j = tile - r * d.tpr;
-  const int t0 = r * d.S + j * kTileTokens;
-  const int len = min(kTileTokens, d.S - j * kTileTokens);
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) hist[e] = 0;
-
-  const int lane = lane_id(), wv = wave_id();
-  const int row = lane / kRowLanes, rl = lane % kRowLanes;
-  const int e0 = rl * V;
-  float b[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) b[v] = (bias != nullptr && e0 + v < E) ? bias[e0 + v] : 0.f;
-
-  // all rows of this wave first (one memory latency), then the rounds
-  float rows[kRoutePasses][V];
-#pragma unroll
-  for (int u = 0; u < kRoutePasses; ++u) {
-    const int i = (u * kRouteWaves + wv) * kRowsPerWave + row;
-    if (i < len) {
-      load_row<V>(logits + ((long long)t0 + i) * E, E, e0, vec, rows[u]);
-    } else {
-#pragma unroll
-      for (int v = 0; v < V; ++v) rows[u][v] = 0.f;
-    }
-  }
-  __syncthreads();   // hist zeroed
-
-#pragma unroll
-  for (int u = 0; u < kRoutePasses; ++u) {
-    const int i = (u * kRouteWaves + wv) * kRowsPerWave + row;
-    const bool valid = i < len;
-    if (!__any(valid)) continue;
-    const float(&raw)[V] = rows[u];
-    uint32_t key[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-      key[v] = (valid && e0 + v < E) ? ordered_key(bias != nullptr ? raw[v] + b[v] : raw[v]) : 0u;
-    uint32_t taken = 0;
-    for (int k = 0; k < K; ++k) {
-      // lane-local best untaken key; strict '>' keeps the lower expert on ties
-      uint32_t best = 0;
-      int bv = 0;
-      float braw = 0.f;
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const bool ok = !((taken >> v) & 1u) && key[v] > best;
-        best = ok ? key[v] : best;
-        bv = ok ? v : bv;
-        braw = ok ? raw[v] : braw;
-      }
-      const uint32_t rmax = row_max_u32(best);
-      const bool cand = valid && best == rmax;
-      const unsigned long long m = __ballot(cand);
-      // candidates below this lane in the wave, minus those in lower rows
-      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const int p1 = __popcll(m & 0xFFFFull), p2 = __popcll(m & 0xFFFFFFFFull),
-                p3 = __popcll(m & 0xFFFFFFFFFFFFull);
-      const int lower = row == 0 ? 0 : row == 1 ? p1 : row == 2 ? p2 : p3;
-      if (cand && below == lower) {        // lowest lane of the row = lowest expert
-        taken |= 1u << bv;
-        s_id[wv][row][k] = e0 + bv;
-        s_raw[wv][row][k] = braw;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    const long long t = (long long)t0 + i;
-    double mx = 0.0, denom = 1.0;
-    if (d.score_fn == LBT_SOFTMAX) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-        if (e0 + v < E) m = fmaxf(m, raw[v]);
-      mx = (double)row_max_f32(m);
-      double s = 0.0;
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-        if (e0 + v < E) s += exp((double)raw[v] - mx);
-      denom = row_sum_f64(s);
-    }
-    double gsum = 1.0;
-    if (d.renorm) {
-      double part = 0.0;
-      for (int kk = rl; kk < K; kk += kRowLanes) {
-        const double lg = (double)s_raw[wv][row][kk];
-        part += d.score_fn == LBT_SIGMOID ? 1.0 / (1.0 + exp(-lg)) : exp(lg - mx) / denom;
-      }
-      gsum = row_sum_f64(part);
-    }
-    if (valid) {
-      for (int kk = rl; kk < K; kk += kRowLanes) {
-        const int id = s_id[wv][row][kk];
-        const double lg = (double)s_raw[wv][row][kk];
-        double g = d.score_fn == LBT_SIGMOID ? 1.0 / (1.0 + exp(-lg)) : exp(lg - mx) / denom;
-        if (d.renorm) g = g / gsum;
-        ids[t * K + kk] = id;
-        gates[t * K + kk] = (float)g;
-        atomicAdd(&hist[id], 1);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kRouteThreads)
-    tile_counts[(long long)e * d.n_tiles + tile] = hist[e];
+  __shared__ RouteSmem sm;
+  route_tile<V>(logits, bias, d, vec, blockIdx.x, ids, gates, tile_counts, sm);
 }
 
 // Histogram of caller-supplied ids, one thread per token of a tile.

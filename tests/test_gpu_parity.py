@@ -457,3 +457,4 @@ def test_dispatch_combine_with_dropped_pairs(H):
     want = oracle.bf16_to_f64(x_bits) * g_fit.sum(axis=1)[:, None]
     got = y.cpu().numpy().astype(np.float64)
     assert (np.abs(got - want) <= gu.COMBINE_RTOL * np.abs(want) + 1e-30).all()
+

@@ -4,5 +4,6 @@ TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the
 benchmark's CPU-baseline leg; never by the product path.
 """
 from .path import (SOFTMAX, SIGMOID, UNSPECIFIED, route_topk, load_matrix,  # noqa: F401
-                   imbalance, capacity, plan_balance, align_sort, dispatch,
+                   imbalance, capacity, plan_balance, plan_quota, replicas_per_rank,
+                   align_sort, dispatch,
                    dispatch_rows, combine, bf16_to_f64)

@@ -121,41 +121,87 @@ def imbalance(counts, S, K):
 
 
 # --------------------------------------------------------------------------- O3
-def capacity(E, K, S, blk, cap=0):
-    """Static rows per rank of the receive buffer.  Each rank holds exactly S*K
-    real rows in at most min(E, S*K) non-empty expert segments, each padded
-    to a multiple of blk, so S*K + min(E, S*K)*(blk-1) rows (rounded up to
-    blk) always suffice.  Static shapes: [MoonEP-GR] section "Online planning,
-    zero copy και στατικά σχήματα".  A caller may ask for a smaller cap."""
+def capacity(E, K, S, blk, cap=0, tau_max=0):
+    """Static rows per rank of the receive buffer.  A plan gives each rank at
+    most tau_max real rows (tau_max = S*K, the exact-balance contract, unless
+    the caller allows more), in at most min(E, tau_max) non-empty expert
+    segments, each padded to a multiple of blk; so tau_max + min(E, tau_max)
+    * (blk-1) rows, rounded up to blk, always suffice.  Static shapes:
+    [MoonEP-GR] section "Online planning, zero copy και στατικά σχήματα".  A
+    caller may ask for a smaller cap."""
     if cap:
         return int(cap)
-    SK = S * K
-    need = SK + min(E, SK) * (blk - 1)
+    t = int(tau_max) if tau_max else S * K
+    need = t + min(E, t) * (blk - 1)
     return ((need + blk - 1) // blk) * blk
 
 
-def plan_balance(counts, K, S, B, blk, cap=0):
-    """Online redundant-expert plan giving every rank exactly S*K pairs.
+def _split_stream_tail(T, R, tau):
+    """Fixed rule: rank r keeps the first min(L_r, tau) pairs of its home
+    stream (its experts ascending, each expert's pairs by ascending flat index
+    f), so the overflow is the stream's tail.  The overflow line lists the
+    experts in ascending order.  Returns (h, o, line order of experts)."""
+    E = len(T)
+    nh = E // R
+    h = np.zeros(E, dtype=np.int64)
+    o = np.zeros(E, dtype=np.int64)
+    for r in range(R):
+        Pe = 0
+        for e in range(r * nh, (r + 1) * nh):
+            h[e] = min(max(tau - Pe, 0), T[e])
+            o[e] = T[e] - h[e]
+            Pe += T[e]
+    return h, o, list(range(E))
+
+
+def _split_hot_first(T, R, tau):
+    """Quota rule ([UltraEP] section "その仕組みは高速なエキスパート複製に依存する":
+    the quota planner decides which hot experts get copies and how many tokens
+    each instance takes).  Reading: an overloaded rank r sheds L_r - tau
+    pairs, taking them from its hottest experts first (load descending, ties
+    to the lower expert index), each expert shedding all it has before the
+    next one sheds any; each expert keeps its first h_e pairs (by f).  The
+    overflow line lists the experts rank by rank (ascending), in that
+    shedding order inside a rank."""
+    E = len(T)
+    nh = E // R
+    h = np.zeros(E, dtype=np.int64)
+    o = np.zeros(E, dtype=np.int64)
+    order = []
+    for r in range(R):
+        mine = list(range(r * nh, (r + 1) * nh))
+        shed = max(int(sum(T[e] for e in mine)) - tau, 0)
+        hot = sorted(mine, key=lambda e: (-int(T[e]), e))
+        for e in hot:
+            o[e] = min(int(T[e]), shed)
+            shed -= o[e]
+            h[e] = T[e] - o[e]
+        order.extend(hot)
+    return h, o, order
+
+
+def _place(counts, K, S, B, blk, C, tau, split):
+    """Lay the overflow and the deficits on one line and build the plan.
 
     [MoonEP-GR] sections "Η βασική υπόσχεση του MoonEP: σταθερό φορτίο S × K"
-    (every rank receives exactly S*K; a few temporary expert copies are placed
-    on other ranks, planned online from the current router output) and "Το
-    memory contract ..." (weight rows 0..E-1 hold the ranks' experts, rows
-    E..E+B-1 are local prefetch slots found by row index; when remote experts
-    exceed the slots they are read from the home rank, still correct).
-    [UltraEP] "その仕組みは..." (replicas exist only when the plan gives them
-    work; per-token destinations come from cumulative quotas).
+    (a few temporary expert copies on other ranks, planned online from the
+    current router output) and "Το memory contract ..." (weight rows 0..E-1
+    hold the ranks' experts, rows E..E+B-1 are local prefetch slots found by
+    row index; when remote experts exceed the slots they are read from the
+    home rank, still correct).  [UltraEP] "その仕組みは..." (replicas exist only
+    when the plan gives them work; per-token destinations come from
+    cumulative quotas).
 
-    The fixed rule: home rank r keeps min(L_r, S*K) of its pairs; the overflow
-    segments fill deficit ranks in ascending order.  Readings taken:
+    Rank r keeps min(L_r, tau) pairs (which ones: `split`) and has deficit
+    def_r = tau - min(L_r, tau).  Readings taken:
       * home experts of rank r are [r*E/R, (r+1)*E/R);
-      * the pairs r keeps are the first S*K of its home stream (its experts
-        ascending, each expert's pairs by ascending flat index f = t*K + k);
-      * the overflow stream lists (expert e, o_e) for o_e > 0 in ascending e
-        (= rank ascending, expert ascending); the deficit stream lists ranks
-        with def_r > 0 in ascending r; both are laid on one line and every
-        non-empty intersection [O_e, O_e+o_e) ∩ [D_d, D_d+def_d) is one
-        replica segment (e, d, count);
+      * the overflow stream lists (expert e, o_e) for o_e > 0 in the split's
+        line order; the deficit stream lists ranks with def_r > 0 in
+        ascending r; both are laid on one line (O_e = start of e's overflow,
+        D_r = start of r's deficit) and every non-empty intersection
+        [O_e, O_e+o_e) ∩ [D_d, D_d+def_d) is one replica segment (e, d,
+        count); with tau > S*K the deficit line is longer than the overflow
+        line and its tail stays unused;
       * on rank d the replica segments, in line order, take prefetch slots
         0..B-1 (weight row E+j); further ones are remote (weight row e);
       * the segment table of rank r is its E/R home experts ascending (count
@@ -169,8 +215,6 @@ def plan_balance(counts, K, S, B, blk, cap=0):
         raise ValueError("E must be a multiple of R")
     nh = E // R
     SK = S * K
-    C = capacity(E, K, S, blk, cap)
-    home = lambda e: e // nh  # noqa: E731
 
     T = counts.sum(axis=0)
     if int(T.sum()) != R * SK:
@@ -178,24 +222,15 @@ def plan_balance(counts, K, S, B, blk, cap=0):
 
     # per-rank load and the keep / overflow / deficit split
     L = np.array([T[r * nh:(r + 1) * nh].sum() for r in range(R)], dtype=np.int64)
-    keep = np.minimum(L, SK)
+    keep = np.minimum(L, tau)
     over = L - keep
-    deficit = SK - keep
+    deficit = tau - keep
+    h, o, order = split(T, R, tau)
 
-    # home stream of each rank: expert e occupies [Pe, Pe + T_e)
-    h = np.zeros(E, dtype=np.int64)
-    o = np.zeros(E, dtype=np.int64)
-    for r in range(R):
-        Pe = 0
-        for e in range(r * nh, (r + 1) * nh):
-            h[e] = min(max(SK - Pe, 0), T[e])
-            o[e] = T[e] - h[e]
-            Pe += T[e]
-
-    # overflow stream offsets O_e and deficit stream offsets D_r
+    # overflow line offsets O_e (in line order) and deficit offsets D_r
     O = np.zeros(E, dtype=np.int64)
     acc = 0
-    for e in range(E):
+    for e in order:
         O[e] = acc
         acc += o[e]
     D = np.zeros(R + 1, dtype=np.int64)
@@ -206,18 +241,10 @@ def plan_balance(counts, K, S, B, blk, cap=0):
     D[R] = acc
 
     # replica segments = non-empty intersections, in line order
-    reps = []
-    for e in range(E):
-        if o[e] == 0:
-            continue
-        for d in range(R):
-            if deficit[d] == 0:
-                continue
-            lo = max(O[e], D[d])
-            hi = min(O[e] + o[e], D[d] + deficit[d])
-            if hi > lo:
-                reps.append((int(lo), e, d, int(hi - lo)))
-    reps.sort()
+    lo = np.maximum(O[:, None], D[None, :R])
+    hi = np.minimum((O + o)[:, None], (D[:R] + deficit)[None, :])
+    ee, dd = np.nonzero((hi > lo) & (o[:, None] > 0) & (deficit[None, :] > 0))
+    reps = sorted(zip(lo[ee, dd].tolist(), ee.tolist(), dd.tolist(), (hi - lo)[ee, dd].tolist()))
 
     # per-rank segment tables
     segs = [[(e, e, int(h[e]), None) for e in range(r * nh, (r + 1) * nh)] for r in range(R)]
@@ -255,15 +282,104 @@ def plan_balance(counts, K, S, B, blk, cap=0):
     for rp in replicas:
         rp["row"] = rep_row[(rp["expert"], rp["rank"])]
 
+    n_rep = n_slots + n_remote
     return {
-        "E": E, "K": K, "R": R, "S": S, "B": B, "blk": blk, "C": C, "SK": SK,
+        "E": E, "K": K, "R": R, "S": S, "B": B, "blk": blk, "C": C, "SK": SK, "tau": int(tau),
         "T": T, "L": L, "keep": keep, "over": over, "deficit": deficit,
-        "h": h, "o": o, "O": O, "D": D,
+        "h": h, "o": o, "O": O, "D": D, "line_order": order,
         "replicas": replicas, "segments": seg_tables,
         "n_rows_padded": n_rows_padded, "n_slots": n_slots, "n_remote": n_remote,
+        "max_replicas": int(n_rep.max()) if R else 0,
         "home_row": home_row,
         "capacity_ok": bool(n_rows_padded.max() <= C) if R else True,
     }
+
+
+def plan_balance(counts, K, S, B, blk, cap=0, tau_max=0):
+    """Online redundant-expert plan giving every rank exactly S*K pairs
+    (MoonEP's contract, [MoonEP-GR] "Η βασική υπόσχεση του MoonEP: σταθερό
+    φορτίο S × K").  The fixed rule: home rank r keeps min(L_r, S*K) of its
+    pairs, the first ones of its home stream; the overflow segments (experts
+    ascending) fill deficit ranks in ascending order; see _place for the
+    readings.  tau_max only sizes the static capacity C."""
+    counts = np.asarray(counts, dtype=np.int64)
+    R, E = counts.shape
+    C = capacity(E, K, S, blk, cap, tau_max)
+    p = _place(counts, K, S, B, blk, C, S * K, _split_stream_tail)
+    p["rule"] = "fixed"
+    p["feasible"] = p["max_replicas"] <= B
+    return p
+
+
+def replicas_per_rank(counts, K, S, tau, split):
+    """Replica segments each rank would hold at threshold tau (the same line
+    construction as _place, counting only)."""
+    counts = np.asarray(counts, dtype=np.int64)
+    R, E = counts.shape
+    T = counts.sum(axis=0)
+    nh = E // R
+    L = T.reshape(R, nh).sum(axis=1)
+    deficit = tau - np.minimum(L, tau)
+    h, o, order = split(T, R, tau)
+    O = np.zeros(E, dtype=np.int64)
+    acc = 0
+    for e in order:
+        O[e] = acc
+        acc += o[e]
+    D = np.concatenate([[0], np.cumsum(deficit)])
+    lo = np.maximum(O[:, None], D[None, :R])
+    hi = np.minimum((O + o)[:, None], (D[:R] + deficit)[None, :])
+    return ((hi > lo) & (o[:, None] > 0) & (deficit[None, :] > 0)).sum(axis=0)
+
+
+def plan_quota(counts, K, S, B, blk, tau_max=0, cap=0):
+    """UltraEP-style quota plan with a searched threshold.
+
+    [UltraEP] section "その仕組みは高速なエキスパート複製に依存する": from the
+    exact post-routing load matrix the runtime searches a target workload
+    threshold that keeps every rank under it within the available replica
+    slots; a quota-driven planner decides which hot experts get copies, where
+    they run and how many tokens each instance takes, creating a replica only
+    when it gets work; per-token destinations come from a lookup against the
+    cumulative quotas (align_sort, unchanged).
+
+    Readings taken:
+      * instances and quotas: at threshold tau every overloaded rank keeps
+        tau pairs and sheds the rest from its hottest experts first
+        (_split_hot_first); the deficit ranks (ascending) absorb the overflow
+        up to tau each (_place), each intersection being one instance;
+      * "within the replica slots" = no rank holds more than B replica
+        segments, so no weight is read from a remote home;
+      * the threshold is the smallest integer tau in [S*K, min(max_r L_r,
+        tau_max)] meeting that (at tau = max_r L_r nothing moves, so the
+        range always holds one when max_r L_r <= tau_max); the search is
+        exhaustive because the condition is not monotone in tau;
+      * if no tau <= tau_max qualifies, the plan at tau_max is used with the
+        remote fallback for replicas beyond B ("feasible" False);
+      * locality: each expert's home instance is filled first (it keeps its
+        earliest pairs up to its quota) before any demand leaves the rank.
+    tau_max = 0 means S*K (exact balance).
+    """
+    counts = np.asarray(counts, dtype=np.int64)
+    R, E = counts.shape
+    SK = S * K
+    t_max = int(tau_max) if tau_max else SK
+    if t_max < SK:
+        raise ValueError("tau_max must be at least S*K")
+    C = capacity(E, K, S, blk, cap, t_max)
+    T = counts.sum(axis=0)
+    L = T.reshape(R, E // R).sum(axis=1)
+    hi = min(int(L.max()), t_max) if R else SK
+    tau, feasible = t_max, False
+    for t in range(SK, hi + 1):
+        if replicas_per_rank(counts, K, S, t, _split_hot_first).max() <= B:
+            tau, feasible = t, True
+            break
+    p = _place(counts, K, S, B, blk, C, tau, _split_hot_first)
+    p["rule"] = "quota"
+    p["feasible"] = feasible
+    p["tau_max"] = t_max
+    return p
 
 
 # --------------------------------------------------------------------------- O4

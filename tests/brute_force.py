@@ -108,3 +108,104 @@ def all_small_routings(E, K, N):
     combos = list(itertools.combinations(range(E), K))
     for choice in itertools.product(combos, repeat=N):
         yield [list(c) for c in choice]
+
+
+def _capped_assignments(P, R, cap):
+    """Every map pair -> rank that gives no rank more than cap pairs."""
+    load = [0] * R
+    cur = [0] * P
+
+    def rec(i):
+        if i == P:
+            yield tuple(cur)
+            return
+        for d in range(R):
+            if load[d] < cap:
+                load[d] += 1
+                cur[i] = d
+                yield from rec(i + 1)
+                load[d] -= 1
+
+    yield from rec(0)
+
+
+def quota_conforming_plans(ids, E, R, S, tau):
+    """All assignments meeting the quota rule at threshold tau, stated
+    declaratively (no prefix offsets, no intervals):
+      (a) no rank holds more than tau pairs;
+      (b) rank r keeps exactly min(L_r, tau) of the pairs of its home experts;
+      (c) hot first: list r's experts by load descending, ties by lower
+          index; if an expert sends any pair away, every expert listed before
+          it sends all of its pairs away;
+      (d) an expert keeps its earliest pairs (ascending flat index);
+      (e) the pairs that leave home, taken rank by rank, in the hot-first
+          list inside a rank, then by flat index, go to non-decreasing ranks;
+      (f) a rank receives a pair from another rank only if every lower rank
+          holds exactly tau pairs."""
+    nh = E // R
+    pairs = pair_list(ids)
+    P = len(pairs)
+    expert_of = {f: e for (f, e) in pairs}
+    T = [0] * E
+    for (_, e) in pairs:
+        T[e] += 1
+    hot = {}
+    for r in range(R):
+        for pos, e in enumerate(sorted(range(r * nh, (r + 1) * nh), key=lambda x: (-T[x], x))):
+            hot[e] = pos
+    by_expert = {e: sorted(f for (f, x) in pairs if x == e) for e in range(E)}
+    leave_order = sorted(range(P), key=lambda f: (expert_of[f] // nh, hot[expert_of[f]], f))
+    found = []
+    for asg in _capped_assignments(P, R, tau):
+        ok = True
+        load = [0] * R
+        for f in range(P):
+            load[asg[f]] += 1
+        for r in range(R):
+            mine = [e for e in range(r * nh, (r + 1) * nh)]
+            L = sum(T[e] for e in mine)
+            kept = sum(1 for e in mine for f in by_expert[e] if asg[f] == r)
+            if kept != min(L, tau):
+                ok = False
+                break
+            order = sorted(mine, key=lambda x: hot[x])
+            sheds = [any(asg[f] != r for f in by_expert[e]) for e in order]
+            alls = [all(asg[f] != r for f in by_expert[e]) for e in order]
+            for i in range(len(order)):
+                if sheds[i] and not all(alls[:i]):
+                    ok = False
+            for e in mine:
+                flags = [asg[f] == r for f in by_expert[e]]
+                nk = sum(flags)
+                if flags != [True] * nk + [False] * (len(flags) - nk):
+                    ok = False
+            if not ok:
+                break
+        if not ok:
+            continue
+        moved = [asg[f] for f in leave_order if asg[f] != expert_of[f] // nh]
+        if any(moved[i] > moved[i + 1] for i in range(len(moved) - 1)):
+            continue
+        if any(not all(load[x] == tau for x in range(d)) for d in set(moved)):
+            continue
+        found.append(asg)
+    return found
+
+
+def quota_threshold(ids, E, R, S, B):
+    """Smallest tau >= S*K whose quota-rule assignment puts no more than B
+    replicas (distinct away-from-home experts) on any rank; with its
+    assignment.  Every tau is tried in ascending order."""
+    K = len(ids[0])
+    nh = E // R
+    T = [0] * E
+    for (_, e) in pair_list(ids):
+        T[e] += 1
+    maxL = max(sum(T[r * nh:(r + 1) * nh]) for r in range(R))
+    for tau in range(S * K, maxL + 1):
+        plans = quota_conforming_plans(ids, E, R, S, tau)
+        assert len(plans) == 1, (tau, len(plans))
+        reps = replicas_of(plans[0], ids, E, R)
+        if all(len([x for x in reps if x[1] == r]) <= B for r in range(R)):
+            return tau, plans[0]
+    raise AssertionError("tau = max load always qualifies")

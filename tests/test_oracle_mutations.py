@@ -20,14 +20,15 @@ from tests import brute_force as bf
 from tests.test_oracle_plan import check_invariants, _tiny_cases
 
 GOLDEN = sorted(glob.glob(os.path.join(os.path.dirname(__file__), "golden", "W*.json")))
+QGOLDEN = sorted(glob.glob(os.path.join(os.path.dirname(__file__), "golden", "Q*.json")))
 
 MUTATIONS = {
     "tie_to_higher_index": ("np.lexsort((expert, -key)", "np.lexsort((-expert, -key)"),
     "sigmoid_sign": ("np.exp(-l64)", "np.exp(l64)"),
     "source_rank_modulo": ("np.arange(N, dtype=np.int64) // S", "np.arange(N, dtype=np.int64) % S"),
-    "home_keep_off_by_one": ("h[e] = min(max(SK - Pe, 0), T[e])", "h[e] = min(max(SK - Pe - 1, 0), T[e])"),
+    "home_keep_off_by_one": ("h[e] = min(max(tau - Pe, 0), T[e])", "h[e] = min(max(tau - Pe - 1, 0), T[e])"),
     "inclusive_overflow_prefix": ("        O[e] = acc\n        acc += o[e]", "        acc += o[e]\n        O[e] = acc"),
-    "intersection_min_for_max": ("lo = max(O[e], D[d])", "lo = min(O[e], D[d])"),
+    "intersection_min_for_max": ("lo = np.maximum(O[:, None], D[None, :R])", "lo = np.minimum(O[:, None], D[None, :R])"),
     "slot_bound_inclusive": ("if j < B:", "if j <= B:"),
     "remote_row_wrong": ("wrow = e\n", "wrow = E + j\n"),
     "pad_always_adds_block": ("pad = lambda c: ((c + blk - 1) // blk) * blk",
@@ -37,6 +38,16 @@ MUTATIONS = {
     "sentinel_minus_one": ("= P                 # padding sentinel", "= P - 1             # padding sentinel"),
     "combine_subtracts": ("y = term if y is None else y + term", "y = term if y is None else y - term"),
     "stable_rank_unstable": ('order = np.argsort(flat, kind="stable")', 'order = np.argsort(-flat, kind="stable")[::-1]'),
+    # quota planner
+    "quota_coldest_first": ("key=lambda e: (-int(T[e]), e))", "key=lambda e: (int(T[e]), e))"),
+    "quota_tie_to_higher_index": ("key=lambda e: (-int(T[e]), e))", "key=lambda e: (-int(T[e]), -e))"),
+    "quota_sheds_one_extra": ("shed = max(int(sum(T[e] for e in mine)) - tau, 0)",
+                              "shed = max(int(sum(T[e] for e in mine)) - tau + 1, 0)"),
+    "quota_line_in_index_order": ("order.extend(hot)", "order.extend(mine)"),
+    "quota_search_skips_SK": ("for t in range(SK, hi + 1):", "for t in range(SK + 1, hi + 1):"),
+    "quota_slot_bound_strict": ("_split_hot_first).max() <= B:", "_split_hot_first).max() < B:"),
+    "quota_fallback_at_SK": ("tau, feasible = t_max, False", "tau, feasible = SK, False"),
+    "quota_deficit_from_SK": ("    deficit = tau - keep\n", "    deficit = S * K - np.minimum(L, S * K)\n"),
 }
 
 
@@ -80,6 +91,35 @@ def _pins(o):
             check_invariants(ids, plan, al)
             plans = bf.rule_conforming_plans(ids.tolist(), E, R, S)
             ok = len(plans) == 1 and tuple(int(s) // plan["C"] for s in al["slot"]) == plans[0]
+        except Exception:
+            ok = False
+        failures += not ok
+    for path in QGOLDEN:
+        g = json.load(open(path))
+        sh = g["shape"]
+        E, R, S, K, blk = (sh[k] for k in ("E", "R", "S", "K", "blk"))
+        for c in g["cases"]:
+            try:
+                ids = np.array(g["ids"])
+                counts = o.load_matrix(ids, R, S, E)
+                plan = o.plan_quota(counts, K, S, c["B"], blk, c["tau_max"])
+                al = o.align_sort(ids, plan)
+                ok = (plan["tau"] == c["tau"] and plan["feasible"] == c["feasible"]
+                      and all(plan[k].tolist() == c[k] for k in ("h", "O", "D", "deficit"))
+                      and plan["segments"] == c["segments"] and plan["replicas"] == c["replicas"]
+                      and al["slot"].tolist() == c["slot"])
+            except Exception:
+                ok = False
+            failures += not ok
+    for case in (0, 3, 6, 9):
+        ids, E, R, S, K = [c for c in _tiny_cases() if len(c[0]) * c[4] <= 9][case]
+        try:
+            counts = o.load_matrix(ids, R, S, E)
+            maxL = int(o.imbalance(counts, S, K)["L"].max())
+            plan = o.plan_quota(counts, K, S, 1, 1, tau_max=maxL)
+            al = o.align_sort(ids, plan)
+            tau, asg = bf.quota_threshold(ids.tolist(), E, R, S, 1)
+            ok = plan["tau"] == tau and tuple(int(s) // plan["C"] for s in al["slot"]) == asg
         except Exception:
             ok = False
         failures += not ok

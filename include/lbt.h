@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LBT_VERSION 1
+#define LBT_VERSION 2
 
 /* return codes */
 #define LBT_OK 0
@@ -68,7 +68,7 @@ extern "C" {
 
 /* Supported limits: 1 <= R <= E <= 512, E % R == 0, 1 <= K <= min(E, 64),
  * S >= 0, H >= 8 with H % 8 == 0, B >= 0, 1 <= blk <= 1024, cap % blk == 0,
- * R*C and P below 2^31. */
+ * tau_max == 0 or S*K <= tau_max < 2^30, R*C and P below 2^31. */
 typedef struct lbt_shape {
   int32_t E;        /* routed experts */
   int32_t K;        /* experts per token */
@@ -80,6 +80,9 @@ typedef struct lbt_shape {
   int32_t score_fn; /* LBT_SOFTMAX or LBT_SIGMOID */
   int32_t renorm;   /* 1: gates renormalised over the K chosen */
   int32_t cap;      /* rows per rank of recv; 0 = worst case (always enough) */
+  int32_t tau_max;  /* largest per-rank load a plan may give a rank; 0 = S*K
+                       (exact balance).  Sizes C and bounds lbt_plan_quota's
+                       threshold search; lbt_plan_balance always uses S*K. */
 } lbt_shape;
 
 /* Sizes (elements unless stated) and plan-blob word offsets. */
@@ -91,17 +94,17 @@ typedef struct lbt_sizes {
   int64_t tiles_per_rank; /* ceil(S / tile_tokens) */
   int64_t n_tiles;        /* R * tiles_per_rank */
   int64_t work_words;     /* int32 words of the route/histogram workspace */
-  int64_t max_seg;        /* segment-table entries per rank: E/R + min(E - E/R, SK) */
+  int64_t max_seg;        /* segment-table entries per rank: E/R + min(E - E/R, tau_max) */
   int64_t max_pieces;     /* replica-segment table entries: E + R */
   int64_t plan_words;     /* int32 words of the plan blob */
   /* plan blob layout: word offsets of each int32 field */
   int64_t off_hdr;        /* [16] see LBT_HDR_* */
   int64_t off_T;          /* [E]  T_e = pairs routed to expert e */
   int64_t off_h;          /* [E]  pairs of e kept on its home rank */
-  int64_t off_O;          /* [E]  exclusive prefix of the overflow o_e = T_e - h_e */
+  int64_t off_O;          /* [E]  start of e's overflow o_e = T_e - h_e on the line */
   int64_t off_home_row;   /* [E]  padded start row of e's home segment */
   int64_t off_L;          /* [R]  L_r = load of rank r's home experts */
-  int64_t off_def;        /* [R]  def_r = S*K - min(L_r, S*K) */
+  int64_t off_def;        /* [R]  def_r = tau - min(L_r, tau), tau = LBT_HDR_TAU */
   int64_t off_D;          /* [R+1] exclusive prefix of def_r (D[R] = total) */
   int64_t off_n_seg;      /* [R]  used segment-table entries: E/R + replicas */
   int64_t off_n_rows_padded; /* [R] padded rows used by rank r (<= C) */
@@ -117,6 +120,8 @@ typedef struct lbt_sizes {
   int64_t off_piece_count;  /*   pairs */
   int64_t off_piece_line;   /*   start on the shared overflow/deficit line */
   int64_t off_piece_row;    /*   padded start row on rank d */
+  int64_t search_groups;    /* workgroups of lbt_plan_quota's threshold search */
+  int64_t off_search;       /* [search_groups] per-group search results (internal) */
 } lbt_sizes;
 
 /* plan header words */
@@ -129,6 +134,9 @@ typedef struct lbt_sizes {
 #define LBT_HDR_N_OVERFLOW_EXPERTS 6
 #define LBT_HDR_STATUS 7      /* LBT_ST_* bits raised by the plan */
 #define LBT_HDR_P 8           /* sum of the load matrix */
+#define LBT_HDR_TAU 9         /* per-rank load threshold the plan used (S*K for plan_balance) */
+#define LBT_HDR_MAX_REPLICAS 10 /* most replica segments on one rank */
+#define LBT_HDR_FEASIBLE 11   /* 1 when no rank holds more than B replicas (no remote reads) */
 #define LBT_HDR_WORDS 16
 
 /* Fill *out for shape *s.  Pure host function.  LBT_EINVAL/LBT_EUNSUPPORTED
@@ -177,6 +185,29 @@ int lbt_histogram(const lbt_shape* s, const int32_t* ids, int32_t* counts, int32
 int lbt_plan_balance(const lbt_shape* s, const int32_t* counts, int32_t* plan, int32_t* status,
                      void* stream);
 
+/* Quota plan with a searched threshold: same blob layout and meaning as
+ * lbt_plan_balance, so lbt_align_sort, lbt_dispatch and lbt_combine take it
+ * unchanged.  [UltraEP] section "その仕組みは高速なエキスパート複製に依存する"
+ * (from the exact load matrix, search a workload threshold that keeps every
+ * rank under it within the replica slots; a quota-driven planner decides
+ * which hot experts get copies, where, and how many tokens each instance
+ * takes; replicas only where there is work; fully on the GPU).  Rule at
+ * threshold tau: an overloaded rank keeps tau pairs and sheds the rest from
+ * its hottest experts first (load descending, ties to the lower index), each
+ * expert keeping its earliest pairs; the overflow line lists experts rank by
+ * rank in that order; deficit ranks (def_r = tau - min(L_r, tau)) fill in
+ * ascending order, one replica segment per overlap.  tau is the smallest
+ * integer in [S*K, min(max_r L_r, tau_max)] for which no rank holds more than
+ * B replica segments (every candidate is checked, in parallel); when none
+ * qualifies, tau = tau_max and replicas beyond B are remote
+ * (LBT_HDR_FEASIBLE = 0).  Every rank then holds at most tau pairs.  Two
+ * launches (search, then plan); the blob's search region is scratch.
+ *   counts [R, E] int32 in
+ *   plan   [plan_words] int32 out (LBT_HDR_TAU holds the threshold)
+ *   status int32 out (may be NULL) */
+int lbt_plan_quota(const lbt_shape* s, const int32_t* counts, int32_t* plan, int32_t* status,
+                   void* stream);
+
 /* Block-aligned sort: destination row of every pair.  [AlignSort] (pairs
  * sorted by expert, each expert's share padded to the GEMM block; the
  * permutation records source -> destination); [UltraEP] (per-token
@@ -186,7 +217,7 @@ int lbt_plan_balance(const lbt_shape* s, const int32_t* counts, int32_t* plan, i
  * (d, line, row) -> rank d, row + o - line.
  *   ids        [N, K] int32 in (the ids the histogram counted)
  *   work       the workspace filled by lbt_route_topk / lbt_histogram
- *   plan       the blob from lbt_plan_balance
+ *   plan       the blob from lbt_plan_balance or lbt_plan_quota
  *   slot       [P] int32 out: d*C + row, or -1 if it did not fit the capacity
  *   sorted_ids [R*C] int32 out: row -> f; padding rows below a rank's
  *              n_rows_padded hold P; rows at or past it are not written

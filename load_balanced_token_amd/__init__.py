@@ -1,5 +1,5 @@
 """MI355X-native load-balanced MoE token path: router top-K, load histogram,
-online S*K balancing plan, block-aligned sort, zero-copy dispatch, combine.
+online S*K balancing plan (or a quota plan with a searched threshold), block-aligned sort, zero-copy dispatch, combine.
 
 The compute lives in liblbt.so (HIP, gfx950) behind include/lbt.h; this
 package only marshals arguments.  Importing it does not load the library;

@@ -32,14 +32,18 @@ HDR_N_OVERFLOW_RANKS = 5
 HDR_N_OVERFLOW_EXPERTS = 6
 HDR_STATUS = 7
 HDR_P = 8
+HDR_TAU = 9
+HDR_MAX_REPLICAS = 10
+HDR_FEASIBLE = 11
 
 EXPORTS = ("lbt_query_sizes", "lbt_route_topk", "lbt_histogram", "lbt_plan_balance",
-           "lbt_align_sort", "lbt_dispatch", "lbt_combine", "lbt_strerror", "lbt_version")
+           "lbt_plan_quota", "lbt_align_sort", "lbt_dispatch", "lbt_combine", "lbt_strerror",
+           "lbt_version")
 
 
 class LbtShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("E", "K", "R", "S", "H", "B", "blk", "score_fn", "renorm", "cap")]
+                ("E", "K", "R", "S", "H", "B", "blk", "score_fn", "renorm", "cap", "tau_max")]
 
 
 _SIZE_FIELDS = (
@@ -49,6 +53,7 @@ _SIZE_FIELDS = (
     "off_n_seg", "off_n_rows_padded", "off_n_slots", "off_n_remote",
     "off_seg_expert", "off_seg_wrow", "off_seg_count", "off_seg_start",
     "off_piece_expert", "off_piece_rank", "off_piece_count", "off_piece_line", "off_piece_row",
+    "search_groups", "off_search",
 )
 
 
@@ -78,6 +83,7 @@ def lib() -> ctypes.CDLL:
         L.lbt_route_topk.argtypes = [SP, P, P, P, P, P, P, P]
         L.lbt_histogram.argtypes = [SP, P, P, P, P, P]
         L.lbt_plan_balance.argtypes = [SP, P, P, P, P]
+        L.lbt_plan_quota.argtypes = [SP, P, P, P, P]
         L.lbt_align_sort.argtypes = [SP, P, P, P, P, P, P, P, P, P]
         L.lbt_dispatch.argtypes = [SP, P, P, P, P]
         L.lbt_combine.argtypes = [SP, P, P, P, ctypes.c_int32, P, P]
@@ -108,6 +114,7 @@ class Shape:
     score_fn: int = SIGMOID
     renorm: int = 0
     cap: int = 0
+    tau_max: int = 0
 
     def c(self) -> LbtShape:
         return LbtShape(*(int(getattr(self, f.name)) for f in dataclasses.fields(self)))
@@ -228,6 +235,18 @@ class Path:
             _stream(stream))
         _check(rc, "lbt_plan_balance")
 
+    # a3, quota variant
+    def plan_quota(self, counts, plan, status=None, stream=None):
+        torch = _torch()
+        s, z = self.shape, self.sizes
+        rc = lib().lbt_plan_quota(
+            ctypes.byref(self._c),
+            _ptr(counts, torch.int32, s.R * s.E, "counts"),
+            _ptr(plan, torch.int32, z["plan_words"], "plan"),
+            _ptr(status, torch.int32, 1, "status"),
+            _stream(stream))
+        _check(rc, "lbt_plan_quota")
+
     # a4
     def align_sort(self, ids, work, plan, slot, sorted_ids, block_wrow, block_expert,
                    status=None, stream=None):
@@ -273,12 +292,16 @@ class Path:
             _stream(stream))
         _check(rc, "lbt_combine")
 
-    def step(self, logits, x, buf, sel_bias=None, out=None, stream=None):
+    def step(self, logits, x, buf, sel_bias=None, out=None, stream=None, planner="fixed"):
         """One pass of the whole path; ``out`` defaults to recv (identity
-        expert).  Returns nothing; results land in ``buf``."""
+        expert); ``planner`` is "fixed" (lbt_plan_balance) or "quota"
+        (lbt_plan_quota).  Returns nothing; results land in ``buf``."""
+        if planner not in ("fixed", "quota"):
+            raise LbtError(f"unknown planner {planner!r}")
         self.route_topk(logits, buf["ids"], buf["gates"], buf["counts"], buf["work"],
                         sel_bias=sel_bias, stream=stream)
-        self.plan_balance(buf["counts"], buf["plan"], buf["status"], stream=stream)
+        plan = self.plan_balance if planner == "fixed" else self.plan_quota
+        plan(buf["counts"], buf["plan"], buf["status"], stream=stream)
         self.align_sort(buf["ids"], buf["work"], buf["plan"], buf["slot"], buf["sorted_ids"],
                         buf["block_wrow"], buf["block_expert"], buf["status"], stream=stream)
         self.dispatch(x, buf["slot"], buf["recv"], stream=stream)

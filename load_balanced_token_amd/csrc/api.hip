@@ -21,9 +21,11 @@ int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z) {
   if (s->cap % blk != 0) return LBT_EINVAL;
 
   const long long nh = E / R, N = R * S, P = N * K, SK = S * K;
+  if (s->tau_max != 0 && (s->tau_max < SK || s->tau_max >= (1 << 30))) return LBT_EINVAL;
+  const long long tmax = s->tau_max != 0 ? s->tau_max : SK;
   long long C = s->cap;
   if (C == 0) {
-    const long long need = SK + (E < SK ? E : SK) * (blk - 1);
+    const long long need = tmax + (E < tmax ? E : tmax) * (blk - 1);
     C = (need + blk - 1) / blk * blk;
     if (C == 0) C = blk;
   }
@@ -32,7 +34,10 @@ int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z) {
   if (P >= (1LL << 31) || R * C >= (1LL << 31) || N * H / 8 >= (1LL << 40)) return LBT_EUNSUPPORTED;
   if (SK >= (1LL << 30)) return LBT_EUNSUPPORTED;
 
-  const long long ms = nh + ((E - nh) < SK ? (E - nh) : SK);
+  const long long ms = nh + ((E - nh) < tmax ? (E - nh) : tmax);
+  const long long n_cand = tmax - SK + 1;
+  long long groups = (n_cand + kSearchThreads - 1) / kSearchThreads;
+  if (groups > kMaxSearchGroups) groups = kMaxSearchGroups;
   const long long mp = E + R;
   PlanLayout pl;
   long long off = 0;
@@ -62,12 +67,14 @@ int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z) {
   pl.piece_count = take(mp);
   pl.piece_line = take(mp);
   pl.piece_row = take(mp);
+  pl.search_groups = (int)groups;
+  pl.search = take(groups);
   pl.total = (int)off;
 
   if (d != nullptr) {
     d->E = (int)E; d->K = (int)K; d->R = (int)R; d->S = (int)S; d->H = (int)H; d->B = (int)B;
     d->blk = (int)blk; d->score_fn = s->score_fn; d->renorm = s->renorm;
-    d->nh = (int)nh; d->N = (int)N; d->P = P; d->SK = (int)SK; d->C = (int)C;
+    d->nh = (int)nh; d->N = (int)N; d->P = P; d->SK = (int)SK; d->tau_max = (int)tmax; d->C = (int)C;
     d->n_blocks = (int)(C / blk); d->tpr = (int)tpr; d->n_tiles = (int)nt; d->pl = pl;
   }
   if (z != nullptr) {
@@ -85,6 +92,7 @@ int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z) {
     z->off_piece_expert = pl.piece_expert; z->off_piece_rank = pl.piece_rank;
     z->off_piece_count = pl.piece_count; z->off_piece_line = pl.piece_line;
     z->off_piece_row = pl.piece_row;
+    z->search_groups = pl.search_groups; z->off_search = pl.search;
   }
   return LBT_OK;
 }
@@ -145,6 +153,15 @@ int lbt_plan_balance(const lbt_shape* s, const int32_t* counts, int32_t* plan, i
   if (rc) return rc;
   if (!counts || !plan) return LBT_EINVAL;
   return hip_rc(launch_plan(d, counts, plan, status, static_cast<hipStream_t>(stream)));
+}
+
+int lbt_plan_quota(const lbt_shape* s, const int32_t* counts, int32_t* plan, int32_t* status,
+                   void* stream) {
+  Dims d;
+  const int rc = make_dims(s, &d, nullptr);
+  if (rc) return rc;
+  if (!counts || !plan) return LBT_EINVAL;
+  return hip_rc(launch_plan_quota(d, counts, plan, status, static_cast<hipStream_t>(stream)));
 }
 
 int lbt_align_sort(const lbt_shape* s, const int32_t* ids, const int32_t* work, const int32_t* plan,

@@ -17,6 +17,8 @@ constexpr int kMaxE = 512;
 constexpr int kMaxR = 512;
 constexpr int kMaxPieces = kMaxE + kMaxR;
 constexpr int kMaxK = 64;
+constexpr int kSearchThreads = 256;     // threshold candidates per search workgroup pass
+constexpr int kMaxSearchGroups = 1024;  // workgroups of the threshold search
 
 // Plan blob word offsets (mirrors lbt_sizes, 32-bit for the device).
 struct PlanLayout {
@@ -24,6 +26,7 @@ struct PlanLayout {
   int hdr, T, h, O, home_row, L, def, D, n_seg, n_rows_padded, n_slots, n_remote;
   int seg_expert, seg_wrow, seg_count, seg_start;
   int piece_expert, piece_rank, piece_count, piece_line, piece_row;
+  int search, search_groups;
   int total;
 };
 
@@ -34,6 +37,7 @@ struct Dims {
   int N;         // R * S tokens
   long long P;   // N * K pairs
   int SK;        // S * K
+  int tau_max;   // largest per-rank load a plan may give (>= SK)
   int C;         // rows per rank
   int n_blocks;  // C / blk
   int tpr;       // tiles per rank
@@ -52,6 +56,8 @@ hipError_t launch_histogram(const Dims& d, const int32_t* ids, int32_t* work, in
 hipError_t launch_tile_scan(const Dims& d, int32_t* work, int32_t* counts, hipStream_t st);
 hipError_t launch_plan(const Dims& d, const int32_t* counts, int32_t* plan, int32_t* status,
                        hipStream_t st);
+hipError_t launch_plan_quota(const Dims& d, const int32_t* counts, int32_t* plan,
+                             int32_t* status, hipStream_t st);
 hipError_t launch_align(const Dims& d, const int32_t* ids, const int32_t* work, const int32_t* plan,
                         int32_t* slot, int32_t* sorted_ids, int32_t* block_wrow,
                         int32_t* block_expert, int32_t* status, hipStream_t st);

@@ -1,6 +1,6 @@
 // The online balancing plan: one workgroup turns the per-expert loads into
 // the replica segments and per-rank segment tables, entirely on the device.
-// The plan body as a device function; the plan kernel wraps it.
+// The plan body as a device function; the plan kernels wrap it.
 //
 // [MoonEP-GR] sections "Η βασική υπόσχεση του MoonEP: σταθερό φορτίο S × K"
 // (each rank receives exactly S*K; a few temporary expert copies, planned
@@ -10,15 +10,19 @@
 // planner's cu_seqlens; replicas beyond the slots are read from home).
 // [UltraEP] section "その仕組みは高速なエキスパート複製に依存する" (the
 // planner runs fully on the GPU, no host round trip inside a layer;
-// replicas exist only when given work).
+// replicas exist only when given work; a quota planner decides which hot
+// experts get copies).
 //
-// The rule: rank r keeps min(L_r, S*K) of its pairs, the first ones of its
-// home stream; the overflow of every expert (experts ascending) and the
-// deficit of every rank (ranks ascending) are laid on one line, and each
-// non-empty overlap is a replica segment ("piece").  The workgroup sums the
-// load matrix, one wave then builds the whole plan in LDS with DPP prefix
-// sums and binary searches (no workgroup barriers on the critical path),
-// and the workgroup writes the blob.  E <= 512 experts, R <= 512 ranks.
+// At threshold tau, rank r keeps min(L_r, tau) of its pairs.  Which pairs
+// overflow: the fixed rule (tau = S*K) sheds the tail of the home stream
+// (experts ascending); the quota rule sheds from the hottest experts first
+// (load descending, ties to the lower index).  The overflow of every expert
+// (in line order: experts ascending, or rank by rank in shedding order) and
+// the deficit tau - min(L_r, tau) of every rank (ranks ascending) are laid on
+// one line, and each non-empty overlap is a replica segment ("piece").  The
+// workgroup sums the load matrix, one wave then builds the whole plan in LDS
+// with DPP prefix sums and binary searches (no workgroup barriers on the
+// critical path), and the workgroup writes the blob.  E <= 512, R <= 512.
 #pragma once
 #include "lbt_internal.h"
 
@@ -45,20 +49,30 @@ struct PlanSmem {
   int sPe[kMaxPieces], sPd[kMaxPieces], sPc[kMaxPieces], sPl[kMaxPieces],
       sPj[kMaxPieces];
   int sF[kMaxE + kMaxPieces + 1];  // flat segment padded lengths -> starts
-  int sStat[8];  // max_T, max_L, over ranks, over experts, status, nP, totOv, Ptot
+  int sLam[kMaxE];        // quota rule: line position of expert e inside its rank block
+  int sPerm[kMaxE];       // quota rule: expert at line position
+  int sHx[kMaxE + 1];     // quota rule: loads in line order, then exclusive prefix
+  // max_T, max_L, over ranks, over experts, status, nP, totOv, Ptot, tau, max replicas
+  int sStat[12];
 
 };
 
 // The plan from T_e (in m.sT and m.sX, written and made visible by a
-// workgroup barrier before the call); 1024 threads; writes the whole blob
-// and *status.
-__device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, int32_t* __restrict__ plan,
+// workgroup barrier before the call; for HOT also m.sLam / m.sPerm) at
+// threshold tau; 1024 threads; writes the whole blob and *status.
+template <bool HOT>
+__device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int tau,
+                                          int32_t* __restrict__ plan,
                                           int32_t* __restrict__ status) {
   auto& sT = m.sT; auto& sX = m.sX; auto& sH = m.sH; auto& sO = m.sO; auto& sNp = m.sNp;
   auto& sDlo = m.sDlo; auto& sL = m.sL; auto& sDef = m.sDef; auto& sD = m.sD;
   auto& sCidx = m.sCidx; auto& sDl = m.sDl; auto& sRep = m.sRep; auto& sPe = m.sPe;
   auto& sPd = m.sPd; auto& sPc = m.sPc; auto& sPl = m.sPl; auto& sPj = m.sPj; auto& sF = m.sF;
   auto& sStat = m.sStat;
+  auto& sLam = m.sLam; auto& sPerm = m.sPerm; auto& sHx = m.sHx;
+  // line position of expert e, expert at line position g (identity for the fixed rule)
+  auto lam = [&](int e) { return HOT ? sLam[e] : e; };
+  auto perm = [&](int g) { return HOT ? sPerm[g] : g; };
   const int tid = threadIdx.x;
   const int E = d.E, R = d.R, nh = d.nh, SK = d.SK, B = d.B, blk = d.blk, C = d.C;
   const PlanLayout pl = d.pl;
@@ -69,28 +83,43 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, int32_t* _
     const int lane = tid;
     const int Ptot = wave_excl_scan_lds<kMaxE / kWave>(sX, E);
     const bool consistent = (long long)Ptot == (long long)R * SK;
+    if (HOT) {
+      for (int g = lane; g < E; g += kWave) sHx[g] = sT[sPerm[g]];
+      __builtin_amdgcn_wave_barrier();
+      wave_excl_scan_lds<kMaxE / kWave>(sHx, E);
+    }
     int maxT = 0, nOverE = 0;
     for (int e = lane; e < E; e += kWave) {
       const int r = e / nh;
       const int T = sT[e];
-      const int Pe = sX[e] - sX[r * nh];        // position in r's home stream
-      const int h = consistent ? min(max(SK - Pe, 0), T) : 0;
+      int h;
+      if (HOT) {
+        // shed L_r - tau from the hottest experts: o_e = clamp(L_r - tau - HP_e, 0, T_e)
+        // with HP_e the load of the experts hotter than e in its rank
+        const int L = sX[(r + 1) * nh] - sX[r * nh];
+        const int HP = sHx[sLam[e]] - sHx[r * nh];
+        h = T - min(max(L - tau - HP, 0), T);
+      } else {
+        const int Pe = sX[e] - sX[r * nh];      // position in r's home stream
+        h = min(max(tau - Pe, 0), T);
+      }
+      if (!consistent) h = 0;
       sH[e] = h;
-      sO[e] = consistent ? T - h : 0;
+      sO[lam(e)] = consistent ? T - h : 0;
       maxT = max(maxT, T);
       nOverE += (consistent && T - h > 0);
     }
     int maxL = 0, nOverR = 0;
     for (int r = lane; r < R; r += kWave) {
       const int L = sX[(r + 1) * nh] - sX[r * nh];
-      const int def = consistent ? SK - min(L, SK) : 0;
+      const int def = consistent ? tau - min(L, tau) : 0;
       sL[r] = L;
       sDef[r] = def;
       sD[r] = def;
       sCidx[r] = def > 0;
       sRep[r] = 0;
       maxL = max(maxL, L);
-      nOverR += (L > SK);
+      nOverR += (L > tau);
     }
     __builtin_amdgcn_wave_barrier();
     const int totOv = wave_excl_scan_lds<kMaxE / kWave>(sO, E);
@@ -98,28 +127,30 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, int32_t* _
     wave_excl_scan_lds<kMaxR / kWave>(sCidx, R);
     for (int r = lane; r < R; r += kWave)
       if (sDef[r] > 0) sDl[sCidx[r]] = r;
-    for (int e = lane; e < E; e += kWave) {
+    for (int g = lane; g < E; g += kWave) {     // line position g, expert perm(g)
+      const int e = perm(g);
       const int o = sT[e] - sH[e];
       int np = 0;
       if (consistent && o > 0) {
-        const int Oe = sO[e];
+        const int Oe = sO[g];
         // the last rank with D <= x is the deficit rank holding x (ranks
         // without deficit have empty intervals and never end up last)
         const int dlo = upper_bound(sD, R, Oe) - 1;
         const int dhi = upper_bound(sD, R, Oe + o - 1) - 1;
         np = sCidx[dhi] - sCidx[dlo] + 1;
-        sDlo[e] = sCidx[dlo];
+        sDlo[g] = sCidx[dlo];
       }
-      sNp[e] = np;
+      sNp[g] = np;
     }
     __builtin_amdgcn_wave_barrier();
     const int nP = wave_excl_scan_lds<kMaxE / kWave>(sNp, E);
     // one lane per replica segment ("piece"), in line order
     for (int g = lane; g < nP; g += kWave) {
-      const int e = upper_bound(sNp, E, g) - 1;
-      const int jj = g - sNp[e];
-      const int dd = sDl[sDlo[e] + jj];
-      const int Oe = sO[e], o = sT[e] - sH[e];
+      const int ge = upper_bound(sNp, E, g) - 1;   // line position of the piece's expert
+      const int e = perm(ge);
+      const int jj = g - sNp[ge];
+      const int dd = sDl[sDlo[ge] + jj];
+      const int Oe = sO[ge], o = sT[e] - sH[e];
       const int lo = max(Oe, sD[dd]);
       const int hi = min(Oe + o, sD[dd] + sDef[dd]);
       sPe[g] = e;
@@ -150,7 +181,12 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, int32_t* _
       nOverE += __shfl_xor(nOverE, o, kWave);
       nOverR += __shfl_xor(nOverR, o, kWave);
     }
+    int maxRep = 0;
+    for (int r = lane; r < R; r += kWave) maxRep = max(maxRep, sRep[r + 1] - sRep[r]);
+    maxRep = wave_max(maxRep);
     if (lane == 0) {
+      sStat[8] = tau;
+      sStat[9] = maxRep;
       sStat[0] = maxT;
       sStat[1] = maxL;
       sStat[2] = nOverR;
@@ -172,7 +208,7 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, int32_t* _
     const int fb = r * nh + sRep[r];
     P[pl.T + e] = sT[e];
     P[pl.h + e] = sH[e];
-    P[pl.O + e] = sO[e];
+    P[pl.O + e] = sO[lam(e)];
     P[pl.home_row + e] = sF[fb + (e - r * nh)] - sF[fb];
   }
   int capflag = 0;
@@ -248,7 +284,10 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, int32_t* _
     P[pl.hdr + LBT_HDR_N_OVERFLOW_EXPERTS] = sStat[3];
     P[pl.hdr + LBT_HDR_STATUS] = st;
     P[pl.hdr + LBT_HDR_P] = sStat[7];
-    for (int i = LBT_HDR_P + 1; i < LBT_HDR_WORDS; ++i) P[pl.hdr + i] = 0;
+    P[pl.hdr + LBT_HDR_TAU] = sStat[8];
+    P[pl.hdr + LBT_HDR_MAX_REPLICAS] = sStat[9];
+    P[pl.hdr + LBT_HDR_FEASIBLE] = sStat[9] <= B ? 1 : 0;
+    for (int i = LBT_HDR_FEASIBLE + 1; i < LBT_HDR_WORDS; ++i) P[pl.hdr + i] = 0;
     if (status != nullptr) *status = st;
   }
 }

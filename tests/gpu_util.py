@@ -7,7 +7,8 @@ import load_balanced_token_amd as lbt
 from load_balanced_token_amd.binding import (HDR_N_PIECES, HDR_MAX_T, HDR_MAX_L,
                                              HDR_TOTAL_OVERFLOW, HDR_N_DEFICIT_RANKS,
                                              HDR_N_OVERFLOW_RANKS, HDR_N_OVERFLOW_EXPERTS,
-                                             HDR_STATUS, HDR_P)
+                                             HDR_STATUS, HDR_P, HDR_TAU, HDR_MAX_REPLICAS,
+                                             HDR_FEASIBLE)
 
 GATE_RTOL = 1e-6       # gates vs the fp64 oracle (relative)
 COMBINE_RTOL = 1e-6    # |y - y_ref| <= 1e-6 * sum_k |g * out|
@@ -18,10 +19,10 @@ def torch():
     return _t
 
 
-def shape_of(w, cap=0, renorm=0):
+def shape_of(w, cap=0, renorm=0, tau_max=0):
     return lbt.Shape(E=w.E, K=w.K, R=w.R, S=w.S, H=w.H, B=w.B, blk=w.blk,
                      score_fn=lbt.SOFTMAX if w.score == "softmax" else lbt.SIGMOID,
-                     renorm=renorm, cap=cap)
+                     renorm=renorm, cap=cap, tau_max=tau_max)
 
 
 def oracle_score(w):
@@ -43,8 +44,9 @@ def d2h(t_):
     return a
 
 
-def run_front(shape, logits, sel_bias=None):
-    """route_topk + plan_balance + align_sort on the GPU; host copies."""
+def run_front(shape, logits, sel_bias=None, planner="fixed"):
+    """route_topk + plan (plan_balance or plan_quota) + align_sort on the GPU;
+    host copies."""
     t = torch()
     path = lbt.Path(shape)
     buf = path.alloc()
@@ -53,7 +55,8 @@ def run_front(shape, logits, sel_bias=None):
     lg = h2d(logits)
     sb = None if sel_bias is None else h2d(np.asarray(sel_bias, np.float32))
     path.route_topk(lg, buf["ids"], buf["gates"], buf["counts"], buf["work"], sel_bias=sb)
-    path.plan_balance(buf["counts"], buf["plan"], buf["status"])
+    plan = path.plan_balance if planner == "fixed" else path.plan_quota
+    plan(buf["counts"], buf["plan"], buf["status"])
     path.align_sort(buf["ids"], buf["work"], buf["plan"], buf["slot"], buf["sorted_ids"],
                     buf["block_wrow"], buf["block_expert"], buf["status"])
     t.cuda.synchronize()
@@ -65,11 +68,16 @@ def run_front(shape, logits, sel_bias=None):
     return out
 
 
-def run_oracle(w, logits, sel_bias=None, B=None, blk=None, cap=0, renorm=False):
+def run_oracle(w, logits, sel_bias=None, B=None, blk=None, cap=0, renorm=False, planner="fixed",
+               tau_max=0):
     ids, gates = oracle.route_topk(logits, w.K, oracle_score(w), sel_bias=sel_bias, renorm=renorm)
     counts = oracle.load_matrix(ids, w.R, w.S, w.E)
-    plan = oracle.plan_balance(counts, w.K, w.S, w.B if B is None else B,
-                               w.blk if blk is None else blk, cap)
+    B_ = w.B if B is None else B
+    blk_ = w.blk if blk is None else blk
+    if planner == "fixed":
+        plan = oracle.plan_balance(counts, w.K, w.S, B_, blk_, cap, tau_max)
+    else:
+        plan = oracle.plan_quota(counts, w.K, w.S, B_, blk_, tau_max, cap)
     al = oracle.align_sort(ids, plan)
     return {"ids": ids, "gates": gates, "counts": counts, "plan": plan, "align": al}
 
@@ -112,10 +120,13 @@ def check_plan(pf, op, P):
     assert hdr[HDR_MAX_L] == op["L"].max()
     assert hdr[HDR_TOTAL_OVERFLOW] == op["o"].sum()
     assert hdr[HDR_N_DEFICIT_RANKS] == (op["deficit"] > 0).sum()
-    assert hdr[HDR_N_OVERFLOW_RANKS] == (op["L"] > SK).sum()
+    assert hdr[HDR_N_OVERFLOW_RANKS] == (op["L"] > op["tau"]).sum()
     assert hdr[HDR_N_OVERFLOW_EXPERTS] == (op["o"] > 0).sum()
     assert hdr[HDR_P] == P
     assert hdr[HDR_STATUS] == 0
+    assert hdr[HDR_TAU] == op["tau"]
+    assert hdr[HDR_MAX_REPLICAS] == op["max_replicas"]
+    assert hdr[HDR_FEASIBLE] == int(op["max_replicas"] <= op["B"])
 
 
 def check_align(g, o, R, C):

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(binding.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.lbt_version() == 1
+    assert L.lbt_version() == 2
 
 
 def test_sizes_match_oracle_capacity_for_every_workload():
@@ -39,21 +39,37 @@ def test_sizes_match_oracle_capacity_for_every_workload():
         assert z["max_seg"] == nh + min(w.E - nh, w.SK)
         assert z["n_tiles"] == w.R * -(-w.S // z["tile_tokens"])
         assert z["work_words"] == 2 * w.E * z["n_tiles"]
+        assert z["search_groups"] == 1          # tau_max = S*K: one candidate
         # offsets are increasing and the blob ends at plan_words
         offs = [z[k] for k in binding._SIZE_FIELDS if k.startswith("off_")]
         assert offs == sorted(offs) and offs[-1] < z["plan_words"]
+        assert z["off_search"] + z["search_groups"] == z["plan_words"]
+
+
+@pytest.mark.parametrize("name,x", [("dsv3", 2), ("wideep", 3), ("decode128", 2), ("tiny", 4)])
+def test_sizes_with_a_larger_threshold_bound(name, x):
+    """tau_max sizes the static capacity like the oracle's capacity()."""
+    w = WORKLOADS[name]
+    z = lbt.query_sizes(lbt.Shape(w.E, w.K, w.R, w.S, w.H, w.B, w.blk, tau_max=x * w.SK))
+    assert z["C"] == oracle.capacity(w.E, w.K, w.S, w.blk, 0, x * w.SK)
+    nh = w.E // w.R
+    assert z["max_seg"] == nh + min(w.E - nh, x * w.SK)
+    cand = x * w.SK - w.SK + 1
+    assert z["search_groups"] == min(-(-cand // 256), 1024)
+    assert z["off_search"] + z["search_groups"] == z["plan_words"]
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(E=10, R=4), -1), (dict(K=9), -1), (dict(H=60), -1), (dict(H=0), -1),
     (dict(blk=0), -1), (dict(S=-1), -1), (dict(score_fn=5), -1), (dict(cap=17), -1),
     (dict(E=1024, R=8), -3), (dict(K=65, E=128, R=8), -3), (dict(blk=2048), -3),
+    (dict(tau_max=15), -1), (dict(tau_max=1 << 30), -1), (dict(tau_max=-2), -1),
 ])
 def test_invalid_shapes_are_rejected(kw, code):
-    base = dict(E=8, K=2, R=4, S=8, H=64, B=1, blk=16, score_fn=1, renorm=0, cap=0)
+    base = dict(E=8, K=2, R=4, S=8, H=64, B=1, blk=16, score_fn=1, renorm=0, cap=0, tau_max=0)
     base.update(kw)
     sh = binding.LbtShape(*[base[f] for f in ("E", "K", "R", "S", "H", "B", "blk",
-                                              "score_fn", "renorm", "cap")])
+                                              "score_fn", "renorm", "cap", "tau_max")])
     z = binding.LbtSizes()
     assert lbt.lib().lbt_query_sizes(ctypes.byref(sh), ctypes.byref(z)) == code
     assert lbt.lib().lbt_strerror(code)
@@ -69,6 +85,8 @@ def test_host_checks_reject_bad_pointers_before_any_launch():
     assert L.lbt_combine(ctypes.byref(sh), P(0x1000), P(0x2000), P(0x3000), 0, P(0x4008), None) == -1
     assert L.lbt_combine(ctypes.byref(sh), P(0x1000), P(0x2000), P(0x3000), 7, P(0x4000), None) == -1
     assert L.lbt_plan_balance(ctypes.byref(sh), None, P(0x1000), None, None) == -1
+    assert L.lbt_plan_quota(ctypes.byref(sh), None, P(0x1000), None, None) == -1
+    assert L.lbt_plan_quota(ctypes.byref(sh), P(0x1000), None, None, None) == -1
     assert L.lbt_route_topk(ctypes.byref(sh), None, None, P(1), P(2), P(3), P(4), None) == -1
     assert L.lbt_align_sort(ctypes.byref(sh), P(1), P(2), None, P(3), P(4), P(5), P(6), None, None) == -1
     assert L.lbt_histogram(None, P(1), P(2), P(3), None, None) == -1

@@ -106,7 +106,7 @@ def cpu_baseline(name, sample_S):
     }
 
 
-def decode_latency(path, buf, w, x, n_steps, dev):
+def decode_latency(path, buf, w, x, n_steps, dev, planner="fixed"):
     """p50/p99 latency of one whole step over ``n_steps`` fresh routings.
 
     Every routing is resident in HBM; the step (route -> plan -> align ->
@@ -127,7 +127,7 @@ def decode_latency(path, buf, w, x, n_steps, dev):
 
     def body():
         torch.index_select(all_logits, 0, idx, out=cur)
-        path.step(cur[0], x, buf)
+        path.step(cur[0], x, buf, planner=planner)
         idx.add_(1)
 
     with torch.cuda.stream(stream):        # warm up outside the graph
@@ -157,6 +157,40 @@ def decode_latency(path, buf, w, x, n_steps, dev):
             "note": "graph replay incl. the gather of fresh router logits"}
 
 
+def planner_report(lbt, torch, w, counts, B, tau_max, dev):
+    """Both planners on the same load matrix: latency (median of 20 back-to-back
+    calls; the quota planner is its search launch plus its plan launch), the
+    threshold, replica segments, the most on one rank, remote replicas."""
+    import numpy as np
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name in ("fixed", "quota"):
+        shape = lbt.Shape(E=w.E, K=w.K, R=w.R, S=w.S, H=w.H, B=B, blk=w.blk,
+                          score_fn=lbt.SOFTMAX if w.score == "softmax" else lbt.SIGMOID,
+                          tau_max=tau_max)
+        p = lbt.Path(shape)
+        plan = torch.empty(p.sizes["plan_words"], dtype=torch.int32, device=dev)
+        fn = p.plan_balance if name == "fixed" else p.plan_quota
+        for _ in range(3):
+            fn(counts, plan)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
+        ev[0].record(stream)
+        for i in range(20):
+            fn(counts, plan)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.median([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(20)]))
+        pf = lbt.plan_fields(plan.cpu().numpy(), p.sizes, w.R, w.E)
+        hdr = pf["hdr"]
+        out[name] = {"us": us, "tau": int(hdr[9]), "tau_over_SK": float(hdr[9]) / max(1, w.SK),
+                     "replica_segments": int(hdr[0]), "max_replicas_per_rank": int(hdr[10]),
+                     "remote_replicas": int(pf["n_remote"].sum()), "feasible": bool(hdr[11]),
+                     "search_candidates": (tau_max or w.SK) - w.SK + 1 if name == "quota" else 0}
+    out["B"] = B
+    out["tau_max"] = tau_max or w.SK
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +204,11 @@ def main():
                     help="fresh-routing graph replays for the decode workloads")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--planner", choices=("fixed", "quota"), default="fixed",
+                    help="planner inside the timed step")
+    ap.add_argument("--B", type=int, default=-1, help="prefetch slots per rank (default: workload's)")
+    ap.add_argument("--tau-max-x", type=float, default=2.0,
+                    help="quota planner's threshold bound, in units of S*K")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -189,8 +228,12 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     w = WORKLOADS[args.workload]
+    if args.B >= 0:
+        w = w.with_(B=args.B)
+    tau_max = int(round(args.tau_max_x * w.SK))
     shape = lbt.Shape(E=w.E, K=w.K, R=w.R, S=w.S, H=w.H, B=w.B, blk=w.blk,
-                      score_fn=lbt.SOFTMAX if w.score == "softmax" else lbt.SIGMOID)
+                      score_fn=lbt.SOFTMAX if w.score == "softmax" else lbt.SIGMOID,
+                      tau_max=tau_max if args.planner == "quota" else 0)
     path = lbt.Path(shape)
     C = path.sizes["C"]
     buf = path.alloc(dev)
@@ -208,13 +251,14 @@ def main():
 
     stream = torch.cuda.current_stream()
     names = ["route", "plan", "align", "dispatch", "combine"]
+    plan_fn = path.plan_balance if args.planner == "fixed" else path.plan_quota
 
     def step(evs=None):
         rec = (lambda i: evs[i].record(stream)) if evs is not None else (lambda i: None)
         rec(0)
         path.route_topk(logits, buf["ids"], buf["gates"], buf["counts"], buf["work"])
         rec(1)
-        path.plan_balance(buf["counts"], buf["plan"], buf["status"])
+        plan_fn(buf["counts"], buf["plan"], buf["status"])
         rec(2)
         path.align_sort(buf["ids"], buf["work"], buf["plan"], buf["slot"], buf["sorted_ids"],
                         buf["block_wrow"], buf["block_expert"], buf["status"])
@@ -249,10 +293,10 @@ def main():
     plan2 = torch.empty_like(buf["plan"])
     pev = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
     for _ in range(3):
-        path.plan_balance(buf["counts"], plan2)
+        plan_fn(buf["counts"], plan2)
     pev[0].record(stream)
     for i in range(20):
-        path.plan_balance(buf["counts"], plan2)
+        plan_fn(buf["counts"], plan2)
         pev[i + 1].record(stream)
     torch.cuda.synchronize()
     plan_alone_us = float(np.median([pev[i].elapsed_time(pev[i + 1]) * 1e3 for i in range(20)]))
@@ -260,6 +304,7 @@ def main():
 
     status = int(buf["status"].item())
     hdr = buf["plan"][:16].cpu().numpy()
+    planners = planner_report(lbt, torch, w, buf["counts"], w.B, tau_max, dev)
     if args.calib_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
         b = torch.empty_like(a)
@@ -290,6 +335,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "E": w.E, "K": w.K, "R": w.R, "S": w.S, "H": w.H,
                    "B": w.B, "blk": w.blk, "C": C, "token_slots_per_step": w.P,
+                   "planner": args.planner,
                    "gate": w.score, "combine_accumulate": "fp32", "y": "fp32",
                    "expert": "identity (out = recv)"},
         "roofline": {"bound": "hbm", "kernel": "k_combine",
@@ -308,13 +354,15 @@ def main():
         "max_vio": float(hdr[1]) * w.E / w.P - 1.0,
         "rank_imbalance_before": float(hdr[2]) / w.SK - 1.0,
         "replica_segments": int(hdr[0]),
+        "planners": planners,
         "status": status,
         "device": torch.cuda.get_device_name(0),
     }
     if w.name.startswith("decode"):
         print(f"[bench] decode latency over {args.decode_steps} fresh routings (HIP graph)",
               file=sys.stderr, flush=True)
-        result["decode_latency"] = decode_latency(path, buf, w, x, args.decode_steps, dev)
+        result["decode_latency"] = decode_latency(path, buf, w, x, args.decode_steps, dev,
+                                                  args.planner)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         sample_S = args.cpu_sample_S or max(1, min(w.S, 32768 // w.R))

@@ -120,8 +120,6 @@ typedef struct lbt_sizes {
   int64_t off_piece_count;  /*   pairs */
   int64_t off_piece_line;   /*   start on the shared overflow/deficit line */
   int64_t off_piece_row;    /*   padded start row on rank d */
-  int64_t search_groups;    /* workgroups of lbt_plan_quota's threshold search */
-  int64_t off_search;       /* [search_groups] per-group search results (internal) */
 } lbt_sizes;
 
 /* plan header words */
@@ -198,10 +196,10 @@ int lbt_plan_balance(const lbt_shape* s, const int32_t* counts, int32_t* plan, i
  * rank in that order; deficit ranks (def_r = tau - min(L_r, tau)) fill in
  * ascending order, one replica segment per overlap.  tau is the smallest
  * integer in [S*K, min(max_r L_r, tau_max)] for which no rank holds more than
- * B replica segments (every candidate is checked, in parallel); when none
- * qualifies, tau = tau_max and replicas beyond B are remote
- * (LBT_HDR_FEASIBLE = 0).  Every rank then holds at most tau pairs.  Two
- * launches (search, then plan); the blob's search region is scratch.
+ * B replica segments (candidates checked in ascending batches of 1024 in
+ * parallel, stopping at the first batch holding one); when none qualifies,
+ * tau = tau_max and replicas beyond B are remote (LBT_HDR_FEASIBLE = 0).
+ * Every rank then holds at most tau pairs.  One workgroup, one launch.
  *   counts [R, E] int32 in
  *   plan   [plan_words] int32 out (LBT_HDR_TAU holds the threshold)
  *   status int32 out (may be NULL) */

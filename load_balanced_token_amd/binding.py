@@ -53,7 +53,6 @@ _SIZE_FIELDS = (
     "off_n_seg", "off_n_rows_padded", "off_n_slots", "off_n_remote",
     "off_seg_expert", "off_seg_wrow", "off_seg_count", "off_seg_start",
     "off_piece_expert", "off_piece_rank", "off_piece_count", "off_piece_line", "off_piece_row",
-    "search_groups", "off_search",
 )
 
 

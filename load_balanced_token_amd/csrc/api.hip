@@ -35,9 +35,7 @@ int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z) {
   if (SK >= (1LL << 30)) return LBT_EUNSUPPORTED;
 
   const long long ms = nh + ((E - nh) < tmax ? (E - nh) : tmax);
-  const long long n_cand = tmax - SK + 1;
-  long long groups = (n_cand + kSearchThreads - 1) / kSearchThreads;
-  if (groups > kMaxSearchGroups) groups = kMaxSearchGroups;
+
   const long long mp = E + R;
   PlanLayout pl;
   long long off = 0;
@@ -67,8 +65,6 @@ int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z) {
   pl.piece_count = take(mp);
   pl.piece_line = take(mp);
   pl.piece_row = take(mp);
-  pl.search_groups = (int)groups;
-  pl.search = take(groups);
   pl.total = (int)off;
 
   if (d != nullptr) {
@@ -92,7 +88,6 @@ int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z) {
     z->off_piece_expert = pl.piece_expert; z->off_piece_rank = pl.piece_rank;
     z->off_piece_count = pl.piece_count; z->off_piece_line = pl.piece_line;
     z->off_piece_row = pl.piece_row;
-    z->search_groups = pl.search_groups; z->off_search = pl.search;
   }
   return LBT_OK;
 }

@@ -17,8 +17,6 @@ constexpr int kMaxE = 512;
 constexpr int kMaxR = 512;
 constexpr int kMaxPieces = kMaxE + kMaxR;
 constexpr int kMaxK = 64;
-constexpr int kSearchThreads = 256;     // threshold candidates per search workgroup pass
-constexpr int kMaxSearchGroups = 1024;  // workgroups of the threshold search
 
 // Plan blob word offsets (mirrors lbt_sizes, 32-bit for the device).
 struct PlanLayout {
@@ -26,7 +24,6 @@ struct PlanLayout {
   int hdr, T, h, O, home_row, L, def, D, n_seg, n_rows_padded, n_slots, n_remote;
   int seg_expert, seg_wrow, seg_count, seg_start;
   int piece_expert, piece_rank, piece_count, piece_line, piece_row;
-  int search, search_groups;
   int total;
 };
 

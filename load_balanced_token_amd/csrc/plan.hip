@@ -47,6 +47,7 @@ __device__ __forceinline__ void column_sums(const int32_t* __restrict__ counts, 
 __device__ __forceinline__ int hot_position(const int* sT, int e, int nh) {
   const int r0 = (e / nh) * nh, T = sT[e];
   int pos = 0;
+#pragma unroll 8
   for (int x = r0; x < r0 + nh; ++x) {
     const int Tx = sT[x];
     pos += (Tx > T) || (Tx == T && x < e);
@@ -60,35 +61,30 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict
   __shared__ PlanSmem m;
   if (threadIdx.x < 12) m.sStat[threadIdx.x] = 0;
   column_sums<kPlanThreads>(counts, d.E, d.R, m.sT, m.sX);
-  // the threshold-search region is unused by this rule; keep every word defined
-  for (int i = threadIdx.x; i < d.pl.search_groups; i += kPlanThreads) plan[d.pl.search + i] = 0;
   __syncthreads();
   plan_core<false>(d, m, d.SK, plan, status);
 }
 
-// ---- quota plan: threshold search ------------------------------------------
+// ---- quota plan ---------------------------------------------------------------
 //
 // [UltraEP] section "その仕組みは高速なエキスパート複製に依存する": the runtime
 // searches a target workload threshold keeping every rank under it within
-// the replica slots.  Replica needs are not monotone in the threshold, so
-// every candidate tau in [S*K, min(max_r L_r, tau_max)] is checked, one
-// candidate per thread across the grid, and the smallest that qualifies wins.
+// the replica slots, then a quota planner decides which hot experts get
+// copies, where, and how many tokens each takes.  Replica needs are not
+// monotone in the threshold, so the smallest qualifying tau in
+// [S*K, min(max_r L_r, tau_max)] is found by checking candidates in
+// ascending batches of 1024, one per thread, stopping at the first batch
+// that holds one.  With the slot counts the pages use, tau = S*K qualifies
+// and one batch suffices.
 //
 // For one tau the check needs no per-expert pass: the overflow of rank r is
-// the first L_r - tau pairs of its shedding order, so with SQ = inclusive
-// prefix of the loads in that order, the experts an overflow interval
-// [a, b) of rank r touches are indices upper_bound(SQ_r, a) ..
-// upper_bound(SQ_r, b-1).  Deficit ranks (ascending) consume the overflow
-// line rank by rank; each rank's replica count is the number of experts its
-// interval touches.  Cost per candidate: O(R) steps plus two binary searches
-// per (deficit rank, overflowing rank) contact.
-
-struct SearchSmem {
-  int sT[kMaxE];
-  int sQ[kMaxE + 1];    // loads in shedding order, then inclusive prefix within each rank
-  int sL[kMaxR];
-  int sRed[kSearchThreads / kWave + 1];
-};
+// the first L_r - tau pairs of its shedding order, so with Q = inclusive
+// prefix of the loads in that order, expert j of rank r holds overflow
+// positions [Q_r[j-1], Q_r[j]).  Deficit ranks (ascending) consume the
+// overflow line rank by rank; a deficit rank's replica count is the number
+// of experts its interval touches.  A cursor on the expert holding the next
+// unconsumed position only moves forward, so one candidate costs O(R) steps
+// plus one step per replica segment.
 
 // Whether threshold tau puts at most B replica segments on every rank.
 __device__ __forceinline__ bool tau_fits(int tau, const int* sQ, const int* sL, int R, int nh,
@@ -96,6 +92,7 @@ __device__ __forceinline__ bool tau_fits(int tau, const int* sQ, const int* sL, 
   int ro = 0;
   while (ro < R && sL[ro] <= tau) ++ro;
   int off = 0;   // consumed part of rank ro's overflow
+  int ei = 0;    // expert (shedding order) holding position off
   for (int d = 0; d < R && ro < R; ++d) {
     int cap = tau - sL[d];
     if (cap <= 0) continue;
@@ -103,14 +100,20 @@ __device__ __forceinline__ bool tau_fits(int tau, const int* sQ, const int* sL, 
     while (cap > 0 && ro < R) {
       const int ov = sL[ro] - tau;
       const int take = min(cap, ov - off);
+      const int end = off + take;
       const int* q = sQ + ro * nh;
-      cnt += upper_bound(q, nh, off + take - 1) - upper_bound(q, nh, off) + 1;
-      off += take;
+      int ej = ei;                      // expert holding end - 1
+      while (ej < nh - 1 && q[ej] < end) ++ej;
+      cnt += ej - ei + 1;
+      off = end;
       cap -= take;
       if (off == ov) {
         off = 0;
+        ei = 0;
         ++ro;
         while (ro < R && sL[ro] <= tau) ++ro;
+      } else {
+        ei = q[ej] == end ? ej + 1 : ej;
       }
     }
     if (cnt > B) return false;
@@ -118,86 +121,98 @@ __device__ __forceinline__ bool tau_fits(int tau, const int* sQ, const int* sL, 
   return true;
 }
 
-__global__ __launch_bounds__(kSearchThreads) void k_tau_search(const int32_t* __restrict__ counts,
-                                                               Dims d, int32_t* __restrict__ plan) {
-  __shared__ SearchSmem m;
-  const int E = d.E, R = d.R, nh = d.nh, tid = threadIdx.x;
-  column_sums<kSearchThreads>(counts, E, R, m.sT, nullptr);
-  __syncthreads();
-  for (int e = tid; e < E; e += kSearchThreads) {
-    const int r0 = (e / nh) * nh;
-    m.sQ[r0 + hot_position(m.sT, e, nh)] = m.sT[e];
+// The same check for one tau by one wave, lanes over ranks (R <= 64): the
+// overflow, expert-count and deficit offsets of every rank come from wave
+// prefix sums; a deficit rank's interval [a, b) on the line touches experts
+// N(a) .. N(b-1), N(x) = index along the line of the expert holding x, found
+// by a search over the ranks' overflow offsets and one inside the rank.
+// Returns the same value in every lane.  ov_off / nv_off: R + 1 ints of LDS
+// owned by the wave.
+__device__ __forceinline__ bool tau_fits_wave(int tau, const int* sQ, const int* sL, int R, int nh,
+                                              int B, int* ov_off, int* nv_off) {
+  const int r = lane_id();
+  const int L = r < R ? sL[r] : 0;
+  const int ov = r < R ? max(L - tau, 0) : 0;
+  const int df = r < R ? max(tau - L, 0) : 0;
+  // experts of rank r that shed anything: those holding positions [0, ov)
+  const int nv = ov > 0 ? upper_bound(sQ + r * nh, nh, ov - 1) + 1 : 0;
+  const int ov_in = wave_incl_scan_dpp(ov), nv_in = wave_incl_scan_dpp(nv);
+  const int df_ex = wave_incl_scan_dpp(df) - df;
+  const int tot = __builtin_amdgcn_readlane(ov_in, kWave - 1);
+  if (r < R) {
+    ov_off[r] = ov_in - ov;
+    nv_off[r] = nv_in - nv;
   }
-  __syncthreads();
-  // inclusive prefix within each rank block: exclusive scan over all, then
-  // rebase on the rank's first entry
-  block_excl_scan<kSearchThreads, kMaxE / kSearchThreads>(m.sQ, E, m.sRed);
-  int maxL = 0;
-  for (int r = tid; r < R; r += kSearchThreads) {
-    const int base = m.sQ[r * nh];
-    m.sL[r] = m.sQ[(r + 1) * nh] - base;
-    maxL = max(maxL, m.sL[r]);
-  }
-  __syncthreads();
-  // turn exclusive prefixes into per-rank inclusive ones (each thread its own
-  // entries; the rank bases are read before any entry is rewritten)
-  int incl[kMaxE / kSearchThreads];
-#pragma unroll
-  for (int i = 0; i < kMaxE / kSearchThreads; ++i) {
-    const int g = tid + i * kSearchThreads;
-    incl[i] = g < E ? m.sQ[g + 1] - m.sQ[(g / nh) * nh] : 0;
-  }
-  maxL = wave_max(maxL);
-  if (lane_id() == 0) m.sRed[wave_id()] = maxL;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kMaxE / kSearchThreads; ++i) {
-    const int g = tid + i * kSearchThreads;
-    if (g < E) m.sQ[g] = incl[i];
-  }
-  maxL = 0;
-  for (int w = 0; w < kSearchThreads / kWave; ++w) maxL = max(maxL, m.sRed[w]);
-  __syncthreads();
-
-  const int hi = min(maxL, d.tau_max);
-  const int stride = gridDim.x * kSearchThreads;
-  int best = INT_MAX;
-  for (int tau = d.SK + blockIdx.x * kSearchThreads + tid; tau <= hi; tau += stride) {
-    if (tau_fits(tau, m.sQ, m.sL, R, nh, d.B)) {
-      best = tau;
-      break;
-    }
-  }
-  // workgroup minimum
-  for (int o = 32; o > 0; o >>= 1) best = min(best, __shfl_xor(best, o, kWave));
-  if (lane_id() == 0) m.sRed[wave_id()] = best;
-  __syncthreads();
-  if (tid == 0) {
-    int b = INT_MAX;
-    for (int w = 0; w < kSearchThreads / kWave; ++w) b = min(b, m.sRed[w]);
-    plan[d.pl.search + blockIdx.x] = b;
-  }
+  if (r == 0) ov_off[R] = tot;
+  __builtin_amdgcn_wave_barrier();
+  auto line_expert = [&](int x) {       // index along the line of the expert holding x
+    const int rx = upper_bound(ov_off, R, x) - 1;
+    return nv_off[rx] + upper_bound(sQ + rx * nh, nh, x - ov_off[rx]);
+  };
+  const int a = df_ex, b = min(df_ex + df, tot);
+  const int pieces = (df > 0 && a < b) ? line_expert(b - 1) - line_expert(a) + 1 : 0;
+  const bool bad = __any(pieces > B);
+  __builtin_amdgcn_wave_barrier();      // ov_off / nv_off may be rewritten next
+  return !bad;
 }
 
-// ---- quota plan: the plan at the chosen threshold ---------------------------
 __global__ __launch_bounds__(kPlanThreads) void k_plan_quota(const int32_t* __restrict__ counts,
                                                             Dims d, int32_t* __restrict__ plan,
                                                             int32_t* __restrict__ status) {
   __shared__ PlanSmem m;
-  const int E = d.E, nh = d.nh, tid = threadIdx.x;
-  if (tid < 12) m.sStat[tid] = tid == 10 ? INT_MAX : 0;   // [10]: smallest qualifying tau
-  column_sums<kPlanThreads>(counts, E, d.R, m.sT, m.sX);
+  __shared__ int sQ[kMaxE];     // per-rank inclusive prefix of the loads in shedding order
+  __shared__ int sLr[kMaxR];    // L_r
+  __shared__ int sTmp[kPlanThreads / kWave + 1];
+  __shared__ int sOvOff[kPlanThreads / kWave][kWave + 1];   // per-wave scratch of the first stage
+  __shared__ int sNvOff[kPlanThreads / kWave][kWave + 1];
+  const int E = d.E, R = d.R, nh = d.nh, tid = threadIdx.x;
+  // [10]: smallest qualifying tau, [11]: max_r L_r
+  if (tid < 12) m.sStat[tid] = tid == 10 ? INT_MAX : 0;
+  column_sums<kPlanThreads>(counts, E, R, m.sT, m.sX);
   __syncthreads();
   for (int e = tid; e < E; e += kPlanThreads) {
     const int g = (e / nh) * nh + hot_position(m.sT, e, nh);
     m.sLam[e] = g;
     m.sPerm[g] = e;
+    m.sHx[g] = m.sT[e];
   }
-  int best = INT_MAX;
-  for (int i = tid; i < d.pl.search_groups; i += kPlanThreads) best = min(best, plan[d.pl.search + i]);
-  for (int o = 32; o > 0; o >>= 1) best = min(best, __shfl_xor(best, o, kWave));
-  if (lane_id() == 0 && best != INT_MAX) atomicMin(&m.sStat[10], best);
   __syncthreads();
+  block_excl_scan<kPlanThreads, kMaxE / kPlanThreads + 1>(m.sHx, E, sTmp);
+  for (int g = tid; g < E; g += kPlanThreads) sQ[g] = m.sHx[g + 1] - m.sHx[(g / nh) * nh];
+  int maxL = 0;
+  for (int r = tid; r < R; r += kPlanThreads) {
+    sLr[r] = m.sHx[(r + 1) * nh] - m.sHx[r * nh];
+    maxL = max(maxL, sLr[r]);
+  }
+  maxL = wave_max(maxL);
+  if (lane_id() == 0 && maxL > 0) atomicMax(&m.sStat[11], maxL);
+  __syncthreads();
+
+  const int hi = min(m.sStat[11], d.tau_max);
+  constexpr int kPlanWaves = kPlanThreads / kWave;
+  int first = d.SK;
+  if (R <= kWave) {
+    // first stage: the kPlanWaves smallest candidates, one per wave (low latency)
+    const int tau = d.SK + wave_id();
+    if (tau <= hi && tau_fits_wave(tau, sQ, sLr, R, nh, d.B, sOvOff[wave_id()], sNvOff[wave_id()]) &&
+        lane_id() == 0)
+      atomicMin(&m.sStat[10], tau);
+    __syncthreads();
+    first = m.sStat[10] != INT_MAX ? INT_MAX : d.SK + kPlanWaves;
+    __syncthreads();   // every thread has read the result before the next stage writes
+  }
+  // then ascending batches, one candidate per thread (high throughput)
+  for (int base = first; base <= hi; base += kPlanThreads) {
+    const int tau = base + tid;
+    const bool ok = tau <= hi && tau_fits(tau, sQ, sLr, R, nh, d.B);
+    const unsigned long long bal = __ballot(ok);
+    // lanes hold ascending candidates: the lowest set lane has the wave's smallest
+    if (bal != 0ull && lane_id() == __ffsll((long long)bal) - 1) atomicMin(&m.sStat[10], tau);
+    __syncthreads();
+    const int found = m.sStat[10];
+    __syncthreads();
+    if (found != INT_MAX) break;
+  }
   const int tau = m.sStat[10] == INT_MAX ? d.tau_max : m.sStat[10];
   plan_core<true>(d, m, tau, plan, status);
 }
@@ -210,10 +225,6 @@ hipError_t launch_plan(const Dims& d, const int32_t* counts, int32_t* plan, int3
 
 hipError_t launch_plan_quota(const Dims& d, const int32_t* counts, int32_t* plan, int32_t* status,
                              hipStream_t st) {
-  hipLaunchKernelGGL(k_tau_search, dim3(d.pl.search_groups), dim3(kSearchThreads), 0, st, counts,
-                     d, plan);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_plan_quota, dim3(1), dim3(kPlanThreads), 0, st, counts, d, plan, status);
   return hipGetLastError();
 }

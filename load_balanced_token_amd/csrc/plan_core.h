@@ -58,8 +58,9 @@ struct PlanSmem {
 };
 
 // The plan from T_e (in m.sT and m.sX, written and made visible by a
-// workgroup barrier before the call; for HOT also m.sLam / m.sPerm) at
-// threshold tau; 1024 threads; writes the whole blob and *status.
+// workgroup barrier before the call; for HOT also m.sLam, m.sPerm and m.sHx
+// = exclusive prefix of the loads in line order) at threshold tau; 1024
+// threads; writes the whole blob and *status.
 template <bool HOT>
 __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int tau,
                                           int32_t* __restrict__ plan,
@@ -83,11 +84,6 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
     const int lane = tid;
     const int Ptot = wave_excl_scan_lds<kMaxE / kWave>(sX, E);
     const bool consistent = (long long)Ptot == (long long)R * SK;
-    if (HOT) {
-      for (int g = lane; g < E; g += kWave) sHx[g] = sT[sPerm[g]];
-      __builtin_amdgcn_wave_barrier();
-      wave_excl_scan_lds<kMaxE / kWave>(sHx, E);
-    }
     int maxT = 0, nOverE = 0;
     for (int e = lane; e < E; e += kWave) {
       const int r = e / nh;

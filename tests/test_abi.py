@@ -39,11 +39,9 @@ def test_sizes_match_oracle_capacity_for_every_workload():
         assert z["max_seg"] == nh + min(w.E - nh, w.SK)
         assert z["n_tiles"] == w.R * -(-w.S // z["tile_tokens"])
         assert z["work_words"] == 2 * w.E * z["n_tiles"]
-        assert z["search_groups"] == 1          # tau_max = S*K: one candidate
         # offsets are increasing and the blob ends at plan_words
         offs = [z[k] for k in binding._SIZE_FIELDS if k.startswith("off_")]
         assert offs == sorted(offs) and offs[-1] < z["plan_words"]
-        assert z["off_search"] + z["search_groups"] == z["plan_words"]
 
 
 @pytest.mark.parametrize("name,x", [("dsv3", 2), ("wideep", 3), ("decode128", 2), ("tiny", 4)])
@@ -54,9 +52,6 @@ def test_sizes_with_a_larger_threshold_bound(name, x):
     assert z["C"] == oracle.capacity(w.E, w.K, w.S, w.blk, 0, x * w.SK)
     nh = w.E // w.R
     assert z["max_seg"] == nh + min(w.E - nh, x * w.SK)
-    cand = x * w.SK - w.SK + 1
-    assert z["search_groups"] == min(-(-cand // 256), 1024)
-    assert z["off_search"] + z["search_groups"] == z["plan_words"]
 
 
 @pytest.mark.parametrize("kw,code", [

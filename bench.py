@@ -64,7 +64,7 @@ def measured_traffic(kernel, workload):
     return float(b.group(1))
 
 
-def cpu_baseline(name, sample_S):
+def cpu_baseline(name, sample_S, **overrides):
     """The oracle, as it stands, on a bounded sample of the workload: the same
     generator and shapes with S reduced to ``sample_S`` tokens per rank."""
     import numpy as np
@@ -76,7 +76,7 @@ def cpu_baseline(name, sample_S):
     import oracle
     from workloads import WORKLOADS, router_logits, activations
 
-    w = WORKLOADS[name].with_(S=sample_S)
+    w = WORKLOADS[name].with_(S=sample_S, **overrides)
     logits = router_logits(w, 0)
     x = activations(w, 0)
     score = oracle.SOFTMAX if w.score == "softmax" else oracle.SIGMOID
@@ -209,6 +209,10 @@ def main():
     ap.add_argument("--B", type=int, default=-1, help="prefetch slots per rank (default: workload's)")
     ap.add_argument("--tau-max-x", type=float, default=2.0,
                     help="quota planner's threshold bound, in units of S*K")
+    ap.add_argument("--vio", type=float, default=-1.0,
+                    help="target max_vio of the moonep workload's routing (default 20)")
+    ap.add_argument("--maxvio-sweep", action="store_true",
+                    help="moonep: also time the step at max_vio 0.2, 1, 10, 20 (same buffers)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -230,6 +234,8 @@ def main():
     w = WORKLOADS[args.workload]
     if args.B >= 0:
         w = w.with_(B=args.B)
+    if args.vio >= 0:
+        w = w.with_(vio=args.vio)
     tau_max = int(round(args.tau_max_x * w.SK))
     shape = lbt.Shape(E=w.E, K=w.K, R=w.R, S=w.S, H=w.H, B=w.B, blk=w.blk,
                       score_fn=lbt.SOFTMAX if w.score == "softmax" else lbt.SIGMOID,
@@ -241,7 +247,6 @@ def main():
           f"C={C}; generating inputs", file=sys.stderr, flush=True)
 
     # inputs resident in HBM before timing
-    logits = torch.from_numpy(router_logits(w, 0)).to(dev)
     x = torch.empty((w.N, w.H), dtype=torch.int16, device=dev)
     for c in range((w.N + X_CHUNK - 1) // X_CHUNK):
         blk = x_chunk(w, 0, c)
@@ -253,7 +258,7 @@ def main():
     names = ["route", "plan", "align", "dispatch", "combine"]
     plan_fn = path.plan_balance if args.planner == "fixed" else path.plan_quota
 
-    def step(evs=None):
+    def step(logits, evs=None):
         rec = (lambda i: evs[i].record(stream)) if evs is not None else (lambda i: None)
         rec(0)
         path.route_topk(logits, buf["ids"], buf["gates"], buf["counts"], buf["work"])
@@ -268,26 +273,57 @@ def main():
         path.combine(buf["recv"], buf["slot"], buf["gates"], buf["y"])
         rec(5)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps}", file=sys.stderr,
-          flush=True)
+    def timed(logits):
+        """Warm up, then time args.steps steps; mean per-kernel event times (us)."""
+        for _ in range(args.warmup):
+            step(logits)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(logits, evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = {n: [] for n in names}
+        for e in evs:
+            for j, n in enumerate(names):
+                per[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)   # microseconds
+        return (wall, {n: float(np.mean(v)) for n, v in per.items()},
+                [e[0].elapsed_time(e[-1]) * 1e3 for e in evs])
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-           for _ in range(args.steps)]
+    ab = algorithmic_bytes(w, C)
+    sweep = []
+    if args.maxvio_sweep:
+        if w.skew != "maxvio":
+            print("--maxvio-sweep needs a workload with the maxvio skew (moonep)", file=sys.stderr)
+            sys.exit(2)
+        from workloads.gen import MAXVIO_SWEEP
+        for v in MAXVIO_SWEEP:
+            wv = w.with_(vio=v)
+            print(f"[bench] max_vio sweep: vio={v}", file=sys.stderr, flush=True)
+            lg = torch.from_numpy(router_logits(wv, 0)).to(dev)
+            wall_v, us_v, _ = timed(lg)
+            hdr_v = buf["plan"][:16].cpu().numpy()
+            sweep.append({
+                "vio": v, "max_vio": float(hdr_v[1]) * w.E / w.P - 1.0,
+                "rank_imbalance_before": float(hdr_v[2]) / w.SK - 1.0,
+                "ms_per_step": wall_v / args.steps * 1e3, "kernel_us": us_v,
+                "dispatch_combine_frac_peak": (ab["dispatch"] + ab["combine"]) /
+                ((us_v["dispatch"] + us_v["combine"]) * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                "replica_segments": int(hdr_v[0]), "max_replicas_per_rank": int(hdr_v[10]),
+                "remote_replicas": int(buf["plan"][path.sizes["off_n_remote"]:
+                                                   path.sizes["off_n_remote"] + w.R].sum().item()),
+                "status": int(buf["status"].item())})
+            del lg
+            torch.cuda.synchronize()
+
+    logits = torch.from_numpy(router_logits(w, 0)).to(dev)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = {n: [] for n in names}
-    for e in evs:
-        for j, n in enumerate(names):
-            per[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)   # microseconds
-    avg_us = {n: float(np.mean(v)) for n, v in per.items()}
-    step_dev_us = [e[0].elapsed_time(e[-1]) * 1e3 for e in evs]
+    print(f"[bench] timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr,
+          flush=True)
+    wall, avg_us, step_dev_us = timed(logits)
 
     # the planner alone (back-to-back launches on the same load matrix)
     plan2 = torch.empty_like(buf["plan"])
@@ -312,7 +348,6 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
 
-    ab = algorithmic_bytes(w, C)
     step_bytes = sum(ab.values())
     ms_per_step = wall / args.steps * 1e3
     slots_per_s = w.P * args.steps / wall
@@ -336,6 +371,7 @@ def main():
         "config": {"workload": w.name, "E": w.E, "K": w.K, "R": w.R, "S": w.S, "H": w.H,
                    "B": w.B, "blk": w.blk, "C": C, "token_slots_per_step": w.P,
                    "planner": args.planner,
+                   **({"vio": w.vio} if w.skew == "maxvio" else {}),
                    "gate": w.score, "combine_accumulate": "fp32", "y": "fp32",
                    "expert": "identity (out = recv)"},
         "roofline": {"bound": "hbm", "kernel": "k_combine",
@@ -355,6 +391,7 @@ def main():
         "rank_imbalance_before": float(hdr[2]) / w.SK - 1.0,
         "replica_segments": int(hdr[0]),
         "planners": planners,
+        **({"maxvio_sweep": sweep} if sweep else {}),
         "status": status,
         "device": torch.cuda.get_device_name(0),
     }
@@ -366,7 +403,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         sample_S = args.cpu_sample_S or max(1, min(w.S, 32768 // w.R))
-        result["cpu_baseline"] = cpu_baseline(w.name, sample_S)
+        result["cpu_baseline"] = cpu_baseline(w.name, sample_S, B=w.B, vio=w.vio)
     print(json.dumps(result), flush=True)
 
 

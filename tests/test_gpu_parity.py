@@ -134,7 +134,7 @@ def test_dispatch_combine_parity_full_rows(name, S):
     _full_move_check(w, res, ref, activations(w, 0))
 
 
-@pytest.mark.parametrize("name", ["dsv3", "wideep", "kimi"])
+@pytest.mark.parametrize("name", ["dsv3", "wideep", "kimi", "moonep"])
 def test_dispatch_combine_full_size_sampled(name):
     """Full-size dispatch + combine in the launch configuration the benchmark
     times; the oracle recomputes sampled rows one by one."""
@@ -176,6 +176,22 @@ def test_dispatch_combine_full_size_sampled(name):
     yh = y[t.from_numpy(tokens).cuda()].cpu().numpy().astype(np.float64)
     want = oracle.bf16_to_f64(xs) * gates32[tokens].astype(np.float64).sum(axis=1)[:, None]
     assert (np.abs(yh - want) <= gu.COMBINE_RTOL * np.abs(want) + 1e-30).all()
+
+
+# --------------------------------------------------------------------------- max_vio sweep
+@pytest.mark.parametrize("vio", [0.2, 1.0, 10.0, 20.0])
+@pytest.mark.parametrize("planner", ["fixed", "quota"])
+def test_maxvio_routing_parity(vio, planner):
+    """The sweep's routings (MoonEP's bench shape with S cut to 1024 tokens
+    per rank) through route, either planner and align, bit-exact."""
+    w = WORKLOADS["moonep"].with_(vio=vio, S=1024)
+    print(f"[parity] moonep vio={vio} {planner}", flush=True)
+    logits = router_logits(w, 0)
+    res = gu.run_front(gu.shape_of(w), logits, planner=planner)
+    ref = gu.run_oracle(w, logits, planner=planner)
+    gu.check_route(res, ref)
+    gu.check_plan(res["plan_fields"], ref["plan"], w.P)
+    gu.check_align(res, ref, w.R, res["sizes"]["C"])
 
 
 # --------------------------------------------------------------------------- edge cases

@@ -14,6 +14,8 @@ claim on the research-vault page, section "WideEP"):
   wideep   E=256 K=8 R=64 S=512  H=7168 B=4  blk=64  sigmoid, Zipf s=1.3, permuted per layer
   kimi     E=384 K=8 R=32 S=8192 H=7168 B=4  blk=128 sigmoid, 5% hot experts draw ~30%
   decodeS  E=256 K=8 R=8  S in {1,16,128} H=7168 B=3 blk=128 sigmoid, Zipf s=1.1
+  moonep   E=384 K=8 R=8  S=8192 H=7168 B=48 blk=128 sigmoid, routing built for a
+           given max_vio (MoonEP's sweep over max_vio in {0.2, 1, 10, 20})
 
 Router logits are fp32 z + bias[e] with z ~ N(0,1) (numpy PCG64, drawn in
 fp32) and bias the log of a Zipf pmf p_i ∝ i^-s over i=1..E, mapped to experts
@@ -53,6 +55,7 @@ class Workload:
     permute: bool = True
     hot_frac: float = 0.0
     seed: int = 0
+    vio: float = 0.0      # target max_vio of the "maxvio" skew
 
     @property
     def N(self) -> int:
@@ -79,7 +82,10 @@ WORKLOADS = {
     "decode1": Workload("decode1", 256, 8, 8, 1, 7168, 3, 128, "sigmoid", "zipf", 1.1, True, seed=4),
     "decode16": Workload("decode16", 256, 8, 8, 16, 7168, 3, 128, "sigmoid", "zipf", 1.1, True, seed=4),
     "decode128": Workload("decode128", 256, 8, 8, 128, 7168, 3, 128, "sigmoid", "zipf", 1.1, True, seed=4),
+    "moonep": Workload("moonep", 384, 8, 8, 8192, 7168, 48, 128, "sigmoid", "maxvio", seed=5, vio=20.0),
 }
+
+MAXVIO_SWEEP = (0.2, 1.0, 10.0, 20.0)
 
 
 def _rng(*key: int) -> np.random.Generator:
@@ -113,9 +119,54 @@ def expert_bias(w: Workload, layer: int = 0, delta: float | None = None) -> np.n
     return bias.astype(np.float32)
 
 
+def hot_pair_count(w: Workload) -> int:
+    """Pairs the hot expert of the "maxvio" skew receives: (1 + vio) times
+    the mean per-expert load N*K/E, rounded to the nearest integer."""
+    return int(round((1.0 + w.vio) * w.N * w.K / w.E))
+
+
+def maxvio_choice(w: Workload, layer: int = 0) -> tuple[int, np.ndarray]:
+    """(hot expert, bool [N, E] choice matrix) of the "maxvio" skew.
+
+    A seeded random set of hot_pair_count(w) tokens picks the hot expert;
+    every other (token, slot) is dealt round-robin over a seeded random cyclic
+    order of the remaining E-1 experts, token by token, so those experts'
+    loads differ by at most one and each token's experts are distinct."""
+    if not (0.0 <= w.vio <= w.E / w.K - 1.0):
+        raise ValueError("vio must lie in [0, E/K - 1]")
+    rng = _rng(w.seed, layer, 4)
+    hot = int(rng.integers(w.E))
+    n_hot = hot_pair_count(w)
+    if n_hot > w.N:
+        raise ValueError("too few tokens for this vio")
+    is_hot = np.zeros(w.N, bool)
+    is_hot[rng.choice(w.N, n_hot, replace=False)] = True
+    others = np.delete(np.arange(w.E), hot)
+    cyc = others[rng.permutation(w.E - 1)]
+    k_t = w.K - is_hot.astype(np.int64)                  # non-hot picks per token
+    start = np.concatenate([[0], np.cumsum(k_t)[:-1]])
+    choice = np.zeros((w.N, w.E), bool)
+    for j in range(w.K):
+        sel = j < k_t
+        choice[np.nonzero(sel)[0], cyc[(start[sel] + j) % (w.E - 1)]] = True
+    choice[is_hot, hot] = True
+    return hot, choice
+
+
+def maxvio_logits(w: Workload, layer: int = 0) -> np.ndarray:
+    """fp32 [N, E] logits whose K largest per row are maxvio_choice's experts:
+    chosen experts get 1 + u, the others -u, u ~ U[0, 1) drawn in fp32."""
+    _, choice = maxvio_choice(w, layer)
+    u = _rng(w.seed, layer, 5).random((w.N, w.E), dtype=np.float32)
+    return np.where(choice, np.float32(1.0) + u, -u).astype(np.float32)
+
+
 def router_logits(w: Workload, layer: int = 0, delta: float | None = None,
                   rows: slice | None = None) -> np.ndarray:
     """fp32 [N, E] router logits z + bias for one layer."""
+    if w.skew == "maxvio":
+        lg = maxvio_logits(w, layer)
+        return lg if rows is None else lg[rows]
     z = _rng(w.seed, layer, 1).standard_normal((w.N, w.E), dtype=np.float32)
     if rows is not None:
         z = z[rows]

@@ -22,9 +22,14 @@ function.  Floating point is fp64 except where the method itself fixes fp32
 (the top-K key is an fp32 value; bf16 rows widen exactly to fp32).
 
 Parity pins (see tests/test_oracle_*.py): brute-force top-K, closed-form gates,
-numpy bincount, hand-derived plans W1-W3, brute-force enumeration of
-rule-conforming plans, the balanced-routing special case (textbook stable
-counting sort), invariants, and the identity-expert closed form for combine.
+numpy bincount, hand-derived plans W1-W3 (fixed rule) and Q1-Q4 (quota rule),
+brute-force enumeration of rule-conforming plans under both rules, the
+balanced-routing special case (textbook stable counting sort), the
+one-expert-per-rank reduction of the quota rule to the fixed rule, invariants,
+the identity-expert closed form for combine; for the training side the
+hand-derived replica lists (prefetch, reduce_grad), exact integer
+conservation and line-order sensitivity of reduce_grad, central differences
+and adjoint identities for the backward.
 Gate values' last fp32 bit is pinned only to 1e-6 relative (parity partially
 unpinned there); rows past each rank's padded end are unspecified.
 """
@@ -502,3 +507,128 @@ def combine(out_rows_of, slot, gates, K, tokens=None):
         y = term if y is None else y + term
         mag = np.abs(term) if mag is None else mag + np.abs(term)
     return y, mag
+
+
+# --------------------------------------------------------------------------- O7
+def prefetch_slots(plan):
+    """Which expert's weights every used prefetch slot must hold.
+
+    [MoonEP-GR] section "Το memory contract ...": one contiguous weight tensor
+    [E+B, H, H'] per expert projection; rows 0..E-1 hold the ranks' experts,
+    rows E..E+B-1 are the rank's local prefetch slots, found by row index;
+    the prefetch pool is process-global (shared by the layers); replicas
+    beyond the slots read their weights from the home rank.  A replica
+    segment of expert e on rank d with weight row E + j therefore needs
+    slot j of rank d to hold e's weights; remote replicas need no slot.
+    Returns {(d, j): e}."""
+    E = plan["E"]
+    return {(rp["rank"], rp["wrow"] - E): rp["expert"]
+            for rp in plan["replicas"] if rp["wrow"] >= E}
+
+
+def prefetch_weights(plan, weights, slots):
+    """Copy home weight rows into the prefetch slots: slots[d, j] =
+    weights[e] for every (d, j) -> e of prefetch_slots (a bit copy); slots
+    the plan does not use are left as they were.  weights [E, ...],
+    slots [R, B, ...] of the same element type.  Returns a new array."""
+    slots = np.array(slots, copy=True)
+    for (d, j), e in prefetch_slots(plan).items():
+        slots[d, j] = weights[e]
+    return slots
+
+
+# --------------------------------------------------------------------------- O8
+def f32_to_bf16_rne(a):
+    """bf16 bits nearest to each finite fp32 value, ties to an even last bit:
+    keep the upper 16 bits and round up when the dropped 16 bits exceed half
+    a bf16 unit, or equal half with the kept last bit odd."""
+    bits = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    keep = bits >> np.uint32(16)
+    drop = bits & np.uint32(0xFFFF)
+    up = (drop > 0x8000) | ((drop == 0x8000) & ((keep & np.uint32(1)) == 1))
+    return (keep + up.astype(np.uint32)).astype(np.uint16)
+
+
+def combine_bwd(out_rows_of, slot, gates, dy, K):
+    """Gradient of combine, y[t] = sum_k g[t,k] out[slot[t*K+k]], with respect
+    to the expert outputs and the gates.  [AlignSort]: permute records the
+    source -> destination map and the gradient of unpermute is a permute
+    (the same map run forward); [MoonEP-GR]: combine is the inverse of the
+    zero-copy dispatch.  So
+
+      d_out[slot[t*K+k]] = g[t,k] * dy[t]      (a dispatch of the scaled
+                                                output gradient into the
+                                                expert-grouped rows)
+      d_g[t,k]          = sum_h dy[t,h] * out[slot[t*K+k], h]
+
+    Precision readings: d_out rows are bf16, like the expert outputs: the
+    fp32 product of the fp32 gate and the fp32 output gradient, rounded to
+    nearest even; d_g is computed in fp64 (then rounded once to fp32 by the
+    caller) with sum_h |dy * out| returned as the scale of its error bound.
+    dy is fp32 [N, H] (bf16 inputs widen to it exactly).
+    Returns (d_out bits [P, H] in pair order, d_g fp64 [N, K], mag [N, K])."""
+    slot = np.asarray(slot, dtype=np.int64)
+    g32 = np.asarray(gates, dtype=np.float32)
+    dy32 = np.asarray(dy, dtype=np.float32)
+    N = g32.shape[0]
+    f = np.arange(N * K, dtype=np.int64)
+    t = f // K
+    # one fp32 product (the exact product of two fp32 numbers fits in fp64)
+    prod = (g32.reshape(-1)[:, None].astype(np.float64) * dy32[t].astype(np.float64)).astype(np.float32)
+    d_out = f32_to_bf16_rne(prod)
+    d_g = np.empty((N, K), dtype=np.float64)
+    mag = np.empty((N, K), dtype=np.float64)
+    for k in range(K):
+        v = bf16_to_f64(out_rows_of(slot[np.arange(N) * K + k]))
+        terms = dy32.astype(np.float64) * v
+        d_g[:, k] = terms.sum(axis=1)
+        mag[:, k] = np.abs(terms).sum(axis=1)
+    return d_out, d_g, mag
+
+
+def dispatch_bwd(d_recv_rows_of, slot, K, N):
+    """Gradient of dispatch, recv[slot[t*K+k]] = x[t], with respect to x:
+    dx[t] = sum_k d_recv[slot[t*K+k]] ([AlignSort]: the backward of a permute
+    gathers the K copies back to their token), in ascending k, fp64 from the
+    bf16 rows.  Returns fp64 dx [N, H] and sum_k |d_recv| (error-bound
+    scale)."""
+    slot = np.asarray(slot, dtype=np.int64)
+    dx = None
+    mag = None
+    for k in range(K):
+        v = bf16_to_f64(d_recv_rows_of(slot[np.arange(N) * K + k]))
+        dx = v if dx is None else dx + v
+        mag = np.abs(v) if mag is None else mag + np.abs(v)
+    return dx, mag
+
+
+# --------------------------------------------------------------------------- O9
+def reduce_grad(plan, slot_grads, grads):
+    """Fold the replicas' weight gradients back into their home experts.
+
+    [MoonEP-GR] section "Τι συμβαίνει στους gradients κατά την εκπαίδευση":
+    training keeps an fp32 gradient buffer laid out like the weights
+    ([E+B, H, H']); the prefetched slots do not write into the parameter
+    gradients but into a separate reduce buffer, seen over all ranks as
+    [R, B, H, H']; reduce_grad reads the slots that belong to each rank's
+    own experts, adds them to the parameter gradient and clears the used
+    slots before the next micro-batch.
+
+    Readings: for expert e its used slots are added in line order
+    (ascending rank), one fp32 addition each: G[e] = ((G[e] + s_1) + s_2)...;
+    remote replicas hold no slot (their gradient is the caller's to route);
+    unused slots are left as they were.
+    slot_grads fp32 [R, B, ...], grads fp32 [E, ...].  Returns new arrays
+    (grads', slot_grads')."""
+    E = plan["E"]
+    grads = np.array(grads, dtype=np.float32, copy=True)
+    slot_grads = np.array(slot_grads, dtype=np.float32, copy=True)
+    used = []
+    for rp in plan["replicas"]:                 # line order
+        if rp["wrow"] >= E:
+            d, j = rp["rank"], rp["wrow"] - E
+            grads[rp["expert"]] = grads[rp["expert"]] + slot_grads[d, j]
+            used.append((d, j))
+    for d, j in used:
+        slot_grads[d, j] = 0.0
+    return grads, slot_grads

@@ -139,6 +139,47 @@ def _pins(o):
     return failures
 
 
+TRAIN_MUTATIONS = {
+    "prefetch_slot_is_weight_row": ('return {(rp["rank"], rp["wrow"] - E): rp["expert"]',
+                                    'return {(rp["rank"], rp["wrow"]): rp["expert"]'),
+    "prefetch_takes_remote_too": ('for rp in plan["replicas"] if rp["wrow"] >= E}',
+                                  'for rp in plan["replicas"] if rp["wrow"] >= 0}'),
+    "reduce_grad_reverse_order": ("    for rp in plan[\"replicas\"]:                 # line order",
+                                  "    for rp in plan[\"replicas\"][::-1]:           # line order"),
+    "reduce_grad_keeps_slots": ("        slot_grads[d, j] = 0.0", "        slot_grads[d, j] = slot_grads[d, j]"),
+    "reduce_grad_clears_all": ("    for d, j in used:\n        slot_grads[d, j] = 0.0",
+                               "    for d, j in used:\n        slot_grads[d, j] = 0.0\n    slot_grads[:] = 0.0"),
+    "combine_bwd_wrong_token": ("t = f // K\n", "t = f % N\n"),
+    "combine_bwd_no_gate": ("prod = (g32.reshape(-1)[:, None].astype(np.float64) * dy32[t].astype(np.float64))",
+                            "prod = (1.0 * dy32[t].astype(np.float64))"),
+    "bf16_ties_up": ("((drop == 0x8000) & ((keep & np.uint32(1)) == 1))", "(drop == 0x8000)"),
+    "dispatch_bwd_drops_last_k": ("    for k in range(K):\n        v = bf16_to_f64(d_recv_rows_of",
+                                  "    for k in range(K - 1):\n        v = bf16_to_f64(d_recv_rows_of"),
+}
+
+
+def _pins_train(o):
+    from tests import test_oracle_train as tt
+    failures = 0
+    for name in dir(tt):
+        if name.startswith("check_"):
+            try:
+                getattr(tt, name)(o)
+            except Exception:
+                failures += 1
+    return failures
+
+
+def test_unmutated_oracle_passes_the_train_pins():
+    assert _pins_train(oracle_path) == 0
+
+
+@pytest.mark.parametrize("name", sorted(TRAIN_MUTATIONS))
+def test_train_pins_catch_planted_mistake(name):
+    old, new = TRAIN_MUTATIONS[name]
+    assert _pins_train(_mutant(old, new)) > 0, f"planted mistake {name!r} went unnoticed"
+
+
 def test_unmutated_oracle_passes_the_pins():
     assert _pins(oracle_path) == 0
 

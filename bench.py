@@ -59,7 +59,7 @@ def measured_traffic(kernel, workload):
     txt = open(path).read()
     m = re.search(r"source_hash:\s*(\w+)", txt)
     b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m or not b or m.group(1) != source_hash("move.hip", "lbt_internal.h"):
+    if not m or not b or m.group(1) != source_hash("move.hip", "rows.h", "lbt_internal.h"):
         return None
     return float(b.group(1))
 

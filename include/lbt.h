@@ -120,6 +120,7 @@ typedef struct lbt_sizes {
   int64_t off_piece_count;  /*   pairs */
   int64_t off_piece_line;   /*   start on the shared overflow/deficit line */
   int64_t off_piece_row;    /*   padded start row on rank d */
+  int64_t off_piece_wrow;   /*   weight row: E + j for prefetch slot j, else the expert (remote) */
 } lbt_sizes;
 
 /* plan header words */
@@ -248,6 +249,59 @@ int lbt_dispatch(const lbt_shape* s, const uint16_t* x, const int32_t* slot, uin
  *         (LBT_Y_BF16), 16-byte aligned */
 int lbt_combine(const lbt_shape* s, const uint16_t* out, const int32_t* slot, const float* gates,
                 int32_t y_dtype, void* y, void* stream);
+
+/* Replica weight prefetch: copy each slotted replica's home weights into its
+ * rank's prefetch slot.  [MoonEP-GR] section "Το memory contract ..." (one
+ * contiguous [E+B, H, H'] weight tensor per expert projection: rows 0..E-1
+ * the ranks' experts, rows E..E+B-1 the rank's local prefetch slots, found by
+ * row index; the pool is process-global, shared by the layers; replicas
+ * beyond the slots read home weights).  For every replica segment of the plan
+ * with weight row E + j on rank d: slots[d][j] = weights[expert], a bit copy
+ * streamed in 32 KiB tiles.  Slots the plan does not use are not written.
+ *   plan      blob from lbt_plan_balance / lbt_plan_quota
+ *   weights   [E][row_bytes] home weight rows (rows 0..E-1 of the pool), 16-byte aligned
+ *   slots     [R][B][row_bytes] each rank's prefetch slots, 16-byte aligned
+ *   row_bytes bytes of one expert's weights (H * H' * element size), a
+ *             positive multiple of 16 */
+int lbt_prefetch_weights(const lbt_shape* s, const int32_t* plan, const void* weights, void* slots,
+                         int64_t row_bytes, void* stream);
+
+/* Fold the replicas' weight gradients into their home experts' gradients
+ * and clear the used slots.  [MoonEP-GR] section "Τι συμβαίνει στους
+ * gradients κατά την εκπαίδευση" (fp32 gradients laid out like the weights;
+ * prefetched slots write to a separate reduce buffer, seen over the ranks as
+ * [R, B, H, H']; reduce_grad adds the slots of each rank's own experts into
+ * the parameter gradient and clears them before the next micro-batch).  For
+ * every expert, its slotted replicas are added in line order (ascending
+ * rank), one fp32 addition each; remote replicas hold no slot.
+ *   plan       blob from lbt_plan_balance / lbt_plan_quota
+ *   slot_grads [R][B][row_elems] fp32, in/out (used slots set to 0)
+ *   grads      [E][row_elems] fp32 home gradients, in/out
+ *   row_elems  elements of one expert's gradient, a positive multiple of 4;
+ *              both pointers 16-byte aligned */
+int lbt_reduce_grad(const lbt_shape* s, const int32_t* plan, float* slot_grads, float* grads,
+                    int64_t row_elems, void* stream);
+
+/* Backward of combine.  [AlignSort] (permute records source -> destination;
+ * the gradient of unpermute is a permute); [MoonEP-GR] (combine inverts the
+ * zero-copy dispatch).  For pair f = t*K + k with row s = slot[f] >= 0:
+ *   d_out[s]     = bf16(g[f] * dy[t])   fp32 product, rounded to nearest even
+ *   d_gates[f]   = sum_h dy[t,h] * out[s,h], accumulated in fp64, rounded once
+ * Pairs with slot < 0 get d_gates = 0 and write no row.
+ *   out     [R*C, H] bf16 expert outputs (as combine read them), 16-byte aligned
+ *   dy      [N, H] fp32 (LBT_Y_F32) or bf16 (LBT_Y_BF16), 16-byte aligned
+ *   d_out   [R*C, H] bf16 out: only rows some pair maps to are written
+ *   d_gates [N, K] fp32 out */
+int lbt_combine_bwd(const lbt_shape* s, const uint16_t* out, const int32_t* slot,
+                    const float* gates, int32_t dy_dtype, const void* dy, uint16_t* d_out,
+                    float* d_gates, void* stream);
+
+/* Backward of dispatch: dx[t] = sum_k d_recv[slot[t*K+k]] in ascending k,
+ * fp32 accumulation (combine with every gate 1); slot < 0 contributes
+ * nothing.  dx fp32 (LBT_Y_F32) or bf16 rounded to nearest even
+ * (LBT_Y_BF16); d_recv and dx 16-byte aligned. */
+int lbt_dispatch_bwd(const lbt_shape* s, const uint16_t* d_recv, const int32_t* slot,
+                     int32_t dx_dtype, void* dx, void* stream);
 
 /* Text for a return code. */
 const char* lbt_strerror(int code);

@@ -37,8 +37,9 @@ HDR_MAX_REPLICAS = 10
 HDR_FEASIBLE = 11
 
 EXPORTS = ("lbt_query_sizes", "lbt_route_topk", "lbt_histogram", "lbt_plan_balance",
-           "lbt_plan_quota", "lbt_align_sort", "lbt_dispatch", "lbt_combine", "lbt_strerror",
-           "lbt_version")
+           "lbt_plan_quota", "lbt_align_sort", "lbt_dispatch", "lbt_combine",
+           "lbt_prefetch_weights", "lbt_reduce_grad", "lbt_combine_bwd", "lbt_dispatch_bwd",
+           "lbt_strerror", "lbt_version")
 
 
 class LbtShape(ctypes.Structure):
@@ -53,6 +54,7 @@ _SIZE_FIELDS = (
     "off_n_seg", "off_n_rows_padded", "off_n_slots", "off_n_remote",
     "off_seg_expert", "off_seg_wrow", "off_seg_count", "off_seg_start",
     "off_piece_expert", "off_piece_rank", "off_piece_count", "off_piece_line", "off_piece_row",
+    "off_piece_wrow",
 )
 
 
@@ -86,6 +88,10 @@ def lib() -> ctypes.CDLL:
         L.lbt_align_sort.argtypes = [SP, P, P, P, P, P, P, P, P, P]
         L.lbt_dispatch.argtypes = [SP, P, P, P, P]
         L.lbt_combine.argtypes = [SP, P, P, P, ctypes.c_int32, P, P]
+        L.lbt_prefetch_weights.argtypes = [SP, P, P, P, ctypes.c_int64, P]
+        L.lbt_reduce_grad.argtypes = [SP, P, P, P, ctypes.c_int64, P]
+        L.lbt_combine_bwd.argtypes = [SP, P, P, P, ctypes.c_int32, P, P, P, P]
+        L.lbt_dispatch_bwd.argtypes = [SP, P, P, ctypes.c_int32, P, P]
         L.lbt_strerror.argtypes = [I]
         L.lbt_strerror.restype = ctypes.c_char_p
         L.lbt_version.argtypes = []
@@ -156,6 +162,16 @@ def _ptr(t, dtype, numel, name, align16=False):
     if align16 and p % 16:
         raise LbtError(f"{name} must be 16-byte aligned")
     return p
+
+
+def _raw(t, name):
+    """Device pointer of a contiguous tensor of any dtype (byte-level calls)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise LbtError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise LbtError(f"{name} must be contiguous")
+    return t.data_ptr()
 
 
 def _stream(stream):
@@ -291,6 +307,65 @@ class Path:
             _stream(stream))
         _check(rc, "lbt_combine")
 
+    # replica weights and gradients (one expert projection per call)
+    def prefetch_weights(self, plan, weights, slots, stream=None):
+        """weights: [E, ...] tensor of home weight rows; slots: [R, B, ...]
+        of the same row size and dtype."""
+        torch = _torch()
+        s, z = self.shape, self.sizes
+        row_bytes = weights[0].numel() * weights.element_size() if weights.shape[0] else 0
+        if weights.shape[0] != s.E or (s.B and tuple(slots.shape[:2]) != (s.R, s.B)):
+            raise LbtError("prefetch_weights: weights must be [E, ...] and slots [R, B, ...]")
+        if slots.numel() * slots.element_size() < s.R * s.B * row_bytes:
+            raise LbtError("prefetch_weights: slots too small")
+        rc = lib().lbt_prefetch_weights(
+            ctypes.byref(self._c), _ptr(plan, torch.int32, z["plan_words"], "plan"),
+            _raw(weights, "weights"), _raw(slots, "slots"), row_bytes, _stream(stream))
+        _check(rc, "lbt_prefetch_weights")
+
+    def reduce_grad(self, plan, slot_grads, grads, stream=None):
+        """slot_grads fp32 [R, B, ...], grads fp32 [E, ...] of the same row size."""
+        torch = _torch()
+        s, z = self.shape, self.sizes
+        row = grads[0].numel() if grads.shape[0] else 0
+        if grads.shape[0] != s.E or (s.B and tuple(slot_grads.shape[:2]) != (s.R, s.B)):
+            raise LbtError("reduce_grad: grads must be [E, ...] and slot_grads [R, B, ...]")
+        rc = lib().lbt_reduce_grad(
+            ctypes.byref(self._c), _ptr(plan, torch.int32, z["plan_words"], "plan"),
+            _ptr(slot_grads, torch.float32, s.R * s.B * row, "slot_grads"),
+            _ptr(grads, torch.float32, s.E * row, "grads"), row, _stream(stream))
+        _check(rc, "lbt_reduce_grad")
+
+    # backward of a6 and a5
+    def combine_bwd(self, out, slot, gates, dy, d_out, d_gates, stream=None):
+        torch = _torch()
+        s, z = self.shape, self.sizes
+        dy_bf16 = dy.dtype == torch.int16
+        rc = lib().lbt_combine_bwd(
+            ctypes.byref(self._c),
+            _ptr(out, torch.int16, s.R * z["C"] * s.H, "out", align16=True),
+            _ptr(slot, torch.int32, z["P"], "slot"),
+            _ptr(gates, torch.float32, s.N * s.K, "gates"),
+            Y_BF16 if dy_bf16 else Y_F32,
+            _ptr(dy, torch.int16 if dy_bf16 else torch.float32, s.N * s.H, "dy", align16=True),
+            _ptr(d_out, torch.int16, s.R * z["C"] * s.H, "d_out", align16=True),
+            _ptr(d_gates, torch.float32, s.N * s.K, "d_gates"),
+            _stream(stream))
+        _check(rc, "lbt_combine_bwd")
+
+    def dispatch_bwd(self, d_recv, slot, dx, stream=None):
+        torch = _torch()
+        s, z = self.shape, self.sizes
+        dx_bf16 = dx.dtype == torch.int16
+        rc = lib().lbt_dispatch_bwd(
+            ctypes.byref(self._c),
+            _ptr(d_recv, torch.int16, s.R * z["C"] * s.H, "d_recv", align16=True),
+            _ptr(slot, torch.int32, z["P"], "slot"),
+            Y_BF16 if dx_bf16 else Y_F32,
+            _ptr(dx, torch.int16 if dx_bf16 else torch.float32, s.N * s.H, "dx", align16=True),
+            _stream(stream))
+        _check(rc, "lbt_dispatch_bwd")
+
     def step(self, logits, x, buf, sel_bias=None, out=None, stream=None, planner="fixed"):
         """One pass of the whole path; ``out`` defaults to recv (identity
         expert); ``planner`` is "fixed" (lbt_plan_balance) or "quota"
@@ -338,5 +413,5 @@ def plan_fields(plan_words, sizes: dict, R: int, E: int) -> dict:
         "seg_start": at("off_seg_start", R * (ms + 1), (R, ms + 1)),
         "piece_expert": at("off_piece_expert", mp), "piece_rank": at("off_piece_rank", mp),
         "piece_count": at("off_piece_count", mp), "piece_line": at("off_piece_line", mp),
-        "piece_row": at("off_piece_row", mp),
+        "piece_row": at("off_piece_row", mp), "piece_wrow": at("off_piece_wrow", mp),
     }

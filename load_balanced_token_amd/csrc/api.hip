@@ -65,6 +65,7 @@ int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z) {
   pl.piece_count = take(mp);
   pl.piece_line = take(mp);
   pl.piece_row = take(mp);
+  pl.piece_wrow = take(mp);
   pl.total = (int)off;
 
   if (d != nullptr) {
@@ -88,6 +89,7 @@ int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z) {
     z->off_piece_expert = pl.piece_expert; z->off_piece_rank = pl.piece_rank;
     z->off_piece_count = pl.piece_count; z->off_piece_line = pl.piece_line;
     z->off_piece_row = pl.piece_row;
+    z->off_piece_wrow = pl.piece_wrow;
   }
   return LBT_OK;
 }
@@ -189,6 +191,54 @@ int lbt_combine(const lbt_shape* s, const uint16_t* out, const int32_t* slot, co
   if (d.N > 0 && (!out || !slot || !gates || !y || !aligned16(out) || !aligned16(y)))
     return LBT_EINVAL;
   return hip_rc(launch_combine(d, out, slot, gates, y_dtype, y, static_cast<hipStream_t>(stream)));
+}
+
+int lbt_prefetch_weights(const lbt_shape* s, const int32_t* plan, const void* weights, void* slots,
+                         int64_t row_bytes, void* stream) {
+  Dims d;
+  const int rc = make_dims(s, &d, nullptr);
+  if (rc) return rc;
+  if (!plan || row_bytes <= 0 || row_bytes % 16 != 0) return LBT_EINVAL;
+  if (d.B > 0 && (!weights || !slots || !aligned16(weights) || !aligned16(slots))) return LBT_EINVAL;
+  return hip_rc(launch_prefetch(d, plan, weights, slots, row_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int lbt_reduce_grad(const lbt_shape* s, const int32_t* plan, float* slot_grads, float* grads,
+                    int64_t row_elems, void* stream) {
+  Dims d;
+  const int rc = make_dims(s, &d, nullptr);
+  if (rc) return rc;
+  if (!plan || row_elems <= 0 || row_elems % 4 != 0) return LBT_EINVAL;
+  if (d.B > 0 && (!slot_grads || !grads || !aligned16(slot_grads) || !aligned16(grads)))
+    return LBT_EINVAL;
+  return hip_rc(launch_reduce_grad(d, plan, slot_grads, grads, row_elems,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int lbt_combine_bwd(const lbt_shape* s, const uint16_t* out, const int32_t* slot,
+                    const float* gates, int32_t dy_dtype, const void* dy, uint16_t* d_out,
+                    float* d_gates, void* stream) {
+  Dims d;
+  const int rc = make_dims(s, &d, nullptr);
+  if (rc) return rc;
+  if (dy_dtype != LBT_Y_F32 && dy_dtype != LBT_Y_BF16) return LBT_EINVAL;
+  if (d.N > 0 && (!out || !slot || !gates || !dy || !d_out || !d_gates || !aligned16(out) ||
+                  !aligned16(dy) || !aligned16(d_out)))
+    return LBT_EINVAL;
+  return hip_rc(launch_combine_bwd(d, out, slot, gates, dy_dtype, dy, d_out, d_gates,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int lbt_dispatch_bwd(const lbt_shape* s, const uint16_t* d_recv, const int32_t* slot,
+                     int32_t dx_dtype, void* dx, void* stream) {
+  Dims d;
+  const int rc = make_dims(s, &d, nullptr);
+  if (rc) return rc;
+  if (dx_dtype != LBT_Y_F32 && dx_dtype != LBT_Y_BF16) return LBT_EINVAL;
+  if (d.N > 0 && (!d_recv || !slot || !dx || !aligned16(d_recv) || !aligned16(dx)))
+    return LBT_EINVAL;
+  return hip_rc(launch_combine(d, d_recv, slot, nullptr, dx_dtype, dx,
+                               static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

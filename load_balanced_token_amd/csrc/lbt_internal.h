@@ -23,7 +23,7 @@ struct PlanLayout {
   int E, R, max_seg, max_pieces;
   int hdr, T, h, O, home_row, L, def, D, n_seg, n_rows_padded, n_slots, n_remote;
   int seg_expert, seg_wrow, seg_count, seg_start;
-  int piece_expert, piece_rank, piece_count, piece_line, piece_row;
+  int piece_expert, piece_rank, piece_count, piece_line, piece_row, piece_wrow;
   int total;
 };
 
@@ -62,6 +62,14 @@ hipError_t launch_dispatch(const Dims& d, const uint16_t* x, const int32_t* slot
                            hipStream_t st);
 hipError_t launch_combine(const Dims& d, const uint16_t* out, const int32_t* slot,
                           const float* gates, int y_dtype, void* y, hipStream_t st);
+// gates == nullptr: every gate is 1 (the backward of dispatch)
+hipError_t launch_prefetch(const Dims& d, const int32_t* plan, const void* weights, void* slots,
+                           long long row_bytes, hipStream_t st);
+hipError_t launch_reduce_grad(const Dims& d, const int32_t* plan, float* slot_grads, float* grads,
+                              long long row_elems, hipStream_t st);
+hipError_t launch_combine_bwd(const Dims& d, const uint16_t* out, const int32_t* slot,
+                              const float* gates, int dy_dtype, const void* dy, uint16_t* d_out,
+                              float* d_gates, hipStream_t st);
 
 // Workspace layout: tile_counts [E][n_tiles] (expert-major, for the column
 // scan) followed by tile_base [n_tiles][E] (tile-major, for the align step).

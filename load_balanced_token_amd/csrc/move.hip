@@ -11,36 +11,9 @@
 // 16 bytes, combine 448 threads x 4 groups of 8 bytes): short-lived waves
 // with all their loads in flight measured fastest on MI355X for both the
 // write-heavy dispatch and the read-heavy combine.
-#include "lbt_internal.h"
+#include "rows.h"
 
 namespace lbt {
-
-// Native clang vector types: the nontemporal builtins take these, not
-// HIP_vector_type.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-
-// Element `byte_off` bytes into a row that starts at a wave-uniform address:
-// a uniform 64-bit base plus an unsigned 32-bit lane offset lets the
-// compiler use scalar-base addressing instead of a 64-bit VGPR address per
-// access.
-template <typename T>
-__device__ __forceinline__ const T* at_bytes(const void* base, uint32_t byte_off) {
-  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
-}
-template <typename T>
-__device__ __forceinline__ T* at_bytes(void* base, uint32_t byte_off) {
-  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + byte_off);
-}
-
-// Workgroup i runs on XCD i % 8; give each XCD a contiguous range of tokens
-// so that one XCD's L2 sees neighbouring rows.  A bijection on [0, G).
-__device__ __forceinline__ int xcd_contiguous(int i, int G) {
-  const int q = G / 8, rem = G % 8, x = i % 8, pos = i / 8;
-  return x * q + min(x, rem) + pos;
-}
 
 // Dispatch: one token per workgroup; per pass thread j moves the 16-byte
 // chunks base + j + i*blockDim (i < CH) of the row: loaded once, stored K
@@ -84,9 +57,6 @@ __global__ __launch_bounds__(1024) void k_dispatch(const u32x4* __restrict__ x,
   }
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
 // acc[0..3] += g * (4 bf16 values), one fused multiply-add each
 __device__ __forceinline__ void fma4(float (&a)[4], float g, const u32x2& v) {
   a[0] = fmaf(g, bf16_lo(v.x), a[0]);
@@ -95,12 +65,6 @@ __device__ __forceinline__ void fma4(float (&a)[4], float g, const u32x2& v) {
   a[3] = fmaf(g, bf16_hi(v.y), a[3]);
 }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if (f != f) return 0x7FC0u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 
 // Combine: one token per workgroup; per pass thread j owns the groups of 4
 // bf16 values base + j + i*blockDim (i < GPT).  Loads are 8 bytes per lane,
@@ -108,10 +72,11 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
 // instruction writes whole cache lines.  The K source rows are loaded in one
 // group of KT (or groups of 8 when K is not a compile-time constant), all in
 // flight before the first multiply-add, and accumulated in ascending k.
-// One pass covers rows up to H = 8192 (512 threads x 4 groups of 4).
+// One pass covers rows up to H = 8192 (512 threads x 4 groups of 4).  UNIT:
+// every gate is 1 (the backward of dispatch, a plain K-row sum).
 constexpr int kCombineMaxThreads = 512;
 
-template <int GPT, bool BF16, int KT, bool FULL>
+template <int GPT, bool BF16, int KT, bool FULL, bool UNIT = false>
 __global__ __launch_bounds__(kCombineMaxThreads) void k_combine(const u32x2* __restrict__ out,
                                                   const int32_t* __restrict__ slot,
                                                   const float* __restrict__ gates, int N, int Krt,
@@ -121,7 +86,7 @@ __global__ __launch_bounds__(kCombineMaxThreads) void k_combine(const u32x2* __r
   const int t = blockIdx.x;
   const int nthr = blockDim.x;
   const int32_t* sl = slot + (long long)t * K;
-  const float* gt = gates + (long long)t * K;
+  const float* gt = UNIT ? nullptr : gates + (long long)t * K;
   for (int base = 0; base < G4; base += GPT * nthr) {
     float acc[GPT][4];
 #pragma unroll
@@ -137,7 +102,7 @@ __global__ __launch_bounds__(kCombineMaxThreads) void k_combine(const u32x2* __r
         const int k = k0 + kk;
         s[kk] = k < K ? sl[k] : -1;
         use[kk] = s[kk] >= 0 && (long long)s[kk] < n_rows;   // k < K and the pair fit
-        g[kk] = use[kk] ? gt[k] : 0.f;
+        g[kk] = use[kk] ? (UNIT ? 1.f : gt[k]) : 0.f;
       }
       // every load is issued before the first multiply-add; an unused k reads
       // row 0 (always present) and is skipped below
@@ -216,7 +181,7 @@ __global__ __launch_bounds__(THR) void k_dispatch_w(const u32x4* __restrict__ x,
 // as k_combine.  With the width fixed at compile time this form measured
 // ~5% faster on MI355X at H = 7168.  A token holding a slot that did not fit
 // (slot < 0, capacity overflow) takes the checked path.
-template <int THR, int GPT, int KT, bool BF16>
+template <int THR, int GPT, int KT, bool BF16, bool UNIT = false>
 __global__ __launch_bounds__(THR) void k_combine_w(const u32x2* __restrict__ out,
                                                    const int32_t* __restrict__ slot,
                                                    const float* __restrict__ gates,
@@ -229,7 +194,7 @@ __global__ __launch_bounds__(THR) void k_combine_w(const u32x2* __restrict__ out
 #pragma unroll
   for (int k = 0; k < KT; ++k) {
     s[k] = slot[(long long)t * KT + k];
-    g[k] = gates[(long long)t * KT + k];
+    g[k] = UNIT ? 1.f : gates[(long long)t * KT + k];
     all_used = all_used && s[k] >= 0 && (long long)s[k] < n_rows;
   }
   float acc[GPT][4];
@@ -316,7 +281,7 @@ hipError_t launch_dispatch(const Dims& d, const uint16_t* x, const int32_t* slot
   return hipGetLastError();
 }
 
-template <bool BF16, int KT>
+template <bool BF16, int KT, bool UNIT>
 static void launch_combine_t(const Dims& d, const u32x2* o, const int32_t* slot, const float* gates,
                              void* y, hipStream_t st) {
   const int G4 = d.H / 4;
@@ -324,24 +289,24 @@ static void launch_combine_t(const Dims& d, const u32x2* o, const int32_t* slot,
   const dim3 grid(d.N), block(thr);
   const long long n_rows = (long long)d.R * d.C;
   if (G4 % (4 * thr) == 0)   // every pass fills every lane: no per-lane bounds checks
-    hipLaunchKernelGGL((k_combine<4, BF16, KT, true>), grid, block, 0, st, o, slot, gates, d.N, d.K, G4, n_rows, y);
+    hipLaunchKernelGGL((k_combine<4, BF16, KT, true, UNIT>), grid, block, 0, st, o, slot, gates, d.N, d.K, G4, n_rows, y);
   else
-    hipLaunchKernelGGL((k_combine<4, BF16, KT, false>), grid, block, 0, st, o, slot, gates, d.N, d.K, G4, n_rows, y);
+    hipLaunchKernelGGL((k_combine<4, BF16, KT, false, UNIT>), grid, block, 0, st, o, slot, gates, d.N, d.K, G4, n_rows, y);
 }
 
-template <bool BF16>
+template <bool BF16, bool UNIT>
 static void launch_combine_k(const Dims& d, const u32x2* o, const int32_t* slot, const float* gates,
                              void* y, hipStream_t st) {
   if (d.H == 7168 && d.K == 8) {   // DeepSeek-V3 / Kimi-K2 hidden size
-    hipLaunchKernelGGL((k_combine_w<224, 8, 8, BF16>), dim3(d.N), dim3(224), 0, st, o, slot, gates,
-                       (long long)d.R * d.C, y);
+    hipLaunchKernelGGL((k_combine_w<224, 8, 8, BF16, UNIT>), dim3(d.N), dim3(224), 0, st, o, slot,
+                       gates, (long long)d.R * d.C, y);
     return;
   }
   switch (d.K) {
-    case 2: launch_combine_t<BF16, 2>(d, o, slot, gates, y, st); break;
-    case 4: launch_combine_t<BF16, 4>(d, o, slot, gates, y, st); break;
-    case 8: launch_combine_t<BF16, 8>(d, o, slot, gates, y, st); break;
-    default: launch_combine_t<BF16, 0>(d, o, slot, gates, y, st); break;
+    case 2: launch_combine_t<BF16, 2, UNIT>(d, o, slot, gates, y, st); break;
+    case 4: launch_combine_t<BF16, 4, UNIT>(d, o, slot, gates, y, st); break;
+    case 8: launch_combine_t<BF16, 8, UNIT>(d, o, slot, gates, y, st); break;
+    default: launch_combine_t<BF16, 0, UNIT>(d, o, slot, gates, y, st); break;
   }
 }
 
@@ -349,8 +314,14 @@ hipError_t launch_combine(const Dims& d, const uint16_t* out, const int32_t* slo
                           const float* gates, int y_dtype, void* y, hipStream_t st) {
   if (d.N == 0) return hipSuccess;
   const u32x2* o = reinterpret_cast<const u32x2*>(out);
-  if (y_dtype == LBT_Y_BF16) launch_combine_k<true>(d, o, slot, gates, y, st);
-  else launch_combine_k<false>(d, o, slot, gates, y, st);
+  const bool unit = gates == nullptr;
+  if (y_dtype == LBT_Y_BF16) {
+    if (unit) launch_combine_k<true, true>(d, o, slot, gates, y, st);
+    else launch_combine_k<true, false>(d, o, slot, gates, y, st);
+  } else {
+    if (unit) launch_combine_k<false, true>(d, o, slot, gates, y, st);
+    else launch_combine_k<false, false>(d, o, slot, gates, y, st);
+  }
   return hipGetLastError();
 }
 

@@ -253,7 +253,7 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
       P[pl.seg_start + row1 + s] = (s < nseg ? sF[fb + s] : sF[fb + nseg]) - f0;
   }
   for (int g = tid; g < pl.max_pieces; g += kPlanThreads) {
-    int ex = -1, dd = -1, cnt = 0, line = -1, row = -1;
+    int ex = -1, dd = -1, cnt = 0, line = -1, row = -1, wrow = -1;
     if (g < nP) {
       ex = sPe[g];
       dd = sPd[g];
@@ -261,7 +261,9 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
       line = sPl[g];
       const int fb = dd * nh + sRep[dd];
       row = sF[fb + nh + sPj[g]] - sF[fb];
+      wrow = sPj[g] < B ? E + sPj[g] : ex;
     }
+    P[pl.piece_wrow + g] = wrow;
     P[pl.piece_expert + g] = ex;
     P[pl.piece_rank + g] = dd;
     P[pl.piece_count + g] = cnt;

@@ -85,3 +85,18 @@ def test_host_checks_reject_bad_pointers_before_any_launch():
     assert L.lbt_route_topk(ctypes.byref(sh), None, None, P(1), P(2), P(3), P(4), None) == -1
     assert L.lbt_align_sort(ctypes.byref(sh), P(1), P(2), None, P(3), P(4), P(5), P(6), None, None) == -1
     assert L.lbt_histogram(None, P(1), P(2), P(3), None, None) == -1
+    # training side: row sizes, null and misaligned pointers
+    assert L.lbt_prefetch_weights(ctypes.byref(sh), P(0x1000), P(0x2000), P(0x3000), 24, None) == -1
+    assert L.lbt_prefetch_weights(ctypes.byref(sh), P(0x1000), P(0x2008), P(0x3000), 32, None) == -1
+    assert L.lbt_prefetch_weights(ctypes.byref(sh), None, P(0x2000), P(0x3000), 32, None) == -1
+    assert L.lbt_prefetch_weights(ctypes.byref(sh), P(0x1000), P(0x2000), P(0x3000), 0, None) == -1
+    assert L.lbt_reduce_grad(ctypes.byref(sh), P(0x1000), P(0x2000), P(0x3000), 6, None) == -1
+    assert L.lbt_reduce_grad(ctypes.byref(sh), P(0x1000), None, P(0x3000), 8, None) == -1
+    assert L.lbt_combine_bwd(ctypes.byref(sh), P(0x1000), P(0x2000), P(0x3000), 0, P(0x4000),
+                             P(0x5008), P(0x6000), None) == -1
+    assert L.lbt_combine_bwd(ctypes.byref(sh), P(0x1000), P(0x2000), P(0x3000), 3, P(0x4000),
+                             P(0x5000), P(0x6000), None) == -1
+    assert L.lbt_combine_bwd(ctypes.byref(sh), P(0x1000), P(0x2000), P(0x3000), 0, P(0x4000),
+                             P(0x5000), None, None) == -1
+    assert L.lbt_dispatch_bwd(ctypes.byref(sh), P(0x1000), P(0x2000), 0, P(0x3004), None) == -1
+    assert L.lbt_dispatch_bwd(ctypes.byref(sh), P(0x1000), P(0x2000), 9, P(0x3000), None) == -1

@@ -191,6 +191,73 @@ def planner_report(lbt, torch, w, counts, B, tau_max, dev):
     return out
 
 
+def training_report(lbt, torch, w, path, buf, dev, Hp, reps):
+    """The training-side kernels at the workload's shape: replica weight
+    prefetch and reduce_grad over the plan's slotted replicas (one expert
+    projection of H x H' elements: bf16 weights, fp32 gradients), and the
+    backward of combine and dispatch on the step's buffers.  Median of
+    ``reps`` back-to-back launches timed with HIP events on the launch
+    stream; algorithmic bytes as stated per kernel."""
+    import numpy as np
+    stream = torch.cuda.current_stream()
+    plan = buf["plan"]
+    pf = lbt.plan_fields(plan.cpu().numpy(), path.sizes, w.R, w.E)
+    nP = int(pf["hdr"][0])
+    wrow = pf["piece_wrow"][:nP]
+    pexp = pf["piece_expert"][:nP]
+    slotted = int((wrow >= w.E).sum())
+    runs = int(len(set(pexp[wrow >= w.E].tolist())))
+    row = w.H * Hp
+
+    def time_it(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps)]))
+
+    def entry(us, nbytes, what):
+        gbps = nbytes / (us * 1e-6) / 1e9 if us > 0 else 0.0
+        return {"us": us, "algorithmic_bytes": nbytes, "gbps": gbps,
+                "frac_peak": gbps / HBM_PEAK_GBPS, "bytes": what}
+
+    out = {"H_prime": Hp, "slotted_replicas": slotted, "experts_with_slots": runs}
+    if w.B > 0 and slotted > 0:
+        W = torch.empty((w.E, row), dtype=torch.int16, device=dev)
+        S = torch.empty((w.R, w.B, row), dtype=torch.int16, device=dev)
+        us = time_it(lambda: path.prefetch_weights(plan, W, S))
+        out["prefetch"] = entry(us, (runs + slotted) * row * 2,
+                                "bf16 H x H' weights: each distinct home row read once, "
+                                "each slotted replica's slot written")
+        del W, S
+        G = torch.zeros((w.E, row), dtype=torch.float32, device=dev)
+        SG = torch.zeros((w.R, w.B, row), dtype=torch.float32, device=dev)
+        us = time_it(lambda: path.reduce_grad(plan, SG, G))
+        out["reduce_grad"] = entry(us, (2 * slotted + 2 * runs) * row * 4,
+                                   "fp32: each used slot read and cleared, each home "
+                                   "gradient with slots read and written once")
+        del G, SG
+        torch.cuda.synchronize()
+    dy = torch.zeros((w.N, w.H), dtype=torch.float32, device=dev)
+    d_out = torch.empty_like(buf["recv"])
+    d_g = torch.empty((w.N, w.K), dtype=torch.float32, device=dev)
+    us = time_it(lambda: path.combine_bwd(buf["recv"], buf["slot"], buf["gates"], dy, d_out, d_g))
+    out["combine_bwd"] = entry(us, w.N * w.H * 4 + 2 * w.P * w.H * 2 + w.P * 12,
+                               "fp32 dy read, K bf16 rows read, K bf16 gradient rows "
+                               "written, slot + gate read, gate gradient written")
+    dx = torch.empty((w.N, w.H), dtype=torch.float32, device=dev)
+    us = time_it(lambda: path.dispatch_bwd(d_out, buf["slot"], dx))
+    out["dispatch_bwd"] = entry(us, w.P * w.H * 2 + w.P * 4 + w.N * w.H * 4,
+                                "K bf16 rows read, slot read, fp32 dx written")
+    del dy, d_out, d_g, dx
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +278,10 @@ def main():
                     help="quota planner's threshold bound, in units of S*K")
     ap.add_argument("--vio", type=float, default=-1.0,
                     help="target max_vio of the moonep workload's routing (default 20)")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip the training-side kernels (prefetch, reduce_grad, backward)")
+    ap.add_argument("--h-prime", type=int, default=2048,
+                    help="expert intermediate size H' of the prefetched weights")
     ap.add_argument("--maxvio-sweep", action="store_true",
                     help="moonep: also time the step at max_vio 0.2, 1, 10, 20 (same buffers)")
     args = ap.parse_args()
@@ -341,6 +412,10 @@ def main():
     status = int(buf["status"].item())
     hdr = buf["plan"][:16].cpu().numpy()
     planners = planner_report(lbt, torch, w, buf["counts"], w.B, tau_max, dev)
+    training = None
+    if not args.no_train:
+        print("[bench] training-side kernels", file=sys.stderr, flush=True)
+        training = training_report(lbt, torch, w, path, buf, dev, args.h_prime, 10)
     if args.calib_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
         b = torch.empty_like(a)
@@ -392,6 +467,7 @@ def main():
         "replica_segments": int(hdr[0]),
         "planners": planners,
         **({"maxvio_sweep": sweep} if sweep else {}),
+        **({"training": training} if training else {}),
         "status": status,
         "device": torch.cuda.get_device_name(0),
     }

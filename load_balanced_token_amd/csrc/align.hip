@@ -14,49 +14,12 @@
 // tile) + popcount of the sub-tile's bit mask of tokens holding e below this
 // token.  A token holds K distinct experts, so ranks by token order equal
 // ranks by flat index f = t*K + k.
-#include "lbt_internal.h"
+#include "align_core.h"
 
 namespace lbt {
 
 constexpr int kAlignThreads = kTileTokens;       // one thread per token
 constexpr int kBlockWaves = kAlignThreads / kWave; // blocks handled per workgroup
-
-__device__ void align_blocks(const int32_t* __restrict__ plan, const Dims& d,
-                             int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_wrow,
-                             int32_t* __restrict__ block_expert) {
-  const PlanLayout& pl = d.pl;
-  const long long gb = (long long)(blockIdx.x - d.n_tiles) * kBlockWaves + wave_id();
-  if (gb >= (long long)d.R * d.n_blocks) return;
-  const int r = (int)(gb / d.n_blocks);
-  const int b = (int)(gb - (long long)r * d.n_blocks);
-  const int lane = lane_id();
-  const int nrp = plan[pl.n_rows_padded + r];
-  const int row0 = b * d.blk;
-  if (row0 >= nrp) {
-    if (lane == 0) {
-      block_wrow[gb] = -1;
-      block_expert[gb] = -1;
-    }
-    return;
-  }
-  const int ns = plan[pl.n_seg + r];
-  const int32_t* starts = plan + pl.seg_start + (long long)r * (pl.max_seg + 1);
-  int lo = 0, hi = ns;  // last segment starting at or before row0
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (starts[mid] <= row0) lo = mid + 1; else hi = mid;
-  }
-  const int s = lo - 1;
-  const long long si = (long long)r * pl.max_seg + s;
-  if (lane == 0) {
-    block_wrow[gb] = plan[pl.seg_wrow + si];
-    block_expert[gb] = plan[pl.seg_expert + si];
-  }
-  const int real_end = starts[s] + plan[pl.seg_count + si];
-  const int sentinel = (int)d.P;
-  for (int row = max(row0, real_end) + lane; row < row0 + d.blk; row += kWave)
-    sorted_ids[(long long)r * d.C + row] = sentinel;
-}
 
 __global__ __launch_bounds__(kAlignThreads) void k_align(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ work,
@@ -64,7 +27,8 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_wrow,
     int32_t* __restrict__ block_expert, int32_t* __restrict__ status) {
   if ((int)blockIdx.x >= d.n_tiles) {
-    align_blocks(plan, d, sorted_ids, block_wrow, block_expert);
+    const long long gb = (long long)(blockIdx.x - d.n_tiles) * kBlockWaves + wave_id();
+    if (gb < (long long)d.R * d.n_blocks) align_blocks(plan, d, gb, sorted_ids, block_wrow, block_expert);
     return;
   }
   __shared__ int sH[kMaxE], sO[kMaxE], sHome[kMaxE], sBase[kMaxE];

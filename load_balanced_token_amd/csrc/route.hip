@@ -70,13 +70,6 @@ __global__ __launch_bounds__(256) void k_tile_scan(Dims d, int32_t* __restrict__
   }
 }
 
-static int route_vec(const float* p, int E) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  if ((a & 15) == 0 && (E & 3) == 0) return 4;
-  if ((a & 7) == 0 && (E & 1) == 0) return 2;
-  return 1;
-}
-
 hipError_t launch_route(const Dims& d, const float* logits, const float* bias, int32_t* ids,
                         float* gates, int32_t* work, hipStream_t st) {
   if (d.n_tiles == 0 || d.S == 0) return hipSuccess;

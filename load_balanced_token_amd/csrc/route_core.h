@@ -106,30 +106,31 @@ __device__ __forceinline__ void load_row(const float* __restrict__ row, int E, i
   for (int v = 0; v < V; ++v) raw[v] = (e0 + v < E) ? row[e0 + v] : 0.f;
 }
 
-// LDS of one route workgroup.
-struct RouteSmem {
-  int hist[kMaxE];
-  // winners of each round: expert and raw logit, per wave, token row and k
+// Winners of each round: expert and raw logit, per wave, token row and k.
+struct RouteScratch {
   int s_id[kRouteWaves][kRowsPerWave][kMaxK];
   float s_raw[kRouteWaves][kRowsPerWave][kMaxK];
 };
 
-// Route the tokens of tile `tile` (1024 threads) and write its expert
-// histogram to tile_counts[e][tile].
-template <int V>
-__device__ __forceinline__ void route_tile(const float* __restrict__ logits,
+// LDS of one route workgroup.
+struct RouteSmem {
+  int hist[kMaxE];
+  RouteScratch rs;
+};
+
+// Route tokens [t0, t0 + len), len <= 128, with 1024 threads; for every
+// chosen (token, expert) pair call hist_add(t, expert).  Contains one
+// workgroup barrier (after the row loads), so state the caller set up before
+// the call (a zeroed histogram) is visible to hist_add.
+template <int V, typename HistAdd>
+__device__ __forceinline__ void route_span(const float* __restrict__ logits,
                                            const float* __restrict__ bias, const Dims& d, int vec,
-                                           int tile, int32_t* __restrict__ ids,
-                                           float* __restrict__ gates,
-                                           int32_t* __restrict__ tile_counts, RouteSmem& sm) {
-  int* hist = sm.hist;
+                                           int t0, int len, int32_t* __restrict__ ids,
+                                           float* __restrict__ gates, RouteScratch& sm,
+                                           HistAdd hist_add) {
   auto& s_id = sm.s_id;
   auto& s_raw = sm.s_raw;
   const int E = d.E, K = d.K;
-  const int r = tile / d.tpr, j = tile - r * d.tpr;
-  const int t0 = r * d.S + j * kTileTokens;
-  const int len = min(kTileTokens, d.S - j * kTileTokens);
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) hist[e] = 0;
 
   const int lane = lane_id(), wv = wave_id();
   const int row = lane / kRowLanes, rl = lane % kRowLanes;
@@ -150,7 +151,7 @@ __device__ __forceinline__ void route_tile(const float* __restrict__ logits,
       for (int v = 0; v < V; ++v) rows[u][v] = 0.f;
     }
   }
-  __syncthreads();   // hist zeroed
+  __syncthreads();   // the caller's histogram set-up is visible
 
 #pragma unroll
   for (int u = 0; u < kRoutePasses; ++u) {
@@ -223,14 +224,39 @@ __device__ __forceinline__ void route_tile(const float* __restrict__ logits,
         if (d.renorm) g = g / gsum;
         ids[t * K + kk] = id;
         gates[t * K + kk] = (float)g;
-        atomicAdd(&hist[id], 1);
+        hist_add(t, id);
       }
     }
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+// Route the tokens of tile `tile` (1024 threads) and write its expert
+// histogram to tile_counts[e][tile].
+template <int V>
+__device__ __forceinline__ void route_tile(const float* __restrict__ logits,
+                                           const float* __restrict__ bias, const Dims& d, int vec,
+                                           int tile, int32_t* __restrict__ ids,
+                                           float* __restrict__ gates,
+                                           int32_t* __restrict__ tile_counts, RouteSmem& sm) {
+  int* hist = sm.hist;
+  const int r = tile / d.tpr, j = tile - r * d.tpr;
+  const int t0 = r * d.S + j * kTileTokens;
+  const int len = min(kTileTokens, d.S - j * kTileTokens);
+  for (int e = threadIdx.x; e < d.E; e += kRouteThreads) hist[e] = 0;
+  route_span<V>(logits, bias, d, vec, t0, len, ids, gates, sm.rs,
+                [&](long long, int id) { atomicAdd(&hist[id], 1); });
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kRouteThreads)
+  for (int e = threadIdx.x; e < d.E; e += kRouteThreads)
     tile_counts[(long long)e * d.n_tiles + tile] = hist[e];
+}
+
+// Widest aligned logit load (floats) for rows of E floats starting at p.
+static inline int route_vec(const float* p, int E) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  if ((a & 15) == 0 && (E & 3) == 0) return 4;
+  if ((a & 7) == 0 && (E & 1) == 0) return 2;
+  return 1;
 }
 
 }  // namespace lbt

@@ -382,11 +382,16 @@ class Path:
         self.combine(buf["recv"] if out is None else out, buf["slot"], buf["gates"], buf["y"],
                      stream=stream)
 
-    def recv_views(self, recv, n_rows_padded):
-        """Zero-copy views recv[r, :n_rows_padded[r]] (valid until the next
-        dispatch into ``recv``); ``n_rows_padded`` is a host sequence."""
+    def recv_views(self, recv, n_rows_padded, zero_copy=True):
+        """Per-rank views recv[r, :n_rows_padded[r]] of the static buffer;
+        ``n_rows_padded`` is a host sequence.  Zero-copy views are
+        overwritten by the next dispatch into ``recv`` and must not be kept
+        past it (autograd must not save them); zero_copy=False returns
+        clones that may be kept ([MoonEP-GR] "Ένα ρεαλιστικό πλαίσιο
+        αξιολόγησης": views are replaced by the next dispatch or combine)."""
         C = self.sizes["C"]
-        return [recv[r * C: r * C + int(n)] for r, n in enumerate(n_rows_padded)]
+        views = [recv[r * C: r * C + int(n)] for r, n in enumerate(n_rows_padded)]
+        return views if zero_copy else [v.clone() for v in views]
 
 
 # --------------------------------------------------------------------------- plan blob

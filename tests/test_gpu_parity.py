@@ -178,6 +178,28 @@ def test_dispatch_combine_full_size_sampled(name):
     assert (np.abs(yh - want) <= gu.COMBINE_RTOL * np.abs(want) + 1e-30).all()
 
 
+def test_recv_views_zero_copy_and_clones():
+    """Zero-copy views alias the receive buffer (the next dispatch changes
+    them); zero_copy=False clones keep the rows."""
+    t = gu.torch()
+    w = WORKLOADS["tiny"]
+    logits = router_logits(w, 0)
+    res = gu.run_front(gu.shape_of(w), logits)
+    path, C = res["path"], res["sizes"]["C"]
+    recv = t.zeros((w.R * C, w.H), dtype=t.int16, device="cuda")
+    x = gu.h2d(activations(w, 0))
+    path.dispatch(x, res["dev"]["slot"], recv)
+    nrp = res["plan_fields"]["n_rows_padded"]
+    views = path.recv_views(recv, nrp)
+    kept = path.recv_views(recv, nrp, zero_copy=False)
+    assert all(v.data_ptr() == recv[r * C:].data_ptr() for r, v in enumerate(views))
+    before = [k.clone() for k in kept]
+    path.dispatch(t.zeros_like(x), res["dev"]["slot"], recv)
+    t.cuda.synchronize()
+    assert any(int(v.abs().sum().item()) != int(b.abs().sum().item()) for v, b in zip(views, before))
+    assert all(t.equal(k, b) for k, b in zip(kept, before))
+
+
 # --------------------------------------------------------------------------- max_vio sweep
 @pytest.mark.parametrize("vio", [0.2, 1.0, 10.0, 20.0])
 @pytest.mark.parametrize("planner", ["fixed", "quota"])

@@ -213,3 +213,20 @@ def test_capacity_formula_bounds_every_plan():
     assert oracle.capacity(256, 8, 4096, 128) == 65280
     assert oracle.capacity(384, 8, 8192, 128) == 114304
     assert oracle.capacity(256, 8, 512, 64) == 20224
+
+
+def test_greedy_replica_gap_is_bounded_and_reported():
+    """The fixed rule's greedy merge is not minimal in general: over the tiny
+    cases, min replicas (brute force, no rule) <= oracle replicas <=
+    overflowing experts + deficit ranks - 1; the gap distribution is printed."""
+    gaps = []
+    for ids, E, R, S, K in _tiny_cases():
+        _, plan, _ = _run(ids, E, R, S, K, B=1, blk=1)
+        n = len(plan["replicas"])
+        lo = bf.min_replicas(ids.tolist(), E, R, S)
+        hi = int((plan["o"] > 0).sum()) + int((plan["deficit"] > 0).sum()) - 1
+        assert lo <= n and (n == 0 or n <= hi)
+        gaps.append(n - lo)
+    hist = {g: gaps.count(g) for g in sorted(set(gaps))}
+    print(f"greedy minus minimum replicas over {len(gaps)} tiny cases: {hist}")
+    assert min(gaps) == 0

@@ -106,11 +106,40 @@ __device__ __forceinline__ void load_row(const float* __restrict__ row, int E, i
   for (int v = 0; v < V; ++v) raw[v] = (e0 + v < E) ? row[e0 + v] : 0.f;
 }
 
-// Winners of each round: expert and raw logit, per wave, token row and k.
+// Winners of each round: expert per wave, token row and k.
 struct RouteScratch {
   int s_id[kRouteWaves][kRowsPerWave][kMaxK];
-  float s_raw[kRouteWaves][kRowsPerWave][kMaxK];
 };
+
+// The lane's best T keys among those that come after (tk, tv) in the order
+// (key descending, local index ascending) -- all keys when !AFTER -- sorted
+// in that order into lk/lv; unused entries hold key 0 (below every valid
+// key, which is > 0x007FFFFF).  Strict '>' keeps the lower index first on
+// equal keys.
+template <int V, int T, bool AFTER>
+__device__ __forceinline__ void build_list(const uint32_t (&key)[V], uint32_t tk, int tv,
+                                           uint32_t (&lk)[T], int (&lv)[T]) {
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    lk[j] = 0u;
+    lv[j] = 0;
+  }
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    uint32_t x = key[v];
+    if constexpr (AFTER) x = (x < tk || (x == tk && v > tv)) ? x : 0u;
+    bool c[T];
+#pragma unroll
+    for (int j = 0; j < T; ++j) c[j] = x > lk[j];
+#pragma unroll
+    for (int j = T - 1; j > 0; --j) {
+      lk[j] = c[j - 1] ? lk[j - 1] : (c[j] ? x : lk[j]);
+      lv[j] = c[j - 1] ? lv[j - 1] : (c[j] ? v : lv[j]);
+    }
+    lk[0] = c[0] ? x : lk[0];
+    lv[0] = c[0] ? v : lv[0];
+  }
+}
 
 // LDS of one route workgroup.
 struct RouteSmem {
@@ -129,15 +158,11 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
                                            float* __restrict__ gates, RouteScratch& sm,
                                            HistAdd hist_add) {
   auto& s_id = sm.s_id;
-  auto& s_raw = sm.s_raw;
   const int E = d.E, K = d.K;
 
   const int lane = lane_id(), wv = wave_id();
   const int row = lane / kRowLanes, rl = lane % kRowLanes;
   const int e0 = rl * V;
-  float b[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) b[v] = (bias != nullptr && e0 + v < E) ? bias[e0 + v] : 0.f;
 
   // all rows of this wave first (one memory latency), then the rounds
   float rows[kRoutePasses][V];
@@ -158,26 +183,31 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
     const int i = (u * kRouteWaves + wv) * kRowsPerWave + row;
     const bool valid = i < len;
     if (!__any(valid)) continue;
-    const float(&raw)[V] = rows[u];
+    // keys only from here on: gates and the softmax re-read the row, so the
+    // raw values do not stay live through the rounds
     uint32_t key[V];
+    if (bias != nullptr) {
 #pragma unroll
-    for (int v = 0; v < V; ++v)
-      key[v] = (valid && e0 + v < E) ? ordered_key(bias != nullptr ? raw[v] + b[v] : raw[v]) : 0u;
-    uint32_t taken = 0;
+      for (int v = 0; v < V; ++v)
+        key[v] = (valid && e0 + v < E) ? ordered_key(rows[u][v] + bias[e0 + v]) : 0u;
+    } else {
+#pragma unroll
+      for (int v = 0; v < V; ++v) key[v] = (valid && e0 + v < E) ? ordered_key(rows[u][v]) : 0u;
+    }
+    // Each lane keeps its best T keys sorted (key desc, local index asc);
+    // a round compares list heads across the row and the winner pops.  A
+    // lane whose full list runs dry refills from the keys after the one it
+    // gave up last, so the order of choices is exactly the K rounds of
+    // "largest untaken key, lowest expert on ties".
+    constexpr int T = V < 4 ? V : 4;
+    uint32_t lk[T];
+    int lv[T];
+    build_list<V, T, false>(key, 0u, 0, lk, lv);
+    bool more = V > T && lk[T - 1] != 0u;   // the lane may hold keys past its list
     for (int k = 0; k < K; ++k) {
-      // lane-local best untaken key; strict '>' keeps the lower expert on ties
-      uint32_t best = 0;
-      int bv = 0;
-      float braw = 0.f;
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const bool ok = !((taken >> v) & 1u) && key[v] > best;
-        best = ok ? key[v] : best;
-        bv = ok ? v : bv;
-        braw = ok ? raw[v] : braw;
-      }
-      const uint32_t rmax = row_max_u32(best);
-      const bool cand = valid && best == rmax;
+      const uint32_t head = lk[0];
+      const uint32_t rmax = row_max_u32(head);
+      const bool cand = valid && head == rmax;
       const unsigned long long m = __ballot(cand);
       // candidates below this lane in the wave, minus those in lower rows
       const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
@@ -185,17 +215,43 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
       const int p1 = __popcll(m & 0xFFFFull), p2 = __popcll(m & 0xFFFFFFFFull),
                 p3 = __popcll(m & 0xFFFFFFFFFFFFull);
       const int lower = row == 0 ? 0 : row == 1 ? p1 : row == 2 ? p2 : p3;
+      bool dry = false;
       if (cand && below == lower) {        // lowest lane of the row = lowest expert
-        taken |= 1u << bv;
-        s_id[wv][row][k] = e0 + bv;
-        s_raw[wv][row][k] = braw;
+        const uint32_t tk = lk[0];
+        const int tv = lv[0];
+        s_id[wv][row][k] = e0 + tv;
+#pragma unroll
+        for (int j = 0; j + 1 < T; ++j) {
+          lk[j] = lk[j + 1];
+          lv[j] = lv[j + 1];
+        }
+        lk[T - 1] = 0u;
+        if constexpr (V > T) {
+          dry = more && lk[0] == 0u;
+          if (dry) {
+            lk[0] = tk;                    // remember the threshold for the refill
+            lv[0] = tv;
+          }
+        }
+      }
+      if constexpr (V > T) {
+        if (__any(dry)) {
+          if (dry) {
+            build_list<V, T, true>(key, lk[0], lv[0], lk, lv);
+            more = lk[T - 1] != 0u;
+          }
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();
 
     const long long t = (long long)t0 + i;
+    // raw logits are read back from the row just loaded (cache hits)
+    const float* lrow = logits + (valid ? t : (long long)t0) * E;
     double mx = 0.0, denom = 1.0;
     if (d.score_fn == LBT_SOFTMAX) {
+      float raw[V];
+      load_row<V>(lrow, E, e0, vec, raw);
       float m = -INFINITY;
 #pragma unroll
       for (int v = 0; v < V; ++v)
@@ -211,7 +267,7 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
     if (d.renorm) {
       double part = 0.0;
       for (int kk = rl; kk < K; kk += kRowLanes) {
-        const double lg = (double)s_raw[wv][row][kk];
+        const double lg = valid ? (double)lrow[s_id[wv][row][kk]] : 0.0;
         part += d.score_fn == LBT_SIGMOID ? 1.0 / (1.0 + exp(-lg)) : exp(lg - mx) / denom;
       }
       gsum = row_sum_f64(part);
@@ -219,7 +275,7 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
     if (valid) {
       for (int kk = rl; kk < K; kk += kRowLanes) {
         const int id = s_id[wv][row][kk];
-        const double lg = (double)s_raw[wv][row][kk];
+        const double lg = (double)lrow[id];
         double g = d.score_fn == LBT_SIGMOID ? 1.0 / (1.0 + exp(-lg)) : exp(lg - mx) / denom;
         if (d.renorm) g = g / gsum;
         ids[t * K + kk] = id;

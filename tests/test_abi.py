@@ -100,3 +100,15 @@ def test_host_checks_reject_bad_pointers_before_any_launch():
                              P(0x5000), None, None) == -1
     assert L.lbt_dispatch_bwd(ctypes.byref(sh), P(0x1000), P(0x2000), 0, P(0x3004), None) == -1
     assert L.lbt_dispatch_bwd(ctypes.byref(sh), P(0x1000), P(0x2000), 9, P(0x3000), None) == -1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 exits with a message (no GPU
+    needed to check it)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""

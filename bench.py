@@ -80,16 +80,30 @@ def cpu_baseline(name, sample_S, **overrides):
     logits = router_logits(w, 0)
     x = activations(w, 0)
     score = oracle.SOFTMAX if w.score == "softmax" else oracle.SIGMOID
-    t0 = time.perf_counter()
+    steps = {}
+    t0 = tl = time.perf_counter()
+
+    def lap(name):
+        nonlocal tl
+        now = time.perf_counter()
+        steps[name] = now - tl
+        tl = now
+
     ids, gates = oracle.route_topk(logits, w.K, score)
+    lap("O1_route")
     counts = oracle.load_matrix(ids, w.R, w.S, w.E)
+    lap("O2_histogram")
     plan = oracle.plan_balance(counts, w.K, w.S, w.B, w.blk)
+    lap("O3_plan")
     al = oracle.align_sort(ids, plan)
+    lap("O4_align")
     rows, data = oracle.dispatch_rows(x, al["slot"], w.K)
+    lap("O5_dispatch")
     order = np.argsort(rows)
     srt = rows[order]
     y, _ = oracle.combine(lambda r: data[order[np.searchsorted(srt, r)]], al["slot"],
                           gates.astype(np.float32), w.K)
+    lap("O6_combine")
     dt = time.perf_counter() - t0
     if limiter is not None:
         limiter.unregister() if hasattr(limiter, "unregister") else None
@@ -101,9 +115,44 @@ def cpu_baseline(name, sample_S, **overrides):
         "sample": f"{name} shape with S={sample_S} tokens/rank (N={w.N}, P={w.P} token-slots, "
                   f"H={w.H}), layer 0; oracle route, histogram, plan, align, dispatch, combine "
                   f"end to end on one host thread in {dt:.2f} s",
-        "host_cpu": platform.processor() or platform.machine(),
+        "step_s": steps,
+        "host_cpu": host_cpu_model(),
         "host_logical_cpus": os.cpu_count(),
+        "host_affinity_cpus": len(os.sched_getaffinity(0)),
     }
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+# hipDeviceAttribute_t values of the ROCm 7 HIP runtime headers
+_HIP_ATTR = {"sclk_khz": 5, "memory_bus_width_bits": 59, "memory_clock_khz": 60,
+             "compute_units": 63}
+
+
+def device_report(torch, dev_index=0):
+    """Name, ISA, compute units, engine and memory clocks and the memory bus
+    width of the device the run used (hipDeviceGetAttribute)."""
+    import ctypes
+    p = torch.cuda.get_device_properties(dev_index)
+    rep = {"name": p.name, "arch": p.gcnArchName, "total_memory_gib": p.total_memory / 2 ** 30}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        for key, attr in _HIP_ATTR.items():
+            v = ctypes.c_int(0)
+            if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev_index) == 0:
+                rep[key] = v.value
+    except OSError:
+        pass
+    return rep
 
 
 def decode_latency(path, buf, w, x, n_steps, dev, planner="fixed"):
@@ -462,6 +511,7 @@ def main():
         "plan_us": plan_alone_us,
         "plan_in_step_us": avg_us["plan"],
         "step_device_us_median": float(np.median(step_dev_us)),
+        "step_device_us_min": float(np.min(step_dev_us)),
         "max_vio": float(hdr[1]) * w.E / w.P - 1.0,
         "rank_imbalance_before": float(hdr[2]) / w.SK - 1.0,
         "replica_segments": int(hdr[0]),
@@ -470,6 +520,7 @@ def main():
         **({"training": training} if training else {}),
         "status": status,
         "device": torch.cuda.get_device_name(0),
+        "device_info": device_report(torch, 0),
     }
     if w.name.startswith("decode"):
         print(f"[bench] decode latency over {args.decode_steps} fresh routings (HIP graph)",

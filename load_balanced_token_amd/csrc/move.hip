@@ -7,8 +7,8 @@
 // results to their source tokens ([MoonEP-GR] evaluation checklist;
 // [UltraEP] tokens return after expert compute).
 //
-// One workgroup per token row (H = 7168: dispatch 448 threads x 2 chunks of
-// 16 bytes, combine 448 threads x 4 groups of 8 bytes): short-lived waves
+// One workgroup per token row (H = 7168: dispatch 896 threads x 1 chunk of
+// 16 bytes, combine 224 threads x 8 groups of 8 bytes): short-lived waves
 // with all their loads in flight measured fastest on MI355X for both the
 // write-heavy dispatch and the read-heavy combine.
 #include "rows.h"
@@ -268,7 +268,7 @@ hipError_t launch_dispatch(const Dims& d, const uint16_t* x, const int32_t* slot
   const u32x4* xs = reinterpret_cast<const u32x4*>(x);
   u32x4* rv = reinterpret_cast<u32x4*>(recv);
   if (d.H == 7168 && d.K == 8) {   // DeepSeek-V3 / Kimi-K2 hidden size
-    hipLaunchKernelGGL((k_dispatch_w<448, 2, 8>), dim3(d.N), dim3(448), 0, st, xs, slot, rv,
+    hipLaunchKernelGGL((k_dispatch_w<896, 1, 8>), dim3(d.N), dim3(896), 0, st, xs, slot, rv,
                        (long long)d.R * d.C);
     return hipGetLastError();
   }

@@ -496,3 +496,35 @@ def test_dispatch_combine_with_dropped_pairs(H):
     got = y.cpu().numpy().astype(np.float64)
     assert (np.abs(got - want) <= gu.COMBINE_RTOL * np.abs(want) + 1e-30).all()
 
+
+
+# --------------------------------------------------------------------------- widths and limits
+@pytest.mark.parametrize("E,K,R", [(24, 4, 4), (40, 6, 8), (64, 8, 8), (128, 8, 16), (200, 8, 8),
+                                   (512, 8, 8)])
+def test_route_width_ladder(E, K, R):
+    """Every compiled route width (a lane holds V = ceil(E/16) experts: V = 2,
+    3 -> 4, 4, 8, 13 -> 16, 32), with ragged last lanes where E is not a
+    multiple of 16; the DSV3 generator at that E, full rows moved."""
+    w = WORKLOADS["dsv3"].with_(E=E, K=K, R=R, S=64, H=64, B=4, blk=16)
+    print(f"[parity] width E={E} K={K} R={R}", flush=True)
+    _edge(w)
+
+
+@pytest.mark.parametrize("case,planner", [("E512_K64", "fixed"), ("E512_K64", "quota"),
+                                          ("R512", "fixed"), ("R512", "quota")])
+def test_maximum_sizes(case, planner):
+    """The library's limits: E = 512 with K = 64 (64 top-K rounds per token,
+    every lane list refilled many times), and R = E = 512 (one expert per
+    rank, up to E + R replica pieces), through either planner."""
+    if case == "E512_K64":
+        w = WORKLOADS["dsv3"].with_(E=512, K=64, R=8, S=64, H=64, B=4, blk=16)
+    else:
+        w = WORKLOADS["dsv3"].with_(E=512, R=512, K=8, S=4, H=64, B=2, blk=4)
+    print(f"[parity] limits {case} {planner}", flush=True)
+    logits = router_logits(w, 0)
+    res = gu.run_front(gu.shape_of(w), logits, planner=planner)
+    ref = gu.run_oracle(w, logits, planner=planner)
+    gu.check_route(res, ref)
+    gu.check_plan(res["plan_fields"], ref["plan"], w.P)
+    gu.check_align(res, ref, w.R, res["sizes"]["C"])
+    _full_move_check(w, res, ref, activations(w, 0))

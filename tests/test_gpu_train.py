@@ -203,3 +203,26 @@ def test_dispatch_bwd_parity(name, S):
     got = dx.cpu().numpy().astype(np.float64)
     assert (np.abs(got - want) <= DX_RTOL * mag + 1e-30).all()
     assert np.array_equal(gu.d2h(dxb), oracle.f32_to_bf16_rne(dx.cpu().numpy()))
+
+
+@pytest.mark.parametrize("planner", ["fixed", "quota"])
+def test_prefetch_and_reduce_grad_at_limits(planner):
+    """R = E = 512 (one expert per rank, 510 replica segments, B = 2): the
+    slot table at the library's size limits through prefetch and reduce_grad."""
+    t = gu.torch()
+    w = WORKLOADS["dsv3"].with_(E=512, R=512, K=8, S=4, H=64, B=2, blk=4)
+    res, ref = _front(w, planner)
+    rng = np.random.default_rng(5)
+    W = rng.integers(0, 256, size=(w.E, 1040), dtype=np.uint8)
+    slots0 = np.full((w.R, w.B, 1040), 0x5A, np.uint8)
+    Sd = t.from_numpy(slots0).cuda()
+    res["path"].prefetch_weights(res["dev"]["plan"], t.from_numpy(W).cuda(), Sd)
+    G = rng.standard_normal((w.E, 260)).astype(np.float32)
+    SG = rng.standard_normal((w.R, w.B, 260)).astype(np.float32)
+    Gd, SGd = t.from_numpy(G).cuda(), t.from_numpy(SG).cuda()
+    res["path"].reduce_grad(res["dev"]["plan"], SGd, Gd)
+    t.cuda.synchronize()
+    assert np.array_equal(Sd.cpu().numpy(), oracle.prefetch_weights(ref["plan"], W, slots0))
+    g2, sg2 = oracle.reduce_grad(ref["plan"], SG, G)
+    assert np.array_equal(Gd.cpu().numpy(), g2) and np.array_equal(SGd.cpu().numpy(), sg2)
+    assert len(oracle.prefetch_slots(ref["plan"])) > 0

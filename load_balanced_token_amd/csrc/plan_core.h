@@ -29,6 +29,12 @@
 namespace lbt {
 
 constexpr int kPlanThreads = 1024;
+// Up to this many deficit ranks the per-expert piece counts come from a
+// register-broadcast count (cost grows with the deficit ranks); above it,
+// from binary searches (cost grows with their logarithm).  Measured on
+// MI355X: 7 deficit ranks 0.96 vs 1.68 us, about 25 3.8 vs 4.7 us, about
+// 49 4.7 vs 3.6 us.
+constexpr int kLinearDeficits = 32;
 
 __device__ __forceinline__ int pad_to(int c, int blk) { return ((c + blk - 1) / blk) * blk; }
 
@@ -45,6 +51,7 @@ struct PlanSmem {
   int sD[kMaxR + 1];      // exclusive prefix D_r
   int sCidx[kMaxR + 1];   // compact index among deficit ranks
   int sDl[kMaxR];         // compact index -> rank
+  int sDc[kMaxR];         // compact index -> D of that deficit rank (strictly increasing)
   int sRep[kMaxR + 1];    // replicas per rank, then first piece of rank
   int sPe[kMaxPieces], sPd[kMaxPieces], sPc[kMaxPieces], sPl[kMaxPieces],
       sPj[kMaxPieces];
@@ -67,7 +74,8 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
                                           int32_t* __restrict__ status) {
   auto& sT = m.sT; auto& sX = m.sX; auto& sH = m.sH; auto& sO = m.sO; auto& sNp = m.sNp;
   auto& sDlo = m.sDlo; auto& sL = m.sL; auto& sDef = m.sDef; auto& sD = m.sD;
-  auto& sCidx = m.sCidx; auto& sDl = m.sDl; auto& sRep = m.sRep; auto& sPe = m.sPe;
+  auto& sCidx = m.sCidx; auto& sDl = m.sDl; auto& sDc = m.sDc; auto& sRep = m.sRep;
+  auto& sPe = m.sPe;
   auto& sPd = m.sPd; auto& sPc = m.sPc; auto& sPl = m.sPl; auto& sPj = m.sPj; auto& sF = m.sF;
   auto& sStat = m.sStat;
   auto& sLam = m.sLam; auto& sPerm = m.sPerm; auto& sHx = m.sHx;
@@ -122,21 +130,64 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
     wave_excl_scan_lds<kMaxR / kWave>(sD, R);
     wave_excl_scan_lds<kMaxR / kWave>(sCidx, R);
     for (int r = lane; r < R; r += kWave)
-      if (sDef[r] > 0) sDl[sCidx[r]] = r;
-    for (int g = lane; g < E; g += kWave) {     // line position g, expert perm(g)
-      const int e = perm(g);
-      const int o = sT[e] - sH[e];
-      int np = 0;
-      if (consistent && o > 0) {
-        const int Oe = sO[g];
-        // the last rank with D <= x is the deficit rank holding x (ranks
-        // without deficit have empty intervals and never end up last)
-        const int dlo = upper_bound(sD, R, Oe) - 1;
-        const int dhi = upper_bound(sD, R, Oe + o - 1) - 1;
-        np = sCidx[dhi] - sCidx[dlo] + 1;
-        sDlo[g] = sCidx[dlo];
+      if (sDef[r] > 0) {
+        sDl[sCidx[r]] = r;
+        sDc[sCidx[r]] = sD[r];
       }
-      sNp[g] = np;
+    __builtin_amdgcn_wave_barrier();
+    // Pieces of the expert at line position g: its overflow [O, O + o)
+    // meets the deficit ranks from the one holding O to the one holding
+    // O + o - 1.  With c(x) = number of deficit ranks starting at or below
+    // x, those are compact indices c(O) - 1 .. c(O + o - 1) - 1.
+    const int nDef = sCidx[R];
+    if (nDef <= kLinearDeficits) {
+      // few deficit ranks: lane c holds start c, and every lane counts the
+      // starts at or below its experts' first and last overflow positions,
+      // one register broadcast per deficit rank (no LDS in the loop)
+      const int dcv = lane < nDef ? sDc[lane] : 0;
+      for (int g0 = 0; g0 < E; g0 += 4 * kWave) {
+        int xlo[4], xhi[4], clo[4], chi[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int g = g0 + lane + i * kWave;
+          const int o = g < E ? sT[perm(g)] - sH[perm(g)] : 0;
+          xlo[i] = g < E ? sO[g] : -1;      // empty slots count nothing
+          xhi[i] = g < E ? xlo[i] + o - 1 : -2;
+          clo[i] = 0;
+          chi[i] = 0;
+        }
+        for (int c = 0; c < nDef; ++c) {
+          const int dc = __builtin_amdgcn_readlane(dcv, c);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            clo[i] += dc <= xlo[i];
+            chi[i] += dc <= xhi[i];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int g = g0 + lane + i * kWave;
+          if (g < E) {
+            const bool has = consistent && xhi[i] >= xlo[i];
+            sNp[g] = has ? chi[i] - clo[i] + 1 : 0;
+            if (has) sDlo[g] = clo[i] - 1;
+          }
+        }
+      }
+    } else {
+      for (int g = lane; g < E; g += kWave) {     // line position g, expert perm(g)
+        const int e = perm(g);
+        const int o = sT[e] - sH[e];
+        int np = 0;
+        if (consistent && o > 0) {
+          const int Oe = sO[g];
+          const int clo = upper_bound(sDc, nDef, Oe);
+          const int chi = upper_bound(sDc, nDef, Oe + o - 1);
+          np = chi - clo + 1;
+          sDlo[g] = clo - 1;
+        }
+        sNp[g] = np;
+      }
     }
     __builtin_amdgcn_wave_barrier();
     const int nP = wave_excl_scan_lds<kMaxE / kWave>(sNp, E);

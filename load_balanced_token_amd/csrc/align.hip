@@ -46,6 +46,14 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
   const int totOv = plan[pl.hdr + LBT_HDR_TOTAL_OVERFLOW];
   const int32_t* tbase = work + work_tile_base(d) + (long long)tile * E;
   const int tid = threadIdx.x;
+  const long long t = (long long)t0 + tid;
+
+  // the token's first kPre expert ids, loaded before the plan so that the
+  // two latencies overlap (for K <= kPre no id is read twice)
+  constexpr int kPre = 8;
+  int idp[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) idp[k] = (tid < len && k < K) ? ids[t * K + k] : -1;
 
   for (int e = tid; e < E; e += kAlignThreads) {
     sH[e] = plan[pl.h + e];
@@ -55,7 +63,9 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
 #pragma unroll
     for (int s = 0; s < kSubTiles; ++s) sMask[s][e] = 0u;
   }
-  for (int g = tid; g < nP; g += kAlignThreads) {
+  // the whole piece table (entries past nP are unused), so that these loads
+  // do not wait for the piece count
+  for (int g = tid; g < pl.max_pieces; g += kAlignThreads) {
     sPl[g] = plan[pl.piece_line + g];
     sPd[g] = plan[pl.piece_rank + g];
     sPr[g] = plan[pl.piece_row + g];
@@ -66,14 +76,16 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
   int flags = 0;
   const int sub = tid / kSubTokens;
   const uint32_t bit = 1u << (tid % kSubTokens);
-  const long long t = (long long)t0 + tid;
+  auto mark = [&](int e) {
+    if (e < 0 || e >= E) return;
+    const uint32_t old = atomicOr(&sMask[sub][e], bit);
+    if (old & bit) flags |= LBT_ST_DUPID;
+  };
   if (tid < len) {
-    for (int k = 0; k < K; ++k) {
-      const int e = ids[t * K + k];
-      if (e < 0 || e >= E) continue;
-      const uint32_t old = atomicOr(&sMask[sub][e], bit);
-      if (old & bit) flags |= LBT_ST_DUPID;
-    }
+#pragma unroll
+    for (int k = 0; k < kPre; ++k)
+      if (k < K) mark(idp[k]);
+    for (int k = kPre; k < K; ++k) mark(ids[t * K + k]);
   }
   __syncthreads();
   for (int e = tid; e < E; e += kAlignThreads) {
@@ -86,38 +98,41 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
   }
   __syncthreads();
 
-  if (tid < len) {
-    for (int k = 0; k < K; ++k) {
-      const long long f = t * K + k;
-      const int e = ids[f];
-      if (e < 0 || e >= E) {
-        flags |= LBT_ST_BADID;
-        slot[f] = -1;
-        continue;
-      }
-      const int q = sBase[e] + sSub[sub][e] + __popc(sMask[sub][e] & (bit - 1u));
-      const int h = sH[e];
-      int dd, row;
-      bool ok = true;
-      if (q < h) {
-        dd = e / nh;
-        row = sHome[e] + q;
-      } else {
-        const int o = sO[e] + (q - h);
-        const int g = upper_bound(sPl, nP, o) - 1;
-        ok = o < totOv && g >= 0 && sPe[g] == e;
-        dd = ok ? sPd[g] : 0;
-        row = ok ? sPr[g] + (o - sPl[g]) : 0;
-      }
-      if (!ok || row >= C) {
-        flags |= LBT_ST_CAPACITY;
-        slot[f] = -1;
-        continue;
-      }
-      const long long dst = (long long)dd * C + row;
-      slot[f] = (int)dst;
-      sorted_ids[dst] = (int)f;
+  auto place = [&](int k, int e) {
+    const long long f = t * K + k;
+    if (e < 0 || e >= E) {
+      flags |= LBT_ST_BADID;
+      slot[f] = -1;
+      return;
     }
+    const int q = sBase[e] + sSub[sub][e] + __popc(sMask[sub][e] & (bit - 1u));
+    const int h = sH[e];
+    int dd, row;
+    bool ok = true;
+    if (q < h) {
+      dd = e / nh;
+      row = sHome[e] + q;
+    } else {
+      const int o = sO[e] + (q - h);
+      const int g = upper_bound(sPl, nP, o) - 1;
+      ok = o < totOv && g >= 0 && sPe[g] == e;
+      dd = ok ? sPd[g] : 0;
+      row = ok ? sPr[g] + (o - sPl[g]) : 0;
+    }
+    if (!ok || row >= C) {
+      flags |= LBT_ST_CAPACITY;
+      slot[f] = -1;
+      return;
+    }
+    const long long dst = (long long)dd * C + row;
+    slot[f] = (int)dst;
+    sorted_ids[dst] = (int)f;
+  };
+  if (tid < len) {
+#pragma unroll
+    for (int k = 0; k < kPre; ++k)
+      if (k < K) place(k, idp[k]);
+    for (int k = kPre; k < K; ++k) place(k, ids[t * K + k]);
   }
   if (flags && status != nullptr) atomicOr(status, flags);
 }

@@ -1,5 +1,5 @@
-// Block tables of the block-aligned sort, shared by the align kernel and the
-// fused small-batch front: for block gb (rank r, block b) of one wave, the
+// Block tables of the block-aligned sort, written by the align kernel's
+// extra workgroups: for block gb (rank r, block b) of one wave, the
 // weight row and expert of the segment covering it (or -1 past the rank's
 // padded end), and the padding sentinel P in its rows past the segment's
 // real rows.  [AlignSort]: every expert's share is padded to the grouped
@@ -18,6 +18,7 @@ __device__ __forceinline__ void align_blocks(const int32_t* __restrict__ plan, c
   const int b = (int)(gb - (long long)r * d.n_blocks);
   const int lane = lane_id();
   const int nrp = plan[pl.n_rows_padded + r];
+  const int ns = plan[pl.n_seg + r];
   const int row0 = b * d.blk;
   if (row0 >= nrp) {
     if (lane == 0) {
@@ -26,14 +27,15 @@ __device__ __forceinline__ void align_blocks(const int32_t* __restrict__ plan, c
     }
     return;
   }
-  const int ns = plan[pl.n_seg + r];
+  // the last segment starting at or before row0: count the starts <= row0
+  // (non-decreasing) with the wave's lanes loading them side by side
   const int32_t* starts = plan + pl.seg_start + (long long)r * (pl.max_seg + 1);
-  int lo = 0, hi = ns;  // last segment starting at or before row0
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (starts[mid] <= row0) lo = mid + 1; else hi = mid;
+  int nle = 0;
+  for (int i0 = 0; i0 < ns; i0 += kWave) {
+    const int i = i0 + lane;
+    nle += __popcll(__ballot(i < ns && starts[i] <= row0));
   }
-  const int s = lo - 1;
+  const int s = nle - 1;
   const long long si = (long long)r * pl.max_seg + s;
   if (lane == 0) {
     block_wrow[gb] = plan[pl.seg_wrow + si];

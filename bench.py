@@ -156,12 +156,14 @@ def device_report(torch, dev_index=0):
 
 
 def decode_latency(path, buf, w, x, n_steps, dev, planner="fixed"):
-    """p50/p99 latency of one whole step over ``n_steps`` fresh routings.
+    """p50/p99 latency of one step over ``n_steps`` fresh routings, for the
+    whole step (route -> plan -> align -> dispatch -> combine) and for the
+    step without the combine.
 
-    Every routing is resident in HBM; the step (route -> plan -> align ->
-    dispatch -> combine) is captured once in a HIP graph whose first node
-    gathers routing number ``idx`` (a device counter the graph advances), so
-    each replay runs on new router logits with no host work in between."""
+    Every routing is resident in HBM; each variant is captured once in a HIP
+    graph whose first node gathers routing number ``idx`` (a device counter
+    the graph advances), so each replay runs on new router logits with no
+    host work in between."""
     import numpy as np
     import torch
     from workloads import router_logits
@@ -173,36 +175,56 @@ def decode_latency(path, buf, w, x, n_steps, dev, planner="fixed"):
     cur = torch.empty((1, w.N, w.E), dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
+    plan_fn = path.plan_balance if planner == "fixed" else path.plan_quota
 
-    def body():
+    def full():
         torch.index_select(all_logits, 0, idx, out=cur)
         path.step(cur[0], x, buf, planner=planner)
         idx.add_(1)
 
-    with torch.cuda.stream(stream):        # warm up outside the graph
-        for _ in range(3):
+    def no_combine():
+        torch.index_select(all_logits, 0, idx, out=cur)
+        path.route_topk(cur[0], buf["ids"], buf["gates"], buf["counts"], buf["work"])
+        plan_fn(buf["counts"], buf["plan"], buf["status"])
+        path.align_sort(buf["ids"], buf["work"], buf["plan"], buf["slot"], buf["sorted_ids"],
+                        buf["block_wrow"], buf["block_expert"], buf["status"])
+        path.dispatch(x, buf["slot"], buf["recv"])
+        idx.add_(1)
+
+    def replay(body):
+        # routing numbers 0, 1, 2 for the warm-up, then 0 .. n_steps - 1 for
+        # the replays: the counter starts from zero for every variant
+        assert n_steps >= 3
+        idx.zero_()
+        with torch.cuda.stream(stream):        # warm up outside the graph
+            for _ in range(3):
+                body()
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
             body()
-    torch.cuda.current_stream().wait_stream(stream)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        body()
-    idx.zero_()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_steps)]
-    t0 = time.perf_counter()
-    for a, b in evs:
-        a.record()
-        g.replay()
-        b.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    lat = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
-    # the last replay's routing, checked for a clean status
-    status = int(buf["status"].item())
+        idx.zero_()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_steps)]
+        t0 = time.perf_counter()
+        for a, b in evs:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        lat = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        # the last replay's routing, checked for a clean status
+        return lat, wall, int(buf["status"].item())
+
+    lat_nc, _, st_nc = replay(no_combine)
+    lat, wall, status = replay(full)
     return {"p50_us": float(np.percentile(lat, 50)), "p99_us": float(np.percentile(lat, 99)),
             "mean_us": float(lat.mean()), "steps": n_steps, "wall_s": wall, "status": status,
+            "without_combine": {"p50_us": float(np.percentile(lat_nc, 50)),
+                                "p99_us": float(np.percentile(lat_nc, 99)), "status": st_nc},
             "note": "graph replay incl. the gather of fresh router logits"}
 
 

@@ -18,16 +18,24 @@
 
 namespace lbt {
 
-constexpr int kAlignThreads = kTileTokens;       // one thread per token
-constexpr int kBlockWaves = kAlignThreads / kWave; // blocks handled per workgroup
+// Threads per token.  Measured on MI355X (align alone, in the step):
+// 1 / 2 / 4 / 8 threads per token took DSV3 15.7 / 11.6 / 9.5 / 8.9 us and
+// Kimi-K3 62 / 49 / 37 / 36 us; 4 keeps every thread busy for K = 4 and 8.
+constexpr int kAlignTPT = 4;
+constexpr int kAlignThreads = kTileTokens * kAlignTPT;
+constexpr int kBlockWaves = kAlignThreads / kWave;   // blocks handled per workgroup
 
-__global__ __launch_bounds__(kAlignThreads) void k_align(
+// Thread tid serves token tid % kTileTokens of the tile and its pairs
+// k = part, part + TPT, ... with part = tid / kTileTokens.
+template <int TPT>
+__global__ __launch_bounds__(kTileTokens * TPT) void k_align(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ work,
     const int32_t* __restrict__ plan, Dims d, int32_t* __restrict__ slot,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_wrow,
     int32_t* __restrict__ block_expert, int32_t* __restrict__ status) {
+  constexpr int NT = kTileTokens * TPT;
   if ((int)blockIdx.x >= d.n_tiles) {
-    const long long gb = (long long)(blockIdx.x - d.n_tiles) * kBlockWaves + wave_id();
+    const long long gb = (long long)(blockIdx.x - d.n_tiles) * (NT / kWave) + wave_id();
     if (gb < (long long)d.R * d.n_blocks) align_blocks(plan, d, gb, sorted_ids, block_wrow, block_expert);
     return;
   }
@@ -46,16 +54,21 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
   const int totOv = plan[pl.hdr + LBT_HDR_TOTAL_OVERFLOW];
   const int32_t* tbase = work + work_tile_base(d) + (long long)tile * E;
   const int tid = threadIdx.x;
-  const long long t = (long long)t0 + tid;
+  const int ti = tid % kTileTokens, part = tid / kTileTokens;
+  const long long t = (long long)t0 + ti;
 
-  // the token's first kPre expert ids, loaded before the plan so that the
-  // two latencies overlap (for K <= kPre no id is read twice)
-  constexpr int kPre = 8;
+  // the thread's first kPre expert ids (k = part + j * TPT), loaded before
+  // the plan so that the two latencies overlap (for K <= 8 no id is read
+  // twice)
+  constexpr int kPre = (8 + TPT - 1) / TPT;
   int idp[kPre];
 #pragma unroll
-  for (int k = 0; k < kPre; ++k) idp[k] = (tid < len && k < K) ? ids[t * K + k] : -1;
+  for (int j = 0; j < kPre; ++j) {
+    const int k = part + j * TPT;
+    idp[j] = (ti < len && k < K) ? ids[t * K + k] : -1;
+  }
 
-  for (int e = tid; e < E; e += kAlignThreads) {
+  for (int e = tid; e < E; e += NT) {
     sH[e] = plan[pl.h + e];
     sO[e] = plan[pl.O + e];
     sHome[e] = plan[pl.home_row + e];
@@ -65,7 +78,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
   }
   // the whole piece table (entries past nP are unused), so that these loads
   // do not wait for the piece count
-  for (int g = tid; g < pl.max_pieces; g += kAlignThreads) {
+  for (int g = tid; g < pl.max_pieces; g += NT) {
     sPl[g] = plan[pl.piece_line + g];
     sPd[g] = plan[pl.piece_rank + g];
     sPr[g] = plan[pl.piece_row + g];
@@ -74,21 +87,21 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
   __syncthreads();
 
   int flags = 0;
-  const int sub = tid / kSubTokens;
-  const uint32_t bit = 1u << (tid % kSubTokens);
+  const int sub = ti / kSubTokens;
+  const uint32_t bit = 1u << (ti % kSubTokens);
   auto mark = [&](int e) {
     if (e < 0 || e >= E) return;
     const uint32_t old = atomicOr(&sMask[sub][e], bit);
     if (old & bit) flags |= LBT_ST_DUPID;
   };
-  if (tid < len) {
+  if (ti < len) {
 #pragma unroll
-    for (int k = 0; k < kPre; ++k)
-      if (k < K) mark(idp[k]);
-    for (int k = kPre; k < K; ++k) mark(ids[t * K + k]);
+    for (int j = 0; j < kPre; ++j)
+      if (part + j * TPT < K) mark(idp[j]);
+    for (int k = part + kPre * TPT; k < K; k += TPT) mark(ids[t * K + k]);
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kAlignThreads) {
+  for (int e = tid; e < E; e += NT) {
     int run = 0;
 #pragma unroll
     for (int s = 0; s < kSubTiles; ++s) {
@@ -128,11 +141,11 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
     slot[f] = (int)dst;
     sorted_ids[dst] = (int)f;
   };
-  if (tid < len) {
+  if (ti < len) {
 #pragma unroll
-    for (int k = 0; k < kPre; ++k)
-      if (k < K) place(k, idp[k]);
-    for (int k = kPre; k < K; ++k) place(k, ids[t * K + k]);
+    for (int j = 0; j < kPre; ++j)
+      if (part + j * TPT < K) place(part + j * TPT, idp[j]);
+    for (int k = part + kPre * TPT; k < K; k += TPT) place(k, ids[t * K + k]);
   }
   if (flags && status != nullptr) atomicOr(status, flags);
 }
@@ -143,8 +156,8 @@ hipError_t launch_align(const Dims& d, const int32_t* ids, const int32_t* work, 
   const long long nblk = (long long)d.R * d.n_blocks;
   const long long grid = d.n_tiles + (nblk + kBlockWaves - 1) / kBlockWaves;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_align, dim3((unsigned)grid), dim3(kAlignThreads), 0, st, ids, work, plan, d,
-                     slot, sorted_ids, block_wrow, block_expert, status);
+  hipLaunchKernelGGL(k_align<kAlignTPT>, dim3((unsigned)grid), dim3(kAlignThreads), 0, st, ids, work,
+                     plan, d, slot, sorted_ids, block_wrow, block_expert, status);
   return hipGetLastError();
 }
 

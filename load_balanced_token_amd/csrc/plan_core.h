@@ -29,12 +29,17 @@
 namespace lbt {
 
 constexpr int kPlanThreads = 1024;
-// Up to this many deficit ranks the per-expert piece counts come from a
-// register-broadcast count (cost grows with the deficit ranks); above it,
-// from binary searches (cost grows with their logarithm).  Measured on
-// MI355X: 7 deficit ranks 0.96 vs 1.68 us, about 25 3.8 vs 4.7 us, about
-// 49 4.7 vs 3.6 us.
+// The pieces per line position are counted one of three ways, by size:
+// with at most kDirectCompares (deficit rank, position) pairs per lane,
+// both ends of every position by register-broadcast counting; with at most
+// kLinearDeficits deficit ranks, one broadcast count per position serving
+// both ends; else one binary search per position.  Measured on MI355X
+// (that phase alone): DSV3, 7 deficit ranks x 4 positions per lane: 0.96 us
+// (both ends) vs 1.20 (one count) vs 1.68 (two searches); Kimi-K3, about 25
+// x 8: 2.7 (one count) vs 3.8 (both ends) vs 4.7; WideEP, about 49 deficit
+// ranks: 2.7 (one search) vs 3.4 (two searches) vs 4.7 (counting).
 constexpr int kLinearDeficits = 32;
+constexpr int kDirectCompares = 64;
 
 __device__ __forceinline__ int pad_to(int c, int blk) { return ((c + blk - 1) / blk) * blk; }
 
@@ -52,6 +57,7 @@ struct PlanSmem {
   int sCidx[kMaxR + 1];   // compact index among deficit ranks
   int sDl[kMaxR];         // compact index -> rank
   int sDc[kMaxR];         // compact index -> D of that deficit rank (strictly increasing)
+  int sLb[kMaxE + 1];     // deficit starts below O_g (line position g); [E]: below the overflow total
   int sRep[kMaxR + 1];    // replicas per rank, then first piece of rank
   int sPe[kMaxPieces], sPd[kMaxPieces], sPc[kMaxPieces], sPl[kMaxPieces],
       sPj[kMaxPieces];
@@ -63,6 +69,101 @@ struct PlanSmem {
   int sStat[12];
 
 };
+
+// Pieces per line position (sNp) and the compact index of each position's
+// first deficit rank (sDlo), by the one wave that builds the plan.  With
+// c(x) = number of deficit starts at or below x, the overflow [O_g, O_g +
+// o_g) of line position g meets compact deficit ranks c(O_g) - 1 ..
+// c(O_g + o_g - 1) - 1.  Since O_g + o_g = O_{g+1}, the upper end is the
+// number of starts below O_{g+1}, so one count per position serves both
+// ends: c(O_g) counted, then reduced by one where O_g is itself a start.
+// NQ positions per lane (g = lane + i * 64).
+template <int NQ, bool HOT>
+__device__ __forceinline__ void count_pieces(PlanSmem& m, const int E, const int nDef,
+                                             const bool consistent, const int lane) {
+  int x[NQ], ub[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int g = lane + i * kWave;
+    x[i] = g < E ? m.sO[g] : INT_MIN;    // starts are >= 0: empty slots count nothing
+    ub[i] = 0;
+  }
+  const int tot = m.sO[E];               // the overflow total
+  if (nDef * NQ <= kDirectCompares) {
+    // very few: count both ends of every position directly, two compares
+    // per (deficit rank, position) and no second pass
+    const int dcv = lane < nDef ? m.sDc[lane] : 0;
+    int xhi[NQ], chi[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int g = lane + i * kWave;
+      const int o = g < E ? m.sT[HOT ? m.sPerm[g] : g] - m.sH[HOT ? m.sPerm[g] : g] : 0;
+      xhi[i] = g < E ? x[i] + o - 1 : INT_MIN;
+      chi[i] = 0;
+    }
+    for (int c = 0; c < nDef; ++c) {
+      const int dc = __builtin_amdgcn_readlane(dcv, c);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        ub[i] += dc <= x[i];
+        chi[i] += dc <= xhi[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int g = lane + i * kWave;
+      if (g < E) {
+        const bool has = consistent && xhi[i] >= x[i];
+        m.sNp[g] = has ? chi[i] - ub[i] + 1 : 0;
+        if (has) m.sDlo[g] = ub[i] - 1;
+      }
+    }
+    return;
+  }
+  if (nDef <= kLinearDeficits) {
+    // few deficit ranks: lane c holds start c; every lane counts the starts
+    // at or below its positions, one register broadcast per deficit rank
+    const int dcv = lane < nDef ? m.sDc[lane] : 0;
+    int below_tot = 0;
+    for (int c = 0; c < nDef; ++c) {
+      const int dc = __builtin_amdgcn_readlane(dcv, c);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) ub[i] += dc <= x[i];
+      below_tot += dc < tot;
+    }
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int g = lane + i * kWave;
+      const int prev = __shfl(dcv, ub[i] > 0 ? ub[i] - 1 : 0, kWave);
+      if (g < E) m.sLb[g] = ub[i] - (ub[i] > 0 && prev == x[i]);
+    }
+    if (lane == 0) m.sLb[E] = below_tot;
+  } else {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int g = lane + i * kWave;
+      if (g < E) {
+        ub[i] = upper_bound(m.sDc, nDef, x[i]);
+        m.sLb[g] = ub[i] - (ub[i] > 0 && m.sDc[ub[i] - 1] == x[i]);
+      }
+    }
+    if (lane == 0) {
+      const int u = upper_bound(m.sDc, nDef, tot);
+      m.sLb[E] = u - (u > 0 && m.sDc[u - 1] == tot);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int g = lane + i * kWave;
+    if (g < E) {
+      const int e = HOT ? m.sPerm[g] : g;
+      const bool has = consistent && m.sT[e] - m.sH[e] > 0;
+      m.sNp[g] = has ? m.sLb[g + 1] - ub[i] + 1 : 0;
+      if (has) m.sDlo[g] = ub[i] - 1;
+    }
+  }
+}
 
 // The plan from T_e (in m.sT and m.sX, written and made visible by a
 // workgroup barrier before the call; for HOT also m.sLam, m.sPerm and m.sHx
@@ -135,60 +236,9 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
         sDc[sCidx[r]] = sD[r];
       }
     __builtin_amdgcn_wave_barrier();
-    // Pieces of the expert at line position g: its overflow [O, O + o)
-    // meets the deficit ranks from the one holding O to the one holding
-    // O + o - 1.  With c(x) = number of deficit ranks starting at or below
-    // x, those are compact indices c(O) - 1 .. c(O + o - 1) - 1.
     const int nDef = sCidx[R];
-    if (nDef <= kLinearDeficits) {
-      // few deficit ranks: lane c holds start c, and every lane counts the
-      // starts at or below its experts' first and last overflow positions,
-      // one register broadcast per deficit rank (no LDS in the loop)
-      const int dcv = lane < nDef ? sDc[lane] : 0;
-      for (int g0 = 0; g0 < E; g0 += 4 * kWave) {
-        int xlo[4], xhi[4], clo[4], chi[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int g = g0 + lane + i * kWave;
-          const int o = g < E ? sT[perm(g)] - sH[perm(g)] : 0;
-          xlo[i] = g < E ? sO[g] : -1;      // empty slots count nothing
-          xhi[i] = g < E ? xlo[i] + o - 1 : -2;
-          clo[i] = 0;
-          chi[i] = 0;
-        }
-        for (int c = 0; c < nDef; ++c) {
-          const int dc = __builtin_amdgcn_readlane(dcv, c);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            clo[i] += dc <= xlo[i];
-            chi[i] += dc <= xhi[i];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int g = g0 + lane + i * kWave;
-          if (g < E) {
-            const bool has = consistent && xhi[i] >= xlo[i];
-            sNp[g] = has ? chi[i] - clo[i] + 1 : 0;
-            if (has) sDlo[g] = clo[i] - 1;
-          }
-        }
-      }
-    } else {
-      for (int g = lane; g < E; g += kWave) {     // line position g, expert perm(g)
-        const int e = perm(g);
-        const int o = sT[e] - sH[e];
-        int np = 0;
-        if (consistent && o > 0) {
-          const int Oe = sO[g];
-          const int clo = upper_bound(sDc, nDef, Oe);
-          const int chi = upper_bound(sDc, nDef, Oe + o - 1);
-          np = chi - clo + 1;
-          sDlo[g] = clo - 1;
-        }
-        sNp[g] = np;
-      }
-    }
+    if (E <= 4 * kWave) count_pieces<4, HOT>(m, E, nDef, consistent, lane);
+    else count_pieces<kMaxE / kWave, HOT>(m, E, nDef, consistent, lane);
     __builtin_amdgcn_wave_barrier();
     const int nP = wave_excl_scan_lds<kMaxE / kWave>(sNp, E);
     // one lane per replica segment ("piece"), in line order

@@ -313,6 +313,8 @@ def plan_balance(counts, K, S, B, blk, cap=0, tau_max=0):
     p = _place(counts, K, S, B, blk, C, S * K, _split_stream_tail)
     p["rule"] = "fixed"
     p["feasible"] = p["max_replicas"] <= B
+    p["home_local"] = np.zeros(E, dtype=np.int64)    # the fixed rule has no locality step
+    p["local"] = False
     return p
 
 
@@ -361,8 +363,8 @@ def plan_quota(counts, K, S, B, blk, tau_max=0, cap=0):
         exhaustive because the condition is not monotone in tau;
       * if no tau <= tau_max qualifies, the plan at tau_max is used with the
         remote fallback for replicas beyond B ("feasible" False);
-      * locality: each expert's home instance is filled first (it keeps its
-        earliest pairs up to its quota) before any demand leaves the rank.
+      * locality: the instance quotas above are split into pairs from the
+        instance's own rank first (_local_counts); align_sort places them.
     tau_max = 0 means S*K (exact balance).
     """
     counts = np.asarray(counts, dtype=np.int64)
@@ -384,7 +386,27 @@ def plan_quota(counts, K, S, B, blk, tau_max=0, cap=0):
     p["rule"] = "quota"
     p["feasible"] = feasible
     p["tau_max"] = t_max
+    _local_counts(p, counts)
     return p
+
+
+def _local_counts(plan, counts):
+    """Locality of the quota plan ([UltraEP] "その仕組みは...": tokens use the
+    capacity of local expert instances before the rest of the demand goes
+    elsewhere).  Every instance of an expert (its home, then its replicas in
+    line order) first serves the pairs that come from its own rank, up to
+    its quota: home_local[e] = min(h_e, pairs of e from e's home rank), and
+    each replica's "local" = min(count, pairs of e from the replica's rank).
+    Reading: only an instance on the token's own rank counts as local (the
+    pages give no node topology to rank other ranks as nearer)."""
+    counts = np.asarray(counts, dtype=np.int64)
+    R, E = counts.shape
+    nh = E // R
+    e_all = np.arange(E)
+    plan["home_local"] = np.minimum(plan["h"], counts[e_all // nh, e_all])
+    for rp in plan["replicas"]:
+        rp["local"] = int(min(rp["count"], counts[rp["rank"], rp["expert"]]))
+    plan["local"] = True
 
 
 # --------------------------------------------------------------------------- O4
@@ -399,6 +421,8 @@ def align_sort(ids, plan):
       q < h_e  -> home rank of e, row = home start of e + q
       q >= h_e -> o = O_e + (q - h_e); d is the rank with D_d <= o < D_d+def_d;
                   row = start of e's replica segment on d + (o - max(O_e, D_d)).
+    Under a quota plan (plan["local"]) the destinations follow its locality
+    step instead (_place_local).
     slot[f] = d*C + row and sorted_ids[d*C + row] = f.  Readings: padding rows
     below a rank's padded end hold the sentinel P (one past the last pair);
     rows at or past the padded end are left unspecified (UNSPECIFIED here);
@@ -424,10 +448,14 @@ def align_sort(ids, plan):
     for rp in plan["replicas"]:
         rep_start[rp["expert"], rp["rank"]] = rp["row"]
 
-    at_home = q < h[flat]
-    d = np.where(at_home, flat // nh, 0)
-    row = np.where(at_home, plan["home_row"][flat] + q, 0)
-    ov = ~at_home
+    if plan.get("local", False):
+        d, row = _place_local(flat, plan, K)
+        ov = np.zeros(P, dtype=bool)
+    else:
+        at_home = q < h[flat]
+        d = np.where(at_home, flat // nh, 0)
+        row = np.where(at_home, plan["home_row"][flat] + q, 0)
+        ov = ~at_home
     if ov.any():
         e_ov = flat[ov]
         o_pos = O[e_ov] + (q[ov] - h[e_ov])
@@ -459,6 +487,53 @@ def align_sort(ids, plan):
 
 
 # --------------------------------------------------------------------------- O5
+def _place_local(flat, plan, K):
+    """Per-pair (rank, row) of a quota plan with locality ([UltraEP]
+    "その仕組みは...": tokens first use the capacity of local instances, then
+    the remaining demand goes elsewhere; per-token destinations are a lookup
+    against the cumulative quotas).  For expert e, with instances I_0 = home
+    (quota h_e) and I_1.. = its replicas in line order (quota = count):
+      1. each instance takes, up to its quota, the earliest (ascending f)
+         pairs of e whose token comes from the instance's own rank;
+      2. the pairs of e not taken in step 1, in ascending f, fill the
+         instances' remaining quotas in instance order (home first);
+      3. inside an instance's segment its step-1 pairs come first, then its
+         step-2 pairs, each in ascending f.
+    The token of pair f comes from rank (f // K) // S."""
+    E, R, S = plan["E"], plan["R"], plan["S"]
+    nh = E // R
+    P = flat.size
+    src = (np.arange(P) // K) // S
+    d = np.zeros(P, dtype=np.int64)
+    row = np.zeros(P, dtype=np.int64)
+    reps_of = {e: [] for e in range(E)}
+    for rp in plan["replicas"]:                       # line order
+        reps_of[rp["expert"]].append(rp)
+    for e in range(E):
+        fs = np.nonzero(flat == e)[0]                 # ascending f
+        if fs.size == 0:
+            continue
+        inst = [(e // nh, int(plan["h"][e]), int(plan["home_row"][e]))]
+        inst += [(rp["rank"], int(rp["count"]), int(rp["row"])) for rp in reps_of[e]]
+        taken = np.zeros(fs.size, dtype=bool)
+        n_local = []
+        for (rank, quota, row0) in inst:              # step 1
+            mine = np.nonzero((src[fs] == rank) & ~taken)[0][:quota]
+            taken[mine] = True
+            d[fs[mine]] = rank
+            row[fs[mine]] = row0 + np.arange(mine.size)
+            n_local.append(mine.size)
+        rest = np.nonzero(~taken)[0]                  # step 2, ascending f
+        pos = 0
+        for (rank, quota, row0), nl in zip(inst, n_local):
+            sel = rest[pos:pos + quota - nl]
+            d[fs[sel]] = rank
+            row[fs[sel]] = row0 + nl + np.arange(sel.size)
+            pos += quota - nl
+        assert pos == rest.size, "instance quotas must add up to the expert's pairs"
+    return d, row
+
+
 def dispatch_rows(x_bits, slot, K):
     """Zero-copy dispatch: pair f's token row is written straight to its final
     expert-grouped row slot[f] of the static receive buffer ([MoonEP-GR]

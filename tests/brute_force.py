@@ -194,8 +194,9 @@ def quota_conforming_plans(ids, E, R, S, tau):
 
 def quota_threshold(ids, E, R, S, B):
     """Smallest tau >= S*K whose quota-rule assignment puts no more than B
-    replicas (distinct away-from-home experts) on any rank; with its
-    assignment.  Every tau is tried in ascending order."""
+    replicas (distinct away-from-home experts) on any rank; with the
+    assignment after the locality step (local_conforming_assignments, same
+    quotas).  Every tau is tried in ascending order."""
     K = len(ids[0])
     nh = E // R
     T = [0] * E
@@ -207,5 +208,49 @@ def quota_threshold(ids, E, R, S, B):
         assert len(plans) == 1, (tau, len(plans))
         reps = replicas_of(plans[0], ids, E, R)
         if all(len([x for x in reps if x[1] == r]) <= B for r in range(R)):
-            return tau, plans[0]
+            local = local_conforming_assignments(ids, E, R, S, plans[0])
+            assert len(local) == 1, (tau, len(local))
+            return tau, local[0]
     raise AssertionError("tau = max load always qualifies")
+
+
+def local_conforming_assignments(ids, E, R, S, base):
+    """Every map pair -> rank that keeps the instance quotas of `base` (the
+    number of pairs of each expert on each rank) and meets the locality
+    rule stated declaratively:
+      (a) an instance (e, d) holds, of the pairs of e whose token comes from
+          rank d, exactly the earliest min(quota, their number);
+      (b) the pairs of e placed away from their own token's rank, taken by
+          ascending flat index, go to instances in non-decreasing order
+          (home first, then replicas by ascending rank).
+    Returns the assignments found (the rule admits exactly one)."""
+    K = len(ids[0])
+    nh = E // R
+    pairs = pair_list(ids)
+    src = {f: (f // K) // S for (f, _) in pairs}
+    quota = {}
+    for (f, e) in pairs:
+        quota[(e, base[f])] = quota.get((e, base[f]), 0) + 1
+    ranks_of = {e: sorted({d for (x, d) in quota if x == e}, key=lambda d: (d != e // nh, d))
+                for e in range(E)}
+    found = []
+    for asg in itertools.product(*[ranks_of[e] for (_, e) in pairs]):
+        asg = dict(zip([f for (f, _) in pairs], asg))
+        got = {}
+        for (f, e) in pairs:
+            got[(e, asg[f])] = got.get((e, asg[f]), 0) + 1
+        if got != quota:
+            continue
+        ok = True
+        for e in range(E):
+            fs = [f for (f, x) in pairs if x == e]
+            for d in ranks_of[e]:
+                own = [f for f in fs if src[f] == d]
+                if [f for f in own if asg[f] == d] != own[:min(quota[(e, d)], len(own))]:
+                    ok = False
+            order = [ranks_of[e].index(asg[f]) for f in fs if asg[f] != src[f]]
+            if order != sorted(order):
+                ok = False
+        if ok:
+            found.append(tuple(asg[f] for (f, _) in pairs))
+    return found

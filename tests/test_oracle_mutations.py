@@ -48,6 +48,15 @@ MUTATIONS = {
     "quota_slot_bound_strict": ("_split_hot_first).max() <= B:", "_split_hot_first).max() < B:"),
     "quota_fallback_at_SK": ("tau, feasible = t_max, False", "tau, feasible = SK, False"),
     "quota_deficit_from_SK": ("    deficit = tau - keep\n", "    deficit = S * K - np.minimum(L, S * K)\n"),
+    # locality of the quota plan
+    "locality_off": ('    if plan.get("local", False):\n        d, row = _place_local', '    if False:\n        d, row = _place_local'),
+    "locality_takes_latest": ("mine = np.nonzero((src[fs] == rank) & ~taken)[0][:quota]",
+                              "mine = np.nonzero((src[fs] == rank) & ~taken)[0][::-1][:quota][::-1]"),
+    "locality_rest_replicas_first": ("for (rank, quota, row0), nl in zip(inst, n_local):",
+                                     "for (rank, quota, row0), nl in list(zip(inst, n_local))[::-1]:"),
+    "locality_rest_before_local": ("row[fs[sel]] = row0 + nl + np.arange(sel.size)",
+                                   "row[fs[sel]] = row0 + np.arange(sel.size); row[fs[taken & (src[fs] == rank)]] += sel.size"),
+    "locality_home_count_from_rank0": ("counts[e_all // nh, e_all])", "counts[0, e_all])"),
 }
 
 
@@ -105,7 +114,7 @@ def _pins(o):
                 plan = o.plan_quota(counts, K, S, c["B"], blk, c["tau_max"])
                 al = o.align_sort(ids, plan)
                 ok = (plan["tau"] == c["tau"] and plan["feasible"] == c["feasible"]
-                      and all(plan[k].tolist() == c[k] for k in ("h", "O", "D", "deficit"))
+                      and all(plan[k].tolist() == c[k] for k in ("h", "O", "D", "deficit", "home_local"))
                       and plan["segments"] == c["segments"] and plan["replicas"] == c["replicas"]
                       and al["slot"].tolist() == c["slot"])
             except Exception:

@@ -99,11 +99,27 @@ def check_invariants(ids, plan, al):
     slot = al["slot"]
     assert len(set(slot.tolist())) == P
     assert (al["sorted_ids"][slot] == np.arange(P)).all()
+    local_count = {}
+    if plan.get("local", False):
+        local_count = {(rp["expert"], rp["rank"]): rp["local"] for rp in plan["replicas"]}
+        for e in range(E):
+            local_count[(e, e // (E // R))] = int(plan["home_local"][e])
     for r in range(R):
         for sg in plan["segments"][r]:
             assert sg["start"] % blk == 0
             rows = al["sorted_ids"][r * C + sg["start"]: r * C + sg["start"] + sg["count"]]
-            assert (np.diff(rows) > 0).all()                     # ascending f inside
+            if plan.get("local", False):
+                # locality: the pairs whose token comes from this rank first,
+                # then the others, each run ascending in f
+                nl = local_count[(sg["expert"], r)]
+                # as many as the instance can take of its own rank's pairs
+                own = int(((flat == sg["expert"]) & ((np.arange(P) // K) // plan["S"] == r)).sum())
+                assert nl == min(sg["count"], own)
+                src = (rows // plan["K"]) // plan["S"]
+                assert (src[:nl] == r).all() and (src[nl:] != r).all()
+                assert (np.diff(rows[:nl]) > 0).all() and (np.diff(rows[nl:]) > 0).all()
+            else:
+                assert (np.diff(rows) > 0).all()                 # ascending f inside
             assert (flat[rows] == sg["expert"]).all()            # right expert
             plen = -(-sg["count"] // blk) * blk
             pad = al["sorted_ids"][r * C + sg["start"] + sg["count"]: r * C + sg["start"] + plen]

@@ -44,7 +44,7 @@ def test_hand_examples(path):
         assert counts.tolist() == g["counts"]
         assert plan["tau"] == c["tau"] and plan["feasible"] == c["feasible"]
         for key in ("T", "L", "deficit", "h", "o", "O", "D", "n_rows_padded", "n_slots",
-                    "n_remote", "home_row"):
+                    "n_remote", "home_row", "home_local"):
             assert plan[key].tolist() == c[key], key
         assert plan["C"] == c["C"]
         assert plan["replicas"] == c["replicas"]
@@ -83,7 +83,8 @@ def test_brute_force_threshold_and_assignment(B):
 
 
 def test_brute_force_every_threshold_below():
-    """At every tau the declarative rule admits one assignment, the oracle's."""
+    """At every tau the declarative rule admits one assignment, the oracle's,
+    before and after the locality step."""
     for ids, E, R, S, K in _small_cases()[:8]:
         counts = oracle.load_matrix(ids, R, S, E)
         maxL = int(oracle.imbalance(counts, S, K)["L"].max())
@@ -94,6 +95,12 @@ def test_brute_force_every_threshold_below():
             plans = bf.quota_conforming_plans(ids.tolist(), E, R, S, tau)
             assert len(plans) == 1
             assert tuple(int(s) // plan["C"] for s in al["slot"]) == plans[0]
+            # the locality step on the same quotas
+            oracle_path._local_counts(plan, counts)
+            al = oracle.align_sort(ids, plan)
+            local = bf.local_conforming_assignments(ids.tolist(), E, R, S, plans[0])
+            assert len(local) == 1
+            assert tuple(int(s) // plan["C"] for s in al["slot"]) == local[0]
 
 
 def test_no_slots_means_nothing_moves():
@@ -139,7 +146,9 @@ def test_one_expert_per_rank_reduces_to_fixed_rule(seed):
     assert a["tau"] == S * K
     for key in ("h", "o", "O", "D", "n_rows_padded", "n_slots", "n_remote", "home_row"):
         assert a[key].tolist() == b[key].tolist(), key
-    assert a["replicas"] == b["replicas"] and a["segments"] == b["segments"]
+    # the same instances; only the quota plan adds its locality counts
+    assert [{k: v for k, v in rp.items() if k != "local"} for rp in a["replicas"]] == b["replicas"]
+    assert a["segments"] == b["segments"]
 
 
 def check_quota_invariants(ids, plan, al, B):

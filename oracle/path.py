@@ -22,8 +22,9 @@ function.  Floating point is fp64 except where the method itself fixes fp32
 (the top-K key is an fp32 value; bf16 rows widen exactly to fp32).
 
 Parity pins (see tests/test_oracle_*.py): brute-force top-K, closed-form gates,
-numpy bincount, hand-derived plans W1-W3 (fixed rule) and Q1-Q4 (quota rule),
-brute-force enumeration of rule-conforming plans under both rules, the
+numpy bincount, hand-derived plans W1-W3 (fixed rule) and Q1-Q4 (quota rule,
+with its locality step), brute-force enumeration of rule-conforming plans
+under both rules and of the locality rule stated declaratively, the
 balanced-routing special case (textbook stable counting sort), the
 one-expert-per-rank reduction of the quota rule to the fixed rule, invariants,
 the identity-expert closed form for combine; for the training side the

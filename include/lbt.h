@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LBT_VERSION 2
+#define LBT_VERSION 3
 
 /* return codes */
 #define LBT_OK 0
@@ -121,6 +121,10 @@ typedef struct lbt_sizes {
   int64_t off_piece_line;   /*   start on the shared overflow/deficit line */
   int64_t off_piece_row;    /*   padded start row on rank d */
   int64_t off_piece_wrow;   /*   weight row: E + j for prefetch slot j, else the expert (remote) */
+  int64_t off_home_local;   /* [E] of e's home quota h_e, the pairs whose token comes from e's
+                               home rank (quota plans; 0 under lbt_plan_balance) */
+  int64_t off_piece_local;  /* [max_pieces] of each replica segment's count, the pairs whose
+                               token comes from its rank d (quota plans; 0 otherwise) */
 } lbt_sizes;
 
 /* plan header words */
@@ -136,6 +140,7 @@ typedef struct lbt_sizes {
 #define LBT_HDR_TAU 9         /* per-rank load threshold the plan used (S*K for plan_balance) */
 #define LBT_HDR_MAX_REPLICAS 10 /* most replica segments on one rank */
 #define LBT_HDR_FEASIBLE 11   /* 1 when no rank holds more than B replicas (no remote reads) */
+#define LBT_HDR_LOCAL 12      /* 1: align places pairs with the locality step (lbt_plan_quota) */
 #define LBT_HDR_WORDS 16
 
 /* Fill *out for shape *s.  Pure host function.  LBT_EINVAL/LBT_EUNSUPPORTED
@@ -192,15 +197,19 @@ int lbt_plan_balance(const lbt_shape* s, const int32_t* counts, int32_t* plan, i
  * which hot experts get copies, where, and how many tokens each instance
  * takes; replicas only where there is work; fully on the GPU).  Rule at
  * threshold tau: an overloaded rank keeps tau pairs and sheds the rest from
- * its hottest experts first (load descending, ties to the lower index), each
- * expert keeping its earliest pairs; the overflow line lists experts rank by
+ * its hottest experts first (load descending, ties to the lower index); the
+ * overflow line lists experts rank by
  * rank in that order; deficit ranks (def_r = tau - min(L_r, tau)) fill in
  * ascending order, one replica segment per overlap.  tau is the smallest
  * integer in [S*K, min(max_r L_r, tau_max)] for which no rank holds more than
  * B replica segments (candidates checked in ascending batches of 1024 in
  * parallel, stopping at the first batch holding one); when none qualifies,
  * tau = tau_max and replicas beyond B are remote (LBT_HDR_FEASIBLE = 0).
- * Every rank then holds at most tau pairs.  One workgroup, one launch.
+ * Every rank then holds at most tau pairs.  Locality (same section: tokens
+ * use local instances' capacity before the rest of the demand goes
+ * elsewhere): the blob sets LBT_HDR_LOCAL and records, per instance, how
+ * many of its quota come from its own rank (home_local, piece_local), and
+ * lbt_align_sort places pairs accordingly.  One workgroup, one launch.
  *   counts [R, E] int32 in
  *   plan   [plan_words] int32 out (LBT_HDR_TAU holds the threshold)
  *   status int32 out (may be NULL) */
@@ -213,7 +222,12 @@ int lbt_plan_quota(const lbt_shape* s, const int32_t* counts, int32_t* plan, int
  * destinations by lookup against cumulative quotas).  For pair f with
  * expert e and q = #{f' < f : ids[f'] = e}: q < h_e -> home rank of e, row
  * home_row[e] + q; else o = O_e + q - h_e lies in one replica segment
- * (d, line, row) -> rank d, row + o - line.
+ * (d, line, row) -> rank d, row + o - line.  With LBT_HDR_LOCAL set (quota
+ * plans) the instances of e -- its home, then its replica segments in line
+ * order -- first take, up to their quota, the earliest pairs of e whose
+ * token comes from their own rank; the other pairs, by ascending f, fill the
+ * remaining quotas in instance order; a segment lists its local pairs
+ * first, then the others, each by ascending f.
  *   ids        [N, K] int32 in (the ids the histogram counted)
  *   work       the workspace filled by lbt_route_topk / lbt_histogram
  *   plan       the blob from lbt_plan_balance or lbt_plan_quota

@@ -35,6 +35,7 @@ HDR_P = 8
 HDR_TAU = 9
 HDR_MAX_REPLICAS = 10
 HDR_FEASIBLE = 11
+HDR_LOCAL = 12
 
 EXPORTS = ("lbt_query_sizes", "lbt_route_topk", "lbt_histogram", "lbt_plan_balance",
            "lbt_plan_quota", "lbt_align_sort", "lbt_dispatch", "lbt_combine",
@@ -54,7 +55,7 @@ _SIZE_FIELDS = (
     "off_n_seg", "off_n_rows_padded", "off_n_slots", "off_n_remote",
     "off_seg_expert", "off_seg_wrow", "off_seg_count", "off_seg_start",
     "off_piece_expert", "off_piece_rank", "off_piece_count", "off_piece_line", "off_piece_row",
-    "off_piece_wrow",
+    "off_piece_wrow", "off_home_local", "off_piece_local",
 )
 
 
@@ -419,4 +420,5 @@ def plan_fields(plan_words, sizes: dict, R: int, E: int) -> dict:
         "piece_expert": at("off_piece_expert", mp), "piece_rank": at("off_piece_rank", mp),
         "piece_count": at("off_piece_count", mp), "piece_line": at("off_piece_line", mp),
         "piece_row": at("off_piece_row", mp), "piece_wrow": at("off_piece_wrow", mp),
+        "home_local": at("off_home_local", E), "piece_local": at("off_piece_local", mp),
     }

@@ -66,6 +66,8 @@ int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z) {
   pl.piece_line = take(mp);
   pl.piece_row = take(mp);
   pl.piece_wrow = take(mp);
+  pl.home_local = take(E);
+  pl.piece_local = take(mp);
   pl.total = (int)off;
 
   if (d != nullptr) {
@@ -90,6 +92,8 @@ int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z) {
     z->off_piece_count = pl.piece_count; z->off_piece_line = pl.piece_line;
     z->off_piece_row = pl.piece_row;
     z->off_piece_wrow = pl.piece_wrow;
+    z->off_home_local = pl.home_local;
+    z->off_piece_local = pl.piece_local;
   }
   return LBT_OK;
 }

@@ -24,6 +24,7 @@ struct PlanLayout {
   int hdr, T, h, O, home_row, L, def, D, n_seg, n_rows_padded, n_slots, n_remote;
   int seg_expert, seg_wrow, seg_count, seg_start;
   int piece_expert, piece_rank, piece_count, piece_line, piece_row, piece_wrow;
+  int home_local, piece_local;
   int total;
 };
 

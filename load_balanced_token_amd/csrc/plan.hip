@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict
   if (threadIdx.x < 12) m.sStat[threadIdx.x] = 0;
   column_sums<kPlanThreads>(counts, d.E, d.R, m.sT, m.sX);
   __syncthreads();
-  plan_core<false>(d, m, d.SK, plan, status);
+  plan_core<false>(d, m, d.SK, counts, plan, status);
 }
 
 // ---- quota plan ---------------------------------------------------------------
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_quota(const int32_t* __re
     if (found != INT_MAX) break;
   }
   const int tau = m.sStat[10] == INT_MAX ? d.tau_max : m.sStat[10];
-  plan_core<true>(d, m, tau, plan, status);
+  plan_core<true>(d, m, tau, counts, plan, status);
 }
 
 hipError_t launch_plan(const Dims& d, const int32_t* counts, int32_t* plan, int32_t* status,

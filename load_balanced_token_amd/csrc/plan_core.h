@@ -171,6 +171,7 @@ __device__ __forceinline__ void count_pieces(PlanSmem& m, const int E, const int
 // threads; writes the whole blob and *status.
 template <bool HOT>
 __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int tau,
+                                          const int32_t* __restrict__ counts,
                                           int32_t* __restrict__ plan,
                                           int32_t* __restrict__ status) {
   auto& sT = m.sT; auto& sX = m.sX; auto& sH = m.sH; auto& sO = m.sO; auto& sNp = m.sNp;
@@ -305,6 +306,8 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
     const int fb = r * nh + sRep[r];
     P[pl.T + e] = sT[e];
     P[pl.h + e] = sH[e];
+    // quota rule: the part of the home quota its own rank's tokens take
+    P[pl.home_local + e] = HOT ? min(sH[e], counts[(long long)r * E + e]) : 0;
     P[pl.O + e] = sO[lam(e)];
     P[pl.home_row + e] = sF[fb + (e - r * nh)] - sF[fb];
   }
@@ -354,7 +357,7 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
       P[pl.seg_start + row1 + s] = (s < nseg ? sF[fb + s] : sF[fb + nseg]) - f0;
   }
   for (int g = tid; g < pl.max_pieces; g += kPlanThreads) {
-    int ex = -1, dd = -1, cnt = 0, line = -1, row = -1, wrow = -1;
+    int ex = -1, dd = -1, cnt = 0, line = -1, row = -1, wrow = -1, loc = 0;
     if (g < nP) {
       ex = sPe[g];
       dd = sPd[g];
@@ -363,7 +366,9 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
       const int fb = dd * nh + sRep[dd];
       row = sF[fb + nh + sPj[g]] - sF[fb];
       wrow = sPj[g] < B ? E + sPj[g] : ex;
+      if (HOT) loc = min(cnt, counts[(long long)dd * E + ex]);   // its own rank's tokens
     }
+    P[pl.piece_local + g] = loc;
     P[pl.piece_wrow + g] = wrow;
     P[pl.piece_expert + g] = ex;
     P[pl.piece_rank + g] = dd;
@@ -386,7 +391,8 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
     P[pl.hdr + LBT_HDR_TAU] = sStat[8];
     P[pl.hdr + LBT_HDR_MAX_REPLICAS] = sStat[9];
     P[pl.hdr + LBT_HDR_FEASIBLE] = sStat[9] <= B ? 1 : 0;
-    for (int i = LBT_HDR_FEASIBLE + 1; i < LBT_HDR_WORDS; ++i) P[pl.hdr + i] = 0;
+    P[pl.hdr + LBT_HDR_LOCAL] = HOT ? 1 : 0;
+    for (int i = LBT_HDR_LOCAL + 1; i < LBT_HDR_WORDS; ++i) P[pl.hdr + i] = 0;
     if (status != nullptr) *status = st;
   }
 }

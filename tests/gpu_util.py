@@ -8,7 +8,7 @@ from load_balanced_token_amd.binding import (HDR_N_PIECES, HDR_MAX_T, HDR_MAX_L,
                                              HDR_TOTAL_OVERFLOW, HDR_N_DEFICIT_RANKS,
                                              HDR_N_OVERFLOW_RANKS, HDR_N_OVERFLOW_EXPERTS,
                                              HDR_STATUS, HDR_P, HDR_TAU, HDR_MAX_REPLICAS,
-                                             HDR_FEASIBLE)
+                                             HDR_FEASIBLE, HDR_LOCAL)
 
 GATE_RTOL = 1e-6       # gates vs the fp64 oracle (relative)
 COMBINE_RTOL = 1e-6    # |y - y_ref| <= 1e-6 * sum_k |g * out|
@@ -127,6 +127,11 @@ def check_plan(pf, op, P):
     assert hdr[HDR_TAU] == op["tau"]
     assert hdr[HDR_MAX_REPLICAS] == op["max_replicas"]
     assert hdr[HDR_FEASIBLE] == int(op["max_replicas"] <= op["B"])
+    # locality counts (quota plans; zero under the fixed rule)
+    assert hdr[HDR_LOCAL] == int(op.get("local", False))
+    assert np.array_equal(pf["home_local"], op["home_local"]), "home_local differs"
+    assert pf["piece_local"][:nP].tolist() == [rp.get("local", 0) for rp in reps], "piece_local"
+    assert (pf["piece_local"][nP:] == 0).all()
 
 
 def check_align(g, o, R, C):

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(binding.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.lbt_version() == 2
+    assert L.lbt_version() == 3
 
 
 def test_sizes_match_oracle_capacity_for_every_workload():

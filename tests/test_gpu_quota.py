@@ -123,7 +123,16 @@ def test_quota_degenerate_shapes():
     logits = router_logits(w, 0)
     q = gu.run_front(gu.shape_of(w), logits, planner="quota")
     f = gu.run_front(gu.shape_of(w), logits, planner="fixed")
-    assert np.array_equal(q["plan"], f["plan"])
+    # the same plan; only the quota plan carries the locality words
+    z = q["sizes"]
+    skip = np.zeros(q["plan"].size, bool)
+    skip[z["off_hdr"] + gu.HDR_LOCAL] = True
+    skip[z["off_home_local"]: z["off_home_local"] + w.E] = True
+    skip[z["off_piece_local"]: z["off_piece_local"] + z["max_pieces"]] = True
+    assert np.array_equal(q["plan"][~skip], f["plan"][~skip])
+    ref = gu.run_oracle(w, logits, planner="quota")
+    gu.check_plan(q["plan_fields"], ref["plan"], w.P)
+    gu.check_align(q, ref, w.R, q["sizes"]["C"])
     # B = 0 with room: tau = max load, nothing moves
     w, res, ref = _quota_pair(base, 0, 8 * base.SK)
     assert ref["plan"]["tau"] == ref["plan"]["L"].max() and ref["plan"]["replicas"] == []

@@ -228,10 +228,12 @@ def decode_latency(path, buf, w, x, n_steps, dev, planner="fixed"):
             "note": "graph replay incl. the gather of fresh router logits"}
 
 
-def planner_report(lbt, torch, w, counts, B, tau_max, dev):
+def planner_report(lbt, torch, w, counts, B, tau_max, dev, ids=None, work=None):
     """Both planners on the same load matrix: latency (median of 20 back-to-back
     calls; the quota planner is its search launch plus its plan launch), the
-    threshold, replica segments, the most on one rank, remote replicas."""
+    threshold, replica segments, the most on one rank, remote replicas, and
+    (given the step's ids and workspace) how many pairs each plan serves on
+    their own token's rank -- the pairs a multi-GPU run would not send."""
     import numpy as np
     stream = torch.cuda.current_stream()
     out = {}
@@ -257,6 +259,20 @@ def planner_report(lbt, torch, w, counts, B, tau_max, dev):
                      "replica_segments": int(hdr[0]), "max_replicas_per_rank": int(hdr[10]),
                      "remote_replicas": int(pf["n_remote"].sum()), "feasible": bool(hdr[11]),
                      "search_candidates": (tau_max or w.SK) - w.SK + 1 if name == "quota" else 0}
+        if ids is not None and work is not None:
+            z = p.sizes
+            i32 = dict(dtype=torch.int32, device=dev)
+            slot = torch.empty(w.P, **i32)
+            sorted_ids = torch.empty(w.R * z["C"], **i32)
+            bw = torch.empty(w.R * z["n_blocks"], **i32)
+            be = torch.empty_like(bw)
+            st = torch.zeros(1, **i32)
+            p.align_sort(ids, work, plan, slot, sorted_ids, bw, be, st)
+            f = torch.arange(w.P, dtype=torch.int64, device=dev)
+            own = int(((slot.long() // z["C"]) == (f // w.K) // w.S).sum().item())
+            out[name]["own_rank_pairs"] = own
+            out[name]["own_rank_fraction"] = own / max(1, w.P)
+            out[name]["align_status"] = int(st.item())
     out["B"] = B
     out["tau_max"] = tau_max or w.SK
     return out
@@ -482,7 +498,8 @@ def main():
 
     status = int(buf["status"].item())
     hdr = buf["plan"][:16].cpu().numpy()
-    planners = planner_report(lbt, torch, w, buf["counts"], w.B, tau_max, dev)
+    planners = planner_report(lbt, torch, w, buf["counts"], w.B, tau_max, dev,
+                              ids=buf["ids"], work=buf["work"])
     training = None
     if not args.no_train:
         print("[bench] training-side kernels", file=sys.stderr, flush=True)

@@ -7,7 +7,12 @@
 // scatters; here the offsets come from the plan and the per-tile prefix
 // counts, so every tile of 128 tokens works independently.
 // [UltraEP] section "その仕組みは高速なエキスパート複製に依存する": per-token
-// destinations are a local lookup against cumulative quotas.
+// destinations are a local lookup against cumulative quotas, and under a
+// quota plan tokens first use the capacity of their own rank's instance of
+// their expert (the locality step): pair rank among its rank's pairs of e
+// below that instance's local count -> that instance; otherwise its rank
+// among the pairs left after the local step picks the home's or a piece's
+// share of the rest.
 //
 // Stable rank of a pair inside its expert: q = (pairs of e in earlier tiles,
 // from the column scan) + (pairs of e in earlier 32-token sub-tiles of this

@@ -82,6 +82,17 @@ def test_quota_plan_parity(name, B, x):
     assert load.max() <= ref["plan"]["tau"]
 
 
+@pytest.mark.parametrize("B,x", [(2, 2), (1, 1)])
+def test_quota_ragged_tiles(B, x):
+    """Several tiles per rank with a ragged last one (S = 300): the locality
+    step's per-rank pair offsets come from rank r's first tile."""
+    w = WORKLOADS["dsv3"].with_(S=300, H=64)
+    w, res, ref = _quota_pair(w, B, x * w.SK)
+    gu.check_plan(res["plan_fields"], ref["plan"], w.P)
+    gu.check_align(res, ref, w.R, res["sizes"]["C"])
+    _full_move_check(w, res, ref, activations(w, 0))
+
+
 def test_quota_plan_parity_more_layers():
     w = WORKLOADS["decode128"]
     for layer in (1, 2, 3):

@@ -45,29 +45,35 @@ __global__ __launch_bounds__(kTileTokens) void k_histogram(const int32_t* __rest
 }
 
 // One wave per expert column: exclusive prefix over tiles (written
-// tile-major for the align step) and per-source-rank sums (the load matrix).
+// tile-major for the align step) and per-source-rank sums (the load
+// matrix), the latter as differences of the prefix at the ranks' first
+// tiles (tiles never cross ranks).
 __global__ __launch_bounds__(256) void k_tile_scan(Dims d, int32_t* __restrict__ work,
                                                    int32_t* __restrict__ counts) {
-  const int e = blockIdx.x * 4 + wave_id();
+  __shared__ int sPre[4][kMaxR + 1];   // per wave: prefix at each rank's first tile, then the total
+  const int w = wave_id();
+  const int e = blockIdx.x * 4 + w;
   if (e >= d.E) return;
   const int lane = lane_id();
-  const int nt = d.n_tiles;
+  const int nt = d.n_tiles, tpr = d.tpr;
   const int32_t* col = work + (long long)e * nt;
   int32_t* base = work + work_tile_base(d);
   const int per = (nt + kWave - 1) / kWave;
   const int lo = min(nt, lane * per), hi = min(nt, lo + per);
   int local = 0;
   for (int t = lo; t < hi; ++t) local += col[t];
-  int run = wave_incl_scan(local) - local;
+  const int incl = wave_incl_scan(local);
+  int run = incl - local;
+  for (int r = lane; r <= d.R; r += kWave) sPre[w][r] = 0;   // ranks without tiles (S = 0) sum to 0
   for (int t = lo; t < hi; ++t) {
+    if (t % tpr == 0) sPre[w][t / tpr] = run;
     base[(long long)t * d.E + e] = run;
     run += col[t];
   }
-  for (int r = lane; r < d.R; r += kWave) {
-    int s = 0;
-    for (int t = r * d.tpr; t < (r + 1) * d.tpr; ++t) s += col[t];
-    counts[(long long)r * d.E + e] = s;
-  }
+  if (lane == 0) sPre[w][d.R] = __builtin_amdgcn_readlane(incl, kWave - 1);
+  __builtin_amdgcn_wave_barrier();
+  for (int r = lane; r < d.R; r += kWave)
+    counts[(long long)r * d.E + e] = sPre[w][r + 1] - sPre[w][r];
 }
 
 hipError_t launch_route(const Dims& d, const float* logits, const float* bias, int32_t* ids,

@@ -225,7 +225,8 @@ __global__ __launch_bounds__(kTileTokens * TPT) void k_align(
       dd = ok ? sPd[g] : 0;
       row = ok ? sPr[g] + (o - sPl[g]) : 0;
     }
-    if (!ok || row >= C) {
+    // a row past the capacity, or a rank / row a corrupt plan would give
+    if (!ok || row >= C || row < 0 || dd < 0 || dd >= d.R) {
       flags |= LBT_ST_CAPACITY;
       slot[f] = -1;
       return;

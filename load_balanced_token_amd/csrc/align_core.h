@@ -18,7 +18,7 @@ __device__ __forceinline__ void align_blocks(const int32_t* __restrict__ plan, c
   const int b = (int)(gb - (long long)r * d.n_blocks);
   const int lane = lane_id();
   const int nrp = plan[pl.n_rows_padded + r];
-  const int ns = plan[pl.n_seg + r];
+  const int ns = min(max(plan[pl.n_seg + r], 1), pl.max_seg);   // clamped against a corrupt blob
   const int row0 = b * d.blk;
   if (row0 >= nrp) {
     if (lane == 0) {
@@ -35,7 +35,7 @@ __device__ __forceinline__ void align_blocks(const int32_t* __restrict__ plan, c
     const int i = i0 + lane;
     nle += __popcll(__ballot(i < ns && starts[i] <= row0));
   }
-  const int s = nle - 1;
+  const int s = max(nle - 1, 0);
   const long long si = (long long)r * pl.max_seg + s;
   if (lane == 0) {
     block_wrow[gb] = plan[pl.seg_wrow + si];

@@ -528,3 +528,32 @@ def test_maximum_sizes(case, planner):
     gu.check_plan(res["plan_fields"], ref["plan"], w.P)
     gu.check_align(res, ref, w.R, res["sizes"]["C"])
     _full_move_check(w, res, ref, activations(w, 0))
+
+
+@pytest.mark.parametrize("planner", ["fixed", "quota"])
+def test_corrupt_plan_is_flagged_not_followed(planner):
+    """A plan blob whose replica segments name a rank past R and rows past C
+    (as a caller's corrupted buffer might): align raises LBT_ST_CAPACITY and
+    gives those pairs slot -1; every other slot stays in range."""
+    t = gu.torch()
+    from load_balanced_token_amd.binding import ST_CAPACITY
+    w = TINY.with_(S=32, B=1)
+    logits = router_logits(w, 0)
+    res = gu.run_front(gu.shape_of(w), logits, planner=planner)
+    assert res["plan_fields"]["hdr"][gu.HDR_N_PIECES] > 0
+    path, z = res["path"], res["sizes"]
+    plan = res["dev"]["plan"].clone()
+    nP = int(res["plan_fields"]["hdr"][gu.HDR_N_PIECES])
+    plan[z["off_piece_rank"]: z["off_piece_rank"] + nP] = w.R + 3
+    plan[z["off_piece_row"]: z["off_piece_row"] + nP] = z["C"] + 100
+    slot = t.empty(w.P, dtype=t.int32, device="cuda")
+    sid = t.empty(w.R * z["C"], dtype=t.int32, device="cuda")
+    bw = t.empty(w.R * z["n_blocks"], dtype=t.int32, device="cuda")
+    be = t.empty_like(bw)
+    st = t.zeros(1, dtype=t.int32, device="cuda")
+    path.align_sort(res["dev"]["ids"], res["dev"]["work"], plan, slot, sid, bw, be, st)
+    t.cuda.synchronize()
+    s = slot.cpu().numpy()
+    assert int(st.item()) & ST_CAPACITY
+    assert ((s == -1) | ((s >= 0) & (s < w.R * z["C"]))).all()
+    assert (s == -1).any()

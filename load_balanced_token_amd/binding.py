@@ -23,6 +23,8 @@ ST_CAPACITY = 2
 ST_BADID = 4
 ST_DUPID = 8
 
+ABI_VERSION = 3          # LBT_VERSION of include/lbt.h this binding's structs follow
+
 HDR_N_PIECES = 0
 HDR_MAX_T = 1
 HDR_MAX_L = 2
@@ -99,6 +101,9 @@ def lib() -> ctypes.CDLL:
         for n in EXPORTS:
             if n != "lbt_strerror":
                 getattr(L, n).restype = I
+        if L.lbt_version() != ABI_VERSION:
+            raise LbtError(f"{LIB_PATH} is ABI version {L.lbt_version()}, this binding expects "
+                           f"{ABI_VERSION} (the lbt_sizes layout differs): rebuild it")
         _lib = L
     return _lib
 

@@ -112,3 +112,21 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_binding_structs_follow_the_header():
+    """The binding's ABI version, lbt_sizes field order and header word
+    indices are those include/lbt.h declares (the ctypes structs would
+    misread the library otherwise)."""
+    from load_balanced_token_amd import binding as b
+    h = open(HEADER).read()
+    assert int(re.search(r"#define LBT_VERSION (\d+)", h).group(1)) == b.ABI_VERSION
+    body = h[h.index("typedef struct lbt_sizes {"):h.index("} lbt_sizes;")]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = []
+    for decl in re.findall(r"int64_t\s+([^;]+);", body):
+        fields += [f.strip() for f in decl.split(",")]
+    assert tuple(fields) == b._SIZE_FIELDS
+    for name, val in re.findall(r"#define LBT_HDR_(\w+) (\d+)", h):
+        if name != "WORDS":
+            assert getattr(b, "HDR_" + name) == int(val), name

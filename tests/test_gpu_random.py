@@ -58,3 +58,43 @@ def test_random_shapes(seed):
     gu.check_plan(res["plan_fields"], ref["plan"], w.P)
     gu.check_align(res, ref, w.R, res["sizes"]["C"])
     _full_move_check(w, res, ref, activations(w, 0))
+
+
+@pytest.mark.parametrize("seed", range(0, N_CASES, 4))
+def test_random_shapes_training(seed):
+    """The training-side kernels on the same random shapes: prefetch and
+    reduce_grad bit-exact, the combine and dispatch gradients within their
+    tolerances."""
+    import oracle
+    from tests.test_gpu_train import _check_combine_bwd, DX_RTOL
+    from workloads import random_expert_out
+    t = gu.torch()
+    w, logits, sb, renorm, planner, tau_max = random_case(seed)
+    res = gu.run_front(gu.shape_of(w, renorm=renorm, tau_max=tau_max), logits, sel_bias=sb,
+                       planner=planner)
+    ref = gu.run_oracle(w, logits, sel_bias=sb, renorm=bool(renorm), planner=planner,
+                        tau_max=tau_max)
+    rng = np.random.default_rng(seed)
+    path, C = res["path"], res["sizes"]["C"]
+    if w.B > 0:
+        row_bytes = 16 * int(rng.integers(1, 300))
+        W = rng.integers(0, 256, size=(w.E, row_bytes), dtype=np.uint8)
+        slots0 = np.full((w.R, w.B, row_bytes), 0x3C, np.uint8)
+        Sd = t.from_numpy(slots0).cuda()
+        path.prefetch_weights(res["dev"]["plan"], t.from_numpy(W).cuda(), Sd)
+        row = 4 * int(rng.integers(1, 300))
+        G = rng.standard_normal((w.E, row)).astype(np.float32)
+        SG = rng.standard_normal((w.R, w.B, row)).astype(np.float32)
+        Gd, SGd = t.from_numpy(G).cuda(), t.from_numpy(SG).cuda()
+        path.reduce_grad(res["dev"]["plan"], SGd, Gd)
+        t.cuda.synchronize()
+        assert np.array_equal(Sd.cpu().numpy(), oracle.prefetch_weights(ref["plan"], W, slots0))
+        g2, sg2 = oracle.reduce_grad(ref["plan"], SG, G)
+        assert np.array_equal(Gd.cpu().numpy(), g2) and np.array_equal(SGd.cpu().numpy(), sg2)
+    _check_combine_bwd(w, res, ref, bool(seed % 8 == 4))
+    d_recv = random_expert_out(w, w.R * C, seed=seed)
+    dx = t.empty((w.N, w.H), dtype=t.float32, device="cuda")
+    path.dispatch_bwd(gu.h2d(d_recv), res["dev"]["slot"], dx)
+    t.cuda.synchronize()
+    want, mag = oracle.dispatch_bwd(lambda r: d_recv[r], ref["align"]["slot"], w.K, w.N)
+    assert (np.abs(dx.cpu().numpy().astype(np.float64) - want) <= DX_RTOL * mag + 1e-30).all()

@@ -130,9 +130,7 @@ int lbt_route_topk(const lbt_shape* s, const float* logits, const float* sel_bia
   if (rc) return rc;
   if (counts == nullptr || (d.N > 0 && (!logits || !ids || !gates || !work))) return LBT_EINVAL;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_route(d, logits, sel_bias, ids, gates, work, st);
-  if (e == hipSuccess) e = launch_tile_scan(d, work, counts, st);
-  return hip_rc(e);
+  return hip_rc(launch_route_and_scan(d, logits, sel_bias, ids, gates, work, counts, st));
 }
 
 int lbt_histogram(const lbt_shape* s, const int32_t* ids, int32_t* counts, int32_t* work,

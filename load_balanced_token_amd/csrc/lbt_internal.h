@@ -52,6 +52,9 @@ hipError_t launch_route(const Dims& d, const float* logits, const float* bias, i
 hipError_t launch_histogram(const Dims& d, const int32_t* ids, int32_t* work, int32_t* status,
                             hipStream_t st);
 hipError_t launch_tile_scan(const Dims& d, int32_t* work, int32_t* counts, hipStream_t st);
+hipError_t launch_route_and_scan(const Dims& d, const float* logits, const float* bias,
+                                 int32_t* ids, float* gates, int32_t* work, int32_t* counts,
+                                 hipStream_t st);
 hipError_t launch_plan(const Dims& d, const int32_t* counts, int32_t* plan, int32_t* status,
                        hipStream_t st);
 hipError_t launch_plan_quota(const Dims& d, const int32_t* counts, int32_t* plan,

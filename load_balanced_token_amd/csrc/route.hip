@@ -104,4 +104,78 @@ hipError_t launch_tile_scan(const Dims& d, int32_t* work, int32_t* counts, hipSt
   return hipGetLastError();
 }
 
+// Small batches (1 <= N <= kSmallTokens and n_tiles * E <= kSmallHist): one
+// workgroup routes every token, keeps each tile's histogram in LDS and does
+// the tile scan itself, so route + scan is one launch.  Same outputs as
+// k_route + k_tile_scan.  Measured on MI355X: N = 8 (decode, S = 1) route +
+// scan 12.3 -> 9.9 us; at N = 128 one workgroup is slower than eight tiles in
+// parallel (11.7 -> 20.3 us), so only batches that fit 8 waves in one pass
+// take it.
+constexpr int kSmallHist = 16384;
+constexpr int kSmallTokens = 32;
+
+static bool small_batch(const Dims& d) {
+  return d.N >= 1 && d.N <= kSmallTokens && (long long)d.n_tiles * d.E <= kSmallHist;
+}
+
+template <int V>
+__global__ __launch_bounds__(kRouteThreads) void k_route_small(const float* __restrict__ logits,
+                                                               const float* __restrict__ bias,
+                                                               Dims d, int vec,
+                                                               int32_t* __restrict__ ids,
+                                                               float* __restrict__ gates,
+                                                               int32_t* __restrict__ work,
+                                                               int32_t* __restrict__ counts) {
+  __shared__ RouteScratch rs;
+  __shared__ int hist[kSmallHist];     // [tile][E]
+  const int E = d.E, nt = d.n_tiles, S = d.S, tpr = d.tpr;
+  for (int i = threadIdx.x; i < nt * E; i += kRouteThreads) hist[i] = 0;
+  route_span<V>(logits, bias, d, vec, 0, d.N, ids, gates, rs, [&](long long t, int id) {
+    const int r = (int)(t / S), j = (int)(t - (long long)r * S) / kTileTokens;
+    atomicAdd(&hist[(r * tpr + j) * E + id], 1);
+  });
+  __syncthreads();
+  int32_t* base = work + work_tile_base(d);
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    int run = 0;
+    for (int r = 0; r < d.R; ++r) {
+      int sum = 0;
+      for (int j = 0; j < tpr; ++j) {
+        const int tile = r * tpr + j;
+        const int c = hist[tile * E + e];
+        work[(long long)e * nt + tile] = c;
+        base[(long long)tile * E + e] = run;
+        run += c;
+        sum += c;
+      }
+      counts[(long long)r * E + e] = sum;
+    }
+  }
+}
+
+// The whole routing step: route + scan, or the one small-batch launch.
+hipError_t launch_route_and_scan(const Dims& d, const float* logits, const float* bias,
+                                 int32_t* ids, float* gates, int32_t* work, int32_t* counts,
+                                 hipStream_t st) {
+  if (!small_batch(d)) {
+    hipError_t e = launch_route(d, logits, bias, ids, gates, work, st);
+    if (e == hipSuccess) e = launch_tile_scan(d, work, counts, st);
+    return e;
+  }
+  const int vec = route_vec(logits, d.E);
+  const dim3 grid(1), block(kRouteThreads);
+  const int V = (d.E + kRowLanes - 1) / kRowLanes;
+#define LBT_SMALL(VV) hipLaunchKernelGGL(k_route_small<VV>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work, counts)
+  if (V <= 1) LBT_SMALL(1);
+  else if (V <= 2) LBT_SMALL(2);
+  else if (V <= 4) LBT_SMALL(4);
+  else if (V <= 8) LBT_SMALL(8);
+  else if (V <= 16) LBT_SMALL(16);
+  else if (V <= 24) LBT_SMALL(24);
+  else LBT_SMALL(32);
+#undef LBT_SMALL
+  return hipGetLastError();
+}
+
+
 }  // namespace lbt

@@ -98,3 +98,34 @@ def test_random_shapes_training(seed):
     t.cuda.synchronize()
     want, mag = oracle.dispatch_bwd(lambda r: d_recv[r], ref["align"]["slot"], w.K, w.N)
     assert (np.abs(dx.cpu().numpy().astype(np.float64) - want) <= DX_RTOL * mag + 1e-30).all()
+
+
+def small_case(seed):
+    """At most 32 tokens (the single-launch route with its own tile scan)."""
+    rng = np.random.default_rng(5000 + seed)
+    R = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    S = int(rng.integers(1, 32 // R + 1))
+    E = R * int(rng.integers(1, 512 // R + 1)) if rng.random() < 0.5 else R * int(rng.integers(1, 9))
+    E = min(E, 512)
+    K = int(rng.integers(1, min(E, 64) + 1))
+    blk = int(rng.choice([1, 4, 16, 128]))
+    B = int(rng.integers(0, 4))
+    score = "softmax" if rng.random() < 0.3 else "sigmoid"
+    logits = rng.standard_normal((R * S, E)).astype(np.float32)
+    planner = "quota" if seed % 2 else "fixed"
+    w = WORKLOADS["tiny"].with_(E=E, K=K, R=R, S=S, H=64, B=B, blk=blk, score=score)
+    return w, logits, planner
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_small_batches(seed):
+    w, logits, planner = small_case(seed)
+    assert 1 <= w.N <= 32 and w.R * w.E <= 16384
+    print(f"[small] seed {seed}: E={w.E} R={w.R} K={w.K} S={w.S} blk={w.blk} B={w.B} {planner}",
+          flush=True)
+    res = gu.run_front(gu.shape_of(w), logits, planner=planner)
+    ref = gu.run_oracle(w, logits, planner=planner)
+    gu.check_route(res, ref)
+    gu.check_plan(res["plan_fields"], ref["plan"], w.P)
+    gu.check_align(res, ref, w.R, res["sizes"]["C"])
+    _full_move_check(w, res, ref, activations(w, 0))

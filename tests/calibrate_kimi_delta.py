@@ -4,7 +4,7 @@ scale workload.  Bisection on [0, 4] over a 16,384-token sample of layer 0,
 routed by the CPU oracle.  Prints the offset, rounded to a multiple of 2^-10,
 and the share it reaches on the full layer-0 routing.
 
-    python workloads/calibrate_kimi_delta.py
+    python tests/calibrate_kimi_delta.py
 """
 import os
 import sys

@@ -34,7 +34,7 @@ X_CHUNK = 1024  # rows of x drawn per independent random stream
 
 # Offset for the hot experts of the Kimi-K3-scale workload.  Chosen so that
 # the realised share of (token, expert) assignments that land on the 19 hot
-# experts (5% of 384) is 0.30; workloads/calibrate_kimi_delta.py recomputes it
+# experts (5% of 384) is 0.30; tests/calibrate_kimi_delta.py recomputes it
 # with the oracle's router and prints the share it reaches.
 KIMI_DELTA = 1.0263671875
 

@@ -161,33 +161,51 @@ __device__ __forceinline__ int wave_incl_scan_dpp(int x) {
   return x;
 }
 
-// Exclusive prefix sum of a[0..n) in LDS by ONE wave (lane l takes the
-// contiguous chunk [l*c, l*c + c), c = ceil(n/64) <= CMAX); a[n] receives the
-// total, which every lane returns.  The chunk is read with independent loads
-// (no dependent LDS round trips) and scanned in registers.  No workgroup
-// barrier.
-template <int CMAX>
-__device__ __forceinline__ int wave_excl_scan_lds(int* a, int n) {
+// Exclusive prefix sum of a[0..n) in LDS by ONE wave, n <= 64*C: lane l
+// takes the contiguous chunk [l*C, l*C + C) with C fixed at compile time, so
+// the chunk is read and written without branches (neighbouring words pair
+// up into wide LDS accesses) and scanned in registers.  a must hold at least
+// 64*C + 1 ints: entries at or past n are read as 0, entries n .. 64*C - 1
+// are overwritten with the total, and a[n] receives the total, which every
+// lane returns.  No workgroup barrier.
+template <int C>
+__device__ __forceinline__ int wave_excl_scan_chunk(int* a, int n) {
   const int lane = lane_id();
-  const int c = (n + kWave - 1) / kWave;
-  const int lo = lane * c;
-  int v[CMAX];
+  const int lo = lane * C;
+  int v[C];
 #pragma unroll
-  for (int i = 0; i < CMAX; ++i) v[i] = (i < c && lo + i < n) ? a[lo + i] : 0;
+  for (int i = 0; i < C; ++i) {
+    const int x = a[lo + i];
+    v[i] = lo + i < n ? x : 0;
+  }
   int s = 0;
 #pragma unroll
-  for (int i = 0; i < CMAX; ++i) s += v[i];
+  for (int i = 0; i < C; ++i) s += v[i];
   const int incl = wave_incl_scan_dpp(s);
   int run = incl - s;
 #pragma unroll
-  for (int i = 0; i < CMAX; ++i) {
-    if (i < c && lo + i < n) a[lo + i] = run;
+  for (int i = 0; i < C; ++i) {
+    a[lo + i] = run;
     run += v[i];
   }
   const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
-  if (lane == 0) a[n] = total;
+  if (lane == 0) a[n] = total;   // after the chunk stores in program order
   __builtin_amdgcn_wave_barrier();
   return total;
+}
+
+// The same for n <= 64*CMAX, with the smallest chunk of 1, 2, 4, 8, 16 or
+// CMAX that covers n.  a must hold at least 64*CMAX + 1 ints, and its entries
+// past n are scratch (overwritten).
+template <int CMAX>
+__device__ __forceinline__ int wave_excl_scan_lds(int* a, int n) {
+  const int c = (n + kWave - 1) / kWave;
+  if (c <= 1) return wave_excl_scan_chunk<1>(a, n);
+  if constexpr (CMAX >= 2) if (c <= 2) return wave_excl_scan_chunk<2>(a, n);
+  if constexpr (CMAX >= 4) if (c <= 4) return wave_excl_scan_chunk<4>(a, n);
+  if constexpr (CMAX >= 8) if (c <= 8) return wave_excl_scan_chunk<8>(a, n);
+  if constexpr (CMAX >= 16) if (c <= 16) return wave_excl_scan_chunk<16>(a, n);
+  return wave_excl_scan_chunk<CMAX>(a, n);
 }
 
 // First index in a[0..n) whose value is > x (a non-decreasing).

@@ -43,31 +43,31 @@ constexpr int kDirectCompares = 64;
 
 __device__ __forceinline__ int pad_to(int c, int blk) { return ((c + blk - 1) / blk) * blk; }
 
-// LDS of the plan.
+// LDS of the plan.  The arrays scanned by one wave hold 64*CMAX + 1 ints
+// (CMAX chunks per lane) and start on 16 bytes.
 struct PlanSmem {
-  int sT[kMaxE + 1];      // T_e
-  int sX[kMaxE + 1];      // exclusive prefix of T over e
-  int sH[kMaxE];          // h_e
-  int sO[kMaxE + 1];      // o_e, then exclusive prefix O_e
-  int sNp[kMaxE + 1];     // pieces of expert e, then exclusive prefix
-  int sDlo[kMaxE];        // compact index of e's first deficit rank
-  int sL[kMaxR];          // L_r
-  int sDef[kMaxR];        // def_r
-  int sD[kMaxR + 1];      // exclusive prefix D_r
-  int sCidx[kMaxR + 1];   // compact index among deficit ranks
-  int sDl[kMaxR];         // compact index -> rank
-  int sDc[kMaxR];         // compact index -> D of that deficit rank (strictly increasing)
-  int sLb[kMaxE + 1];     // deficit starts below O_g (line position g); [E]: below the overflow total
-  int sRep[kMaxR + 1];    // replicas per rank, then first piece of rank
+  int sT[kMaxE + 1];                    // T_e
+  alignas(16) int sX[kMaxE + 1];        // exclusive prefix of T over e
+  int sH[kMaxE];                        // h_e
+  alignas(16) int sO[kMaxE + 1];        // o_e, then exclusive prefix O_e
+  alignas(16) int sNp[kMaxE + 1];       // pieces of expert e, then exclusive prefix
+  int sDlo[kMaxE];                      // compact index of e's first deficit rank
+  int sL[kMaxR];                        // L_r
+  int sDef[kMaxR];                      // def_r
+  alignas(16) int sD[kMaxR + 1];        // exclusive prefix D_r
+  alignas(16) int sCidx[kMaxR + 1];     // compact index among deficit ranks
+  int sDl[kMaxR];                       // compact index -> rank
+  int sDc[kMaxR];                       // compact index -> D of that deficit rank (strictly increasing)
+  int sLb[kMaxE + 1];                   // deficit starts below O_g (line position g); [E]: below the overflow total
+  alignas(16) int sRep[kMaxR + 1];      // replicas per rank, then first piece of rank
   int sPe[kMaxPieces], sPd[kMaxPieces], sPc[kMaxPieces], sPl[kMaxPieces],
       sPj[kMaxPieces];
-  int sF[kMaxE + kMaxPieces + 1];  // flat segment padded lengths -> starts
-  int sLam[kMaxE];        // quota rule: line position of expert e inside its rank block
-  int sPerm[kMaxE];       // quota rule: expert at line position
-  int sHx[kMaxE + 1];     // quota rule: loads in line order, then exclusive prefix
+  alignas(16) int sF[kMaxE + kMaxPieces + 1];  // flat segment padded lengths -> starts
+  int sLam[kMaxE];                      // quota rule: line position of expert e inside its rank block
+  int sPerm[kMaxE];                     // quota rule: expert at line position
+  int sHx[kMaxE + 1];                   // quota rule: loads in line order, then exclusive prefix
   // max_T, max_L, over ranks, over experts, status, nP, totOv, Ptot, tau, max replicas
   int sStat[12];
-
 };
 
 // Pieces per line position (sNp) and the compact index of each position's
@@ -279,9 +279,15 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
       nOverE += __shfl_xor(nOverE, o, kWave);
       nOverR += __shfl_xor(nOverR, o, kWave);
     }
+    // replicas and padded rows per rank: the capacity check
     int maxRep = 0;
-    for (int r = lane; r < R; r += kWave) maxRep = max(maxRep, sRep[r + 1] - sRep[r]);
+    bool over_cap = false;
+    for (int r = lane; r < R; r += kWave) {
+      maxRep = max(maxRep, sRep[r + 1] - sRep[r]);
+      over_cap = over_cap || sF[(r + 1) * nh + sRep[r + 1]] - sF[r * nh + sRep[r]] > C;
+    }
     maxRep = wave_max(maxRep);
+    over_cap = __any(over_cap);
     if (lane == 0) {
       sStat[8] = tau;
       sStat[9] = maxRep;
@@ -289,7 +295,7 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
       sStat[1] = maxL;
       sStat[2] = nOverR;
       sStat[3] = nOverE;
-      sStat[4] = consistent ? 0 : LBT_ST_BADCOUNT;
+      sStat[4] = (consistent ? 0 : LBT_ST_BADCOUNT) | (over_cap ? LBT_ST_CAPACITY : 0);
       sStat[5] = nP;
       sStat[6] = totOv;
       sStat[7] = Ptot;
@@ -298,9 +304,30 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
   __syncthreads();
   // rank r's flat entries are [fb(r), fb(r+1)) with fb(r) = r*nh + sRep[r]
   const int nP = sStat[5];
+  int32_t* P = plan;
+
+  // the header and the status word: everything they hold is in LDS already,
+  // so no further barrier (which would also wait for the blob's stores)
+  if (tid == 0) {
+    const int st = sStat[4];
+    P[pl.hdr + LBT_HDR_N_PIECES] = nP;
+    P[pl.hdr + LBT_HDR_MAX_T] = sStat[0];
+    P[pl.hdr + LBT_HDR_MAX_L] = sStat[1];
+    P[pl.hdr + LBT_HDR_TOTAL_OVERFLOW] = sStat[6];
+    P[pl.hdr + LBT_HDR_N_DEFICIT_RANKS] = sCidx[R];
+    P[pl.hdr + LBT_HDR_N_OVERFLOW_RANKS] = sStat[2];
+    P[pl.hdr + LBT_HDR_N_OVERFLOW_EXPERTS] = sStat[3];
+    P[pl.hdr + LBT_HDR_STATUS] = st;
+    P[pl.hdr + LBT_HDR_P] = sStat[7];
+    P[pl.hdr + LBT_HDR_TAU] = sStat[8];
+    P[pl.hdr + LBT_HDR_MAX_REPLICAS] = sStat[9];
+    P[pl.hdr + LBT_HDR_FEASIBLE] = sStat[9] <= B ? 1 : 0;
+    P[pl.hdr + LBT_HDR_LOCAL] = HOT ? 1 : 0;
+    for (int i = LBT_HDR_LOCAL + 1; i < LBT_HDR_WORDS; ++i) P[pl.hdr + i] = 0;
+    if (status != nullptr) *status = st;
+  }
 
   // 3. every wave: write the blob from LDS
-  int32_t* P = plan;
   for (int e = tid; e < E; e += kPlanThreads) {
     const int r = e / nh;
     const int fb = r * nh + sRep[r];
@@ -311,7 +338,6 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
     P[pl.O + e] = sO[lam(e)];
     P[pl.home_row + e] = sF[fb + (e - r * nh)] - sF[fb];
   }
-  int capflag = 0;
   for (int r = tid; r < R; r += kPlanThreads) {
     const int fb = r * nh + sRep[r];
     const int fe = (r + 1) * nh + sRep[r + 1];
@@ -324,9 +350,7 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
     P[pl.n_rows_padded + r] = nrp;
     P[pl.n_slots + r] = min(nrep, B);
     P[pl.n_remote + r] = nrep - min(nrep, B);
-    if (nrp > C) capflag = LBT_ST_CAPACITY;
   }
-  if (capflag) atomicOr(&sStat[4], capflag);
   if (tid == 0) P[pl.D + R] = sD[R];
   // segment tables, one rank per wave at a time, entries across the lanes
   constexpr int kPlanWaves = kPlanThreads / kWave;
@@ -375,25 +399,6 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
     P[pl.piece_count + g] = cnt;
     P[pl.piece_line + g] = line;
     P[pl.piece_row + g] = row;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    const int st = sStat[4];
-    P[pl.hdr + LBT_HDR_N_PIECES] = nP;
-    P[pl.hdr + LBT_HDR_MAX_T] = sStat[0];
-    P[pl.hdr + LBT_HDR_MAX_L] = sStat[1];
-    P[pl.hdr + LBT_HDR_TOTAL_OVERFLOW] = sStat[6];
-    P[pl.hdr + LBT_HDR_N_DEFICIT_RANKS] = sCidx[R];
-    P[pl.hdr + LBT_HDR_N_OVERFLOW_RANKS] = sStat[2];
-    P[pl.hdr + LBT_HDR_N_OVERFLOW_EXPERTS] = sStat[3];
-    P[pl.hdr + LBT_HDR_STATUS] = st;
-    P[pl.hdr + LBT_HDR_P] = sStat[7];
-    P[pl.hdr + LBT_HDR_TAU] = sStat[8];
-    P[pl.hdr + LBT_HDR_MAX_REPLICAS] = sStat[9];
-    P[pl.hdr + LBT_HDR_FEASIBLE] = sStat[9] <= B ? 1 : 0;
-    P[pl.hdr + LBT_HDR_LOCAL] = HOT ? 1 : 0;
-    for (int i = LBT_HDR_LOCAL + 1; i < LBT_HDR_WORDS; ++i) P[pl.hdr + i] = 0;
-    if (status != nullptr) *status = st;
   }
 }
 

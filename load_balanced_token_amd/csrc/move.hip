@@ -241,6 +241,74 @@ __global__ __launch_bounds__(THR) void k_combine_w(const u32x2* __restrict__ out
   }
 }
 
+// Small batches (at most kColsTokens tokens): one wave per (token, 64
+// consecutive pieces of its row), so that a few tokens still spread over many
+// CUs instead of keeping a handful of workgroups busy.  Same stores as
+// k_dispatch: lane c of slice y moves chunk y*64 + c of the row to all K
+// destinations.
+constexpr int kColsTokens = 256;
+constexpr int kMaxGridY = 65535;   // largest grid y dimension
+
+template <int KT>
+__global__ __launch_bounds__(kWave) void k_dispatch_cols(const u32x4* __restrict__ x,
+                                                         const int32_t* __restrict__ slot,
+                                                         u32x4* __restrict__ recv, int Krt,
+                                                         int H8, long long n_rows) {
+  const int K = KT > 0 ? KT : Krt;
+  const int t = blockIdx.x;
+  const int c = blockIdx.y * kWave + threadIdx.x;
+  if (c >= H8) return;
+  const u32x4 v = x[(long long)t * H8 + c];
+  const int32_t* sl = slot + (long long)t * K;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int s = sl[k];
+    if (s >= 0 && (long long)s < n_rows) recv[(long long)s * H8 + c] = v;
+  }
+}
+
+// Combine of a small batch, one wave per (token, 64 groups of 4 values):
+// the same multiply-adds as k_combine in the same ascending-k order, so the
+// results are bit-identical.  The K rows are loaded in groups of KT (or 8
+// when K is not a compile-time constant) before the group's multiply-adds.
+template <int KT, bool BF16, bool UNIT>
+__global__ __launch_bounds__(kWave) void k_combine_cols(const u32x2* __restrict__ out,
+                                                        const int32_t* __restrict__ slot,
+                                                        const float* __restrict__ gates, int Krt,
+                                                        int G4, long long n_rows,
+                                                        void* __restrict__ y) {
+  constexpr int G = KT > 0 ? KT : 8;
+  const int K = KT > 0 ? KT : Krt;
+  const int t = blockIdx.x;
+  const int q = blockIdx.y * kWave + threadIdx.x;
+  if (q >= G4) return;
+  const int32_t* sl = slot + (long long)t * K;
+  const float* gt = UNIT ? nullptr : gates + (long long)t * K;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < K; k0 += G) {
+    int s[G];
+    bool use[G];
+    u32x2 v[G];
+#pragma unroll
+    for (int kk = 0; kk < G; ++kk) {
+      s[kk] = k0 + kk < K ? sl[k0 + kk] : -1;
+      use[kk] = s[kk] >= 0 && (long long)s[kk] < n_rows;   // the same for the whole wave
+      v[kk] = use[kk] ? __builtin_nontemporal_load(out + (long long)s[kk] * G4 + q) : u32x2{0u, 0u};
+    }
+#pragma unroll
+    for (int kk = 0; kk < G; ++kk)
+      if (use[kk]) fma4(acc, UNIT ? 1.f : gt[k0 + kk], v[kk]);
+  }
+  if constexpr (BF16) {
+    const u32x2 o{to_bf16(acc[0]) | (to_bf16(acc[1]) << 16),
+                  to_bf16(acc[2]) | (to_bf16(acc[3]) << 16)};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(y) + (long long)t * G4 + q);
+  } else {
+    __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]},
+                                reinterpret_cast<f32x4*>(y) + (long long)t * G4 + q);
+  }
+}
+
 // Threads of a row workgroup: enough for `per` pieces each, a multiple of
 // 64, at most `cap` (wider rows take several passes).
 static int row_threads(int pieces, int per, int cap) {
@@ -267,9 +335,21 @@ hipError_t launch_dispatch(const Dims& d, const uint16_t* x, const int32_t* slot
   if (d.N == 0) return hipSuccess;
   const u32x4* xs = reinterpret_cast<const u32x4*>(x);
   u32x4* rv = reinterpret_cast<u32x4*>(recv);
+  const long long n_rows = (long long)d.R * d.C;
+  if (d.N <= kColsTokens && d.H / 8 <= kWave * kMaxGridY) {
+    const int H8 = d.H / 8;
+    const dim3 grid(d.N, (H8 + kWave - 1) / kWave), block(kWave);
+    switch (d.K) {
+      case 2: hipLaunchKernelGGL(k_dispatch_cols<2>, grid, block, 0, st, xs, slot, rv, d.K, H8, n_rows); break;
+      case 4: hipLaunchKernelGGL(k_dispatch_cols<4>, grid, block, 0, st, xs, slot, rv, d.K, H8, n_rows); break;
+      case 8: hipLaunchKernelGGL(k_dispatch_cols<8>, grid, block, 0, st, xs, slot, rv, d.K, H8, n_rows); break;
+      default: hipLaunchKernelGGL(k_dispatch_cols<0>, grid, block, 0, st, xs, slot, rv, d.K, H8, n_rows); break;
+    }
+    return hipGetLastError();
+  }
   if (d.H == 7168 && d.K == 8) {   // DeepSeek-V3 / Kimi-K2 hidden size
     hipLaunchKernelGGL((k_dispatch_w<896, 1, 8>), dim3(d.N), dim3(896), 0, st, xs, slot, rv,
-                       (long long)d.R * d.C);
+                       n_rows);
     return hipGetLastError();
   }
   switch (d.K) {
@@ -297,6 +377,18 @@ static void launch_combine_t(const Dims& d, const u32x2* o, const int32_t* slot,
 template <bool BF16, bool UNIT>
 static void launch_combine_k(const Dims& d, const u32x2* o, const int32_t* slot, const float* gates,
                              void* y, hipStream_t st) {
+  if (d.N <= kColsTokens && d.H / 4 <= kWave * kMaxGridY) {
+    const int G4 = d.H / 4;
+    const long long n_rows = (long long)d.R * d.C;
+    const dim3 grid(d.N, (G4 + kWave - 1) / kWave), block(kWave);
+    switch (d.K) {
+      case 2: hipLaunchKernelGGL((k_combine_cols<2, BF16, UNIT>), grid, block, 0, st, o, slot, gates, d.K, G4, n_rows, y); break;
+      case 4: hipLaunchKernelGGL((k_combine_cols<4, BF16, UNIT>), grid, block, 0, st, o, slot, gates, d.K, G4, n_rows, y); break;
+      case 8: hipLaunchKernelGGL((k_combine_cols<8, BF16, UNIT>), grid, block, 0, st, o, slot, gates, d.K, G4, n_rows, y); break;
+      default: hipLaunchKernelGGL((k_combine_cols<0, BF16, UNIT>), grid, block, 0, st, o, slot, gates, d.K, G4, n_rows, y); break;
+    }
+    return;
+  }
   if (d.H == 7168 && d.K == 8) {   // DeepSeek-V3 / Kimi-K2 hidden size
     hipLaunchKernelGGL((k_combine_w<224, 8, 8, BF16, UNIT>), dim3(d.N), dim3(224), 0, st, o, slot,
                        gates, (long long)d.R * d.C, y);

@@ -466,12 +466,13 @@ def test_graph_capture_replays_match_eager():
         assert buf["status"].item() == 0
 
 
-@pytest.mark.parametrize("H", [7168, 512])
-def test_dispatch_combine_with_dropped_pairs(H):
+@pytest.mark.parametrize("H,S", [(7168, 32), (7168, 33), (512, 32), (512, 33)])
+def test_dispatch_combine_with_dropped_pairs(H, S):
     """A capacity below the plan's need drops pairs (slot -1): dispatch skips
-    them and combine sums only the pairs that fit (both row-width paths)."""
+    them and combine sums only the pairs that fit (both row widths; N = 256
+    takes the small-batch kernels, N = 264 the row-per-workgroup ones)."""
     t = gu.torch()
-    w = WORKLOADS["dsv3"].with_(S=32, H=H)
+    w = WORKLOADS["dsv3"].with_(S=S, H=H)
     logits = router_logits(w, 0)
     ref = gu.run_oracle(w, logits)
     need = int(ref["plan"]["n_rows_padded"].max())
@@ -496,6 +497,54 @@ def test_dispatch_combine_with_dropped_pairs(H):
     got = y.cpu().numpy().astype(np.float64)
     assert (np.abs(got - want) <= gu.COMBINE_RTOL * np.abs(want) + 1e-30).all()
 
+
+
+@pytest.mark.parametrize("H,K", [(7168, 8), (512, 8), (136, 3), (64, 4)])
+def test_small_batch_kernels_bitwise_equal_row_kernels(H, K):
+    """Batches of up to 256 tokens move rows with one wave per slice of a row;
+    larger ones with one workgroup per row.  The same pairs through both (256
+    tokens vs the same 256 plus 8 more) give bit-identical recv rows,
+    combine outputs (fp32 and bf16) and dispatch gradients."""
+    import load_balanced_token_amd as lbt
+    t = gu.torch()
+    R, E, cap = 8, 64, 512
+    small = lbt.Path(lbt.Shape(E=E, K=K, R=R, S=32, H=H, B=2, blk=128, cap=cap))
+    large = lbt.Path(lbt.Shape(E=E, K=K, R=R, S=33, H=H, B=2, blk=128, cap=cap))
+    Ns, Nl = R * 32, R * 33
+    rng = np.random.default_rng(7 + H + K)
+    rows = rng.permutation(R * cap)[: Nl * K].astype(np.int32)
+    rows[rng.random(Nl * K) < 0.05] = -1               # some pairs did not fit
+    slot_l = gu.h2d(rows)
+    slot_s = gu.h2d(rows[: Ns * K].copy())
+    gates = gu.h2d(rng.random((Nl, K)).astype(np.float32))
+    gates_s = gates[:Ns].contiguous()
+    bf16 = lambda n: t.randn(n, H, device="cuda").to(t.bfloat16).view(t.int16)
+    out = bf16(R * cap)
+    x = bf16(Nl)
+    for y_dtype in (t.float32, t.int16):
+        ys = t.empty(Ns, H, dtype=y_dtype, device="cuda")
+        yl = t.empty(Nl, H, dtype=y_dtype, device="cuda")
+        small.combine(out, slot_s, gates_s, ys)
+        large.combine(out, slot_l, gates, yl)
+        assert t.equal(ys.view(t.int32) if y_dtype == t.float32 else ys,
+                       (yl.view(t.int32) if y_dtype == t.float32 else yl)[:Ns])
+        small.dispatch_bwd(out, slot_s, ys)
+        large.dispatch_bwd(out, slot_l, yl)
+        assert t.equal(ys.view(t.int32) if y_dtype == t.float32 else ys,
+                       (yl.view(t.int32) if y_dtype == t.float32 else yl)[:Ns])
+    rs = t.zeros(R * cap, H, dtype=t.int16, device="cuda")
+    rl = t.zeros(R * cap, H, dtype=t.int16, device="cuda")
+    small.dispatch(x[:Ns].contiguous(), slot_s, rs)
+    large.dispatch(x, slot_l, rl)
+    t.cuda.synchronize()
+    mine = rows[: Ns * K]
+    mine = mine[mine >= 0]
+    idx = t.from_numpy(mine.astype(np.int64)).cuda()
+    assert t.equal(rs[idx], rl[idx])
+    assert t.equal(rs[idx], x[t.from_numpy(np.nonzero(rows[: Ns * K] >= 0)[0] // K).cuda()])
+    untouched = np.ones(R * cap, bool)
+    untouched[mine] = False
+    assert not rs[t.from_numpy(np.nonzero(untouched)[0]).cuda()].any()
 
 
 # --------------------------------------------------------------------------- widths and limits

@@ -90,7 +90,7 @@ typedef struct lbt_sizes {
   int64_t N, P, SK;
   int64_t C;              /* rows per rank of recv / out */
   int64_t n_blocks;       /* C / blk blocks per rank */
-  int64_t tile_tokens;    /* tokens per histogram tile (tiles never cross ranks) */
+  int64_t tile_tokens;    /* tokens per align tile (tiles never cross ranks) */
   int64_t tiles_per_rank; /* ceil(S / tile_tokens) */
   int64_t n_tiles;        /* R * tiles_per_rank */
   int64_t work_words;     /* int32 words of the route/histogram workspace */
@@ -147,8 +147,9 @@ typedef struct lbt_sizes {
  * when the shape is outside the limits above. */
 int lbt_query_sizes(const lbt_shape* s, lbt_sizes* out);
 
-/* Router top-K and the per-tile expert histogram (one launch), then the
- * per-rank load matrix and per-tile prefix offsets (a second launch).
+/* Router top-K and the expert histogram of every 32-token sub-tile (one
+ * launch), then the per-rank load matrix and per-tile prefix offsets (a
+ * second launch; batches of at most 32 tokens do both in one).
  * [AlignSort] (the MoE layer gates each token to its Top-K experts by gate
  * score, DeepSeek's gating bias steering the choice); [UltraEP] section
  * "その仕組みは高速なエキスパート複製に依存する" (the exact post-routing load

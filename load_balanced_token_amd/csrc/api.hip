@@ -31,6 +31,7 @@ int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z) {
   }
   const long long tpr = (S + kTileTokens - 1) / kTileTokens;
   const long long nt = R * tpr;
+  const long long spr = (S + kSubTokens - 1) / kSubTokens;
   if (P >= (1LL << 31) || R * C >= (1LL << 31) || N * H / 8 >= (1LL << 40)) return LBT_EUNSUPPORTED;
   if (SK >= (1LL << 30)) return LBT_EUNSUPPORTED;
 
@@ -74,13 +75,14 @@ int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z) {
     d->E = (int)E; d->K = (int)K; d->R = (int)R; d->S = (int)S; d->H = (int)H; d->B = (int)B;
     d->blk = (int)blk; d->score_fn = s->score_fn; d->renorm = s->renorm;
     d->nh = (int)nh; d->N = (int)N; d->P = P; d->SK = (int)SK; d->tau_max = (int)tmax; d->C = (int)C;
-    d->n_blocks = (int)(C / blk); d->tpr = (int)tpr; d->n_tiles = (int)nt; d->pl = pl;
+    d->n_blocks = (int)(C / blk); d->tpr = (int)tpr; d->n_tiles = (int)nt;
+    d->spr = (int)spr; d->n_sub = (int)(R * spr); d->pl = pl;
   }
   if (z != nullptr) {
     memset(z, 0, sizeof(*z));
     z->N = N; z->P = P; z->SK = SK; z->C = C; z->n_blocks = C / blk;
     z->tile_tokens = kTileTokens; z->tiles_per_rank = tpr; z->n_tiles = nt;
-    z->work_words = 2 * E * nt;
+    z->work_words = E * (R * spr + nt);
     z->max_seg = ms; z->max_pieces = mp; z->plan_words = off;
     z->off_hdr = pl.hdr; z->off_T = pl.T; z->off_h = pl.h; z->off_O = pl.O;
     z->off_home_row = pl.home_row; z->off_L = pl.L; z->off_def = pl.def; z->off_D = pl.D;

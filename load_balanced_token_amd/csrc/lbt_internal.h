@@ -10,8 +10,8 @@
 namespace lbt {
 
 constexpr int kWave = 64;
-constexpr int kTileTokens = 128;   // tokens per histogram tile
-constexpr int kSubTokens = 32;     // tokens per bit-mask sub-tile (one u32)
+constexpr int kTileTokens = 128;   // tokens per align tile (prefix offsets)
+constexpr int kSubTokens = 32;     // tokens per histogram sub-tile (one u32 bit mask)
 constexpr int kSubTiles = kTileTokens / kSubTokens;
 constexpr int kMaxE = 512;
 constexpr int kMaxR = 512;
@@ -38,8 +38,10 @@ struct Dims {
   int tau_max;   // largest per-rank load a plan may give (>= SK)
   int C;         // rows per rank
   int n_blocks;  // C / blk
-  int tpr;       // tiles per rank
+  int tpr;       // align tiles per rank
   int n_tiles;   // R * tpr
+  int spr;       // histogram sub-tiles per rank
+  int n_sub;     // R * spr
   PlanLayout pl;
 };
 
@@ -75,11 +77,12 @@ hipError_t launch_combine_bwd(const Dims& d, const uint16_t* out, const int32_t*
                               const float* gates, int dy_dtype, const void* dy, uint16_t* d_out,
                               float* d_gates, hipStream_t st);
 
-// Workspace layout: tile_counts [E][n_tiles] (expert-major, for the column
-// scan) followed by tile_base [n_tiles][E] (tile-major, for the align step).
-__host__ __device__ inline long long work_tile_counts(const Dims&) { return 0; }
+// Workspace layout: sub_counts [E][n_sub] (per 32-token sub-tile, expert-
+// major, for the column scan) followed by tile_base [n_tiles][E] (per
+// 128-token tile, tile-major, for the align step).  Sub-tiles and tiles
+// never cross ranks; tile j of rank r holds its sub-tiles 4j .. 4j+3.
 __host__ __device__ inline long long work_tile_base(const Dims& d) {
-  return (long long)d.E * d.n_tiles;
+  return (long long)d.E * d.n_sub;
 }
 
 // ---- device helpers -------------------------------------------------------

@@ -1,6 +1,6 @@
-// Router top-K with the fused per-tile expert histogram, the histogram of
-// caller-supplied ids, and the column scan that turns per-tile counts into
-// per-tile prefix offsets and the per-rank load matrix.
+// Router top-K with the fused per-sub-tile expert histogram, the histogram
+// of caller-supplied ids, and the column scan that turns per-sub-tile counts
+// into per-tile prefix offsets and the per-rank load matrix.
 //
 // The top-K itself is in route_core.h.
 #include "route_core.h"
@@ -12,22 +12,23 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict
                                                          const float* __restrict__ bias, Dims d,
                                                          int vec, int32_t* __restrict__ ids,
                                                          float* __restrict__ gates,
-                                                         int32_t* __restrict__ tile_counts) {
+                                                         int32_t* __restrict__ sub_counts) {
   __shared__ RouteSmem sm;
-  route_tile<V>(logits, bias, d, vec, blockIdx.x, ids, gates, tile_counts, sm);
+  route_sub<V>(logits, bias, d, vec, blockIdx.x, ids, gates, sub_counts, sm);
 }
 
-// Histogram of caller-supplied ids, one thread per token of a tile.
-__global__ __launch_bounds__(kTileTokens) void k_histogram(const int32_t* __restrict__ ids, Dims d,
-                                                           int32_t* __restrict__ tile_counts,
-                                                           int32_t* __restrict__ status) {
+// Histogram of caller-supplied ids, one thread per token of a sub-tile.
+constexpr int kHistThreads = 64;
+__global__ __launch_bounds__(kHistThreads) void k_histogram(const int32_t* __restrict__ ids, Dims d,
+                                                            int32_t* __restrict__ sub_counts,
+                                                            int32_t* __restrict__ status) {
   __shared__ int hist[kMaxE];
   const int E = d.E, K = d.K;
-  const int tile = blockIdx.x;
-  const int r = tile / d.tpr, j = tile - r * d.tpr;
-  const int t0 = r * d.S + j * kTileTokens;
-  const int len = min(kTileTokens, d.S - j * kTileTokens);
-  for (int e = threadIdx.x; e < E; e += kTileTokens) hist[e] = 0;
+  const int sub = blockIdx.x;
+  const int r = sub / d.spr, j = sub - r * d.spr;
+  const int t0 = r * d.S + j * kSubTokens;
+  const int len = min(kSubTokens, d.S - j * kSubTokens);
+  for (int e = threadIdx.x; e < E; e += kHistThreads) hist[e] = 0;
   __syncthreads();
   int flags = 0;
   if ((int)threadIdx.x < len) {
@@ -40,35 +41,42 @@ __global__ __launch_bounds__(kTileTokens) void k_histogram(const int32_t* __rest
   }
   if (flags && status != nullptr) atomicOr(status, flags);
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kTileTokens)
-    tile_counts[(long long)e * d.n_tiles + tile] = hist[e];
+  for (int e = threadIdx.x; e < E; e += kHistThreads)
+    sub_counts[(long long)e * d.n_sub + sub] = hist[e];
 }
 
-// One wave per expert column: exclusive prefix over tiles (written
-// tile-major for the align step) and per-source-rank sums (the load
-// matrix), the latter as differences of the prefix at the ranks' first
-// tiles (tiles never cross ranks).
+// One wave per expert column: exclusive prefix over the sub-tiles, written
+// at each 128-token tile's first sub-tile (tile-major, for the align step),
+// and per-source-rank sums (the load matrix) as differences of the prefix at
+// the ranks' first sub-tiles (sub-tiles never cross ranks).
 __global__ __launch_bounds__(256) void k_tile_scan(Dims d, int32_t* __restrict__ work,
                                                    int32_t* __restrict__ counts) {
-  __shared__ int sPre[4][kMaxR + 1];   // per wave: prefix at each rank's first tile, then the total
+  __shared__ int sPre[4][kMaxR + 1];   // per wave: prefix at each rank's first sub-tile, then the total
   const int w = wave_id();
   const int e = blockIdx.x * 4 + w;
   if (e >= d.E) return;
   const int lane = lane_id();
-  const int nt = d.n_tiles, tpr = d.tpr;
-  const int32_t* col = work + (long long)e * nt;
+  const int ns = d.n_sub, spr = d.spr, tpr = d.tpr;
+  const int32_t* col = work + (long long)e * ns;
   int32_t* base = work + work_tile_base(d);
-  const int per = (nt + kWave - 1) / kWave;
-  const int lo = min(nt, lane * per), hi = min(nt, lo + per);
+  const int per = (ns + kWave - 1) / kWave;
+  const int lo = min(ns, lane * per), hi = min(ns, lo + per);
   int local = 0;
   for (int t = lo; t < hi; ++t) local += col[t];
   const int incl = wave_incl_scan(local);
   int run = incl - local;
-  for (int r = lane; r <= d.R; r += kWave) sPre[w][r] = 0;   // ranks without tiles (S = 0) sum to 0
-  for (int t = lo; t < hi; ++t) {
-    if (t % tpr == 0) sPre[w][t / tpr] = run;
-    base[(long long)t * d.E + e] = run;
-    run += col[t];
+  for (int r = lane; r <= d.R; r += kWave) sPre[w][r] = 0;   // ranks without tokens (S = 0) sum to 0
+  if (lo < hi) {
+    int r = lo / spr, j = lo - r * spr;          // rank and sub-tile within it of position t
+    for (int t = lo; t < hi; ++t) {
+      if (j == 0) sPre[w][r] = run;
+      if (j % kSubTiles == 0) base[(long long)(r * tpr + j / kSubTiles) * d.E + e] = run;
+      run += col[t];
+      if (++j == spr) {
+        j = 0;
+        ++r;
+      }
+    }
   }
   if (lane == 0) sPre[w][d.R] = __builtin_amdgcn_readlane(incl, kWave - 1);
   __builtin_amdgcn_wave_barrier();
@@ -78,9 +86,9 @@ __global__ __launch_bounds__(256) void k_tile_scan(Dims d, int32_t* __restrict__
 
 hipError_t launch_route(const Dims& d, const float* logits, const float* bias, int32_t* ids,
                         float* gates, int32_t* work, hipStream_t st) {
-  if (d.n_tiles == 0 || d.S == 0) return hipSuccess;
+  if (d.n_sub == 0) return hipSuccess;
   const int vec = route_vec(logits, d.E);
-  const dim3 grid(d.n_tiles), block(kRouteThreads);
+  const dim3 grid(d.n_sub), block(kRouteThreads);
   const int V = (d.E + kRowLanes - 1) / kRowLanes;
   if (V <= 1) hipLaunchKernelGGL(k_route<1>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
   else if (V <= 2) hipLaunchKernelGGL(k_route<2>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
@@ -94,8 +102,8 @@ hipError_t launch_route(const Dims& d, const float* logits, const float* bias, i
 
 hipError_t launch_histogram(const Dims& d, const int32_t* ids, int32_t* work, int32_t* status,
                             hipStream_t st) {
-  if (d.n_tiles == 0 || d.S == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_histogram, dim3(d.n_tiles), dim3(kTileTokens), 0, st, ids, d, work, status);
+  if (d.n_sub == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_histogram, dim3(d.n_sub), dim3(kHistThreads), 0, st, ids, d, work, status);
   return hipGetLastError();
 }
 
@@ -104,18 +112,18 @@ hipError_t launch_tile_scan(const Dims& d, int32_t* work, int32_t* counts, hipSt
   return hipGetLastError();
 }
 
-// Small batches (1 <= N <= kSmallTokens and n_tiles * E <= kSmallHist): one
-// workgroup routes every token, keeps each tile's histogram in LDS and does
-// the tile scan itself, so route + scan is one launch.  Same outputs as
+// Small batches (1 <= N <= kSmallTokens and n_sub * E <= kSmallHist): one
+// workgroup routes every token, keeps each sub-tile's histogram in LDS and
+// does the scan itself, so route + scan is one launch.  Same outputs as
 // k_route + k_tile_scan.  Measured on MI355X: N = 8 (decode, S = 1) route +
-// scan 12.3 -> 9.9 us; at N = 128 one workgroup is slower than eight tiles in
-// parallel (11.7 -> 20.3 us), so only batches that fit 8 waves in one pass
-// take it.
+// scan 12.3 -> 9.9 us; at N = 128 one workgroup is slower than spreading
+// the tokens over several (11.7 -> 20.3 us), so only batches that fit one
+// pass take it.
 constexpr int kSmallHist = 16384;
-constexpr int kSmallTokens = 32;
+constexpr int kSmallTokens = kRouteTokens;
 
 static bool small_batch(const Dims& d) {
-  return d.N >= 1 && d.N <= kSmallTokens && (long long)d.n_tiles * d.E <= kSmallHist;
+  return d.N >= 1 && d.N <= kSmallTokens && (long long)d.n_sub * d.E <= kSmallHist;
 }
 
 template <int V>
@@ -127,12 +135,12 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_small(const float* __re
                                                                int32_t* __restrict__ work,
                                                                int32_t* __restrict__ counts) {
   __shared__ RouteScratch rs;
-  __shared__ int hist[kSmallHist];     // [tile][E]
-  const int E = d.E, nt = d.n_tiles, S = d.S, tpr = d.tpr;
-  for (int i = threadIdx.x; i < nt * E; i += kRouteThreads) hist[i] = 0;
+  __shared__ int hist[kSmallHist];     // [sub-tile][E]
+  const int E = d.E, ns = d.n_sub, S = d.S, spr = d.spr, tpr = d.tpr;
+  for (int i = threadIdx.x; i < ns * E; i += kRouteThreads) hist[i] = 0;
   route_span<V>(logits, bias, d, vec, 0, d.N, ids, gates, rs, [&](long long t, int id) {
-    const int r = (int)(t / S), j = (int)(t - (long long)r * S) / kTileTokens;
-    atomicAdd(&hist[(r * tpr + j) * E + id], 1);
+    const int r = (int)(t / S), j = (int)(t - (long long)r * S) / kSubTokens;
+    atomicAdd(&hist[(r * spr + j) * E + id], 1);
   });
   __syncthreads();
   int32_t* base = work + work_tile_base(d);
@@ -140,11 +148,11 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_small(const float* __re
     int run = 0;
     for (int r = 0; r < d.R; ++r) {
       int sum = 0;
-      for (int j = 0; j < tpr; ++j) {
-        const int tile = r * tpr + j;
-        const int c = hist[tile * E + e];
-        work[(long long)e * nt + tile] = c;
-        base[(long long)tile * E + e] = run;
+      for (int j = 0; j < spr; ++j) {
+        const int sub = r * spr + j;
+        const int c = hist[sub * E + e];
+        work[(long long)e * ns + sub] = c;
+        if (j % kSubTiles == 0) base[(long long)(r * tpr + j / kSubTiles) * E + e] = run;
         run += c;
         sum += c;
       }

@@ -1,5 +1,5 @@
-// Router top-K over one 128-token tile plus its expert histogram, as a device
-// function (the route kernel is a thin wrapper around it).
+// Router top-K over one 32-token sub-tile plus its expert histogram, as a
+// device function (the route kernel is a thin wrapper around it).
 //
 // Top-K: [AlignSort] -- the MoE layer routes each token to its Top-K experts
 // by gate score (DeepSeek V3/R1 add a per-expert gating bias that penalises
@@ -15,11 +15,17 @@
 
 namespace lbt {
 
-constexpr int kRouteThreads = 1024;
+// One workgroup routes one 32-token sub-tile in a single pass (eight waves
+// of four tokens): small batches spread over as many CUs as they have
+// sub-tiles, and at 32K tokens the chip holds more resident waves than with
+// 128-token workgroups taking two passes.
+constexpr int kRouteThreads = 512;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kRowLanes = 16;                        // lanes per token
 constexpr int kRowsPerWave = kWave / kRowLanes;      // tokens per wave
-constexpr int kRoutePasses = kTileTokens / (kRouteWaves * kRowsPerWave);
+constexpr int kRouteTokens = kRouteWaves * kRowsPerWave;   // tokens per pass
+constexpr int kRoutePasses = kSubTokens / kRouteTokens;
+static_assert(kRoutePasses * kRouteTokens == kSubTokens, "whole passes per sub-tile");
 
 // Order-preserving map of a finite fp32 value to u32; -0.0 maps like +0.0 so
 // the two tie (IEEE equality).  Every finite value maps above 0x007FFFFF.
@@ -147,7 +153,7 @@ struct RouteSmem {
   RouteScratch rs;
 };
 
-// Route tokens [t0, t0 + len), len <= 128, with 1024 threads; for every
+// Route tokens [t0, t0 + len), len <= kSubTokens, with kRouteThreads threads; for every
 // chosen (token, expert) pair call hist_add(t, expert).  Contains one
 // workgroup barrier (after the row loads), so state the caller set up before
 // the call (a zeroed histogram) is visible to hist_add.
@@ -287,24 +293,24 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
   }
 }
 
-// Route the tokens of tile `tile` (1024 threads) and write its expert
-// histogram to tile_counts[e][tile].
+// Route the tokens of sub-tile `sub` (kRouteThreads threads) and write its
+// expert histogram to sub_counts[e][sub].
 template <int V>
-__device__ __forceinline__ void route_tile(const float* __restrict__ logits,
-                                           const float* __restrict__ bias, const Dims& d, int vec,
-                                           int tile, int32_t* __restrict__ ids,
-                                           float* __restrict__ gates,
-                                           int32_t* __restrict__ tile_counts, RouteSmem& sm) {
+__device__ __forceinline__ void route_sub(const float* __restrict__ logits,
+                                          const float* __restrict__ bias, const Dims& d, int vec,
+                                          int sub, int32_t* __restrict__ ids,
+                                          float* __restrict__ gates,
+                                          int32_t* __restrict__ sub_counts, RouteSmem& sm) {
   int* hist = sm.hist;
-  const int r = tile / d.tpr, j = tile - r * d.tpr;
-  const int t0 = r * d.S + j * kTileTokens;
-  const int len = min(kTileTokens, d.S - j * kTileTokens);
+  const int r = sub / d.spr, j = sub - r * d.spr;
+  const int t0 = r * d.S + j * kSubTokens;
+  const int len = min(kSubTokens, d.S - j * kSubTokens);
   for (int e = threadIdx.x; e < d.E; e += kRouteThreads) hist[e] = 0;
   route_span<V>(logits, bias, d, vec, t0, len, ids, gates, sm.rs,
                 [&](long long, int id) { atomicAdd(&hist[id], 1); });
   __syncthreads();
   for (int e = threadIdx.x; e < d.E; e += kRouteThreads)
-    tile_counts[(long long)e * d.n_tiles + tile] = hist[e];
+    sub_counts[(long long)e * d.n_sub + sub] = hist[e];
 }
 
 // Widest aligned logit load (floats) for rows of E floats starting at p.

@@ -38,7 +38,8 @@ def test_sizes_match_oracle_capacity_for_every_workload():
         nh = w.E // w.R
         assert z["max_seg"] == nh + min(w.E - nh, w.SK)
         assert z["n_tiles"] == w.R * -(-w.S // z["tile_tokens"])
-        assert z["work_words"] == 2 * w.E * z["n_tiles"]
+        # per-expert counts of every 32-token sub-tile, then a prefix per tile
+        assert z["work_words"] == w.E * (w.R * -(-w.S // 32) + z["n_tiles"])
         # offsets are increasing and the blob ends at plan_words
         offs = [z[k] for k in binding._SIZE_FIELDS if k.startswith("off_")]
         assert offs == sorted(offs) and offs[-1] < z["plan_words"]

@@ -74,7 +74,9 @@ int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z) {
   if (d != nullptr) {
     d->E = (int)E; d->K = (int)K; d->R = (int)R; d->S = (int)S; d->H = (int)H; d->B = (int)B;
     d->blk = (int)blk; d->score_fn = s->score_fn; d->renorm = s->renorm;
-    d->nh = (int)nh; d->N = (int)N; d->P = P; d->SK = (int)SK; d->tau_max = (int)tmax; d->C = (int)C;
+    d->nh = (int)nh;
+    d->nh_magic = nh >= 2 ? (uint32_t)(((1ULL << 32) + nh - 1) / nh) : 0u;
+    d->N = (int)N; d->P = P; d->SK = (int)SK; d->tau_max = (int)tmax; d->C = (int)C;
     d->n_blocks = (int)(C / blk); d->tpr = (int)tpr; d->n_tiles = (int)nt;
     d->spr = (int)spr; d->n_sub = (int)(R * spr); d->pl = pl;
   }

@@ -32,6 +32,7 @@ struct PlanLayout {
 struct Dims {
   int E, K, R, S, H, B, blk, score_fn, renorm;
   int nh;        // E / R home experts per rank
+  uint32_t nh_magic;   // ceil(2^32 / nh) for nh >= 2: e / nh = umulhi(e, nh_magic) for e < 2^16
   int N;         // R * S tokens
   long long P;   // N * K pairs
   int SK;        // S * K
@@ -87,6 +88,12 @@ __host__ __device__ inline long long work_tile_base(const Dims& d) {
 
 // ---- device helpers -------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// e / nh for 0 <= e < 2^16 by one multiply-high (exact there: the rounding
+// error of the multiplier is below nh, so e times it stays below 2^32).
+__device__ __forceinline__ int div_nh(int e, const Dims& d) {
+  return d.nh == 1 ? e : (int)__umulhi((uint32_t)e, d.nh_magic);
+}
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 
 __device__ __forceinline__ int wave_incl_scan(int x) {

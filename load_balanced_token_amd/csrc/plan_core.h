@@ -41,7 +41,11 @@ constexpr int kPlanThreads = 1024;
 constexpr int kLinearDeficits = 32;
 constexpr int kDirectCompares = 64;
 
-__device__ __forceinline__ int pad_to(int c, int blk) { return ((c + blk - 1) / blk) * blk; }
+// c rounded up to a multiple of blk (a mask when blk is a power of two).
+__device__ __forceinline__ int pad_to(int c, int blk) {
+  if ((blk & (blk - 1)) == 0) return (c + blk - 1) & -blk;
+  return ((c + blk - 1) / blk) * blk;
+}
 
 // LDS of the plan.  The arrays scanned by one wave hold 64*CMAX + 1 ints
 // (CMAX chunks per lane) and start on 16 bytes.
@@ -165,6 +169,60 @@ __device__ __forceinline__ void count_pieces(PlanSmem& m, const int E, const int
   }
 }
 
+// Per expert (NQ per lane, e = lane + 64 i): the home keep h_e into sH and
+// the overflow o_e into sO at its line position, from the exclusive prefix
+// of T (sX) -- the fixed rule keeps the first tau pairs of the rank's home
+// stream, the quota rule sheds L_r - tau from the hottest experts first:
+// o_e = clamp(L_r - tau - HP_e, 0, T_e) with HP_e the load of the experts
+// hotter than e in its rank.  Loads are unconditional (clamped index) so the
+// unrolled iterations overlap; stores are guarded.
+template <int NQ, bool HOT>
+__device__ __forceinline__ void keep_and_overflow(PlanSmem& m, const Dims& d, const int tau,
+                                                  const bool consistent, const int lane,
+                                                  int& maxT, int& nOverE) {
+  const int E = d.E, nh = d.nh;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int e = lane + i * kWave;
+    const bool in = e < E;
+    const int ec = in ? e : 0;
+    const int r0 = div_nh(ec, d) * nh;      // first expert of e's rank
+    const int T = m.sT[ec];
+    int h;
+    if (HOT) {
+      const int L = m.sX[r0 + nh] - m.sX[r0];
+      const int HP = m.sHx[m.sLam[ec]] - m.sHx[r0];
+      h = T - min(max(L - tau - HP, 0), T);
+    } else {
+      const int Pe = m.sX[ec] - m.sX[r0];    // position in the rank's home stream
+      h = min(max(tau - Pe, 0), T);
+    }
+    if (!consistent) h = 0;
+    if (in) {
+      m.sH[e] = h;
+      m.sO[HOT ? m.sLam[e] : e] = consistent ? T - h : 0;
+      maxT = max(maxT, T);
+      nOverE += (consistent && T - h > 0);
+    }
+  }
+}
+
+// The padded home-segment lengths into the flat segment list: rank r's
+// entries start at r*nh + (replicas of earlier ranks), home experts first.
+template <int NQ>
+__device__ __forceinline__ void home_lengths(PlanSmem& m, const Dims& d, const int lane) {
+  const int E = d.E, nh = d.nh;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int e = lane + i * kWave;
+    const int ec = e < E ? e : 0;
+    const int r = div_nh(ec, d);
+    const int len = pad_to(m.sH[ec], d.blk);
+    const int at = r * nh + m.sRep[r] + (ec - r * nh);
+    if (e < E) m.sF[at] = len;
+  }
+}
+
 // The plan from T_e (in m.sT and m.sX, written and made visible by a
 // workgroup barrier before the call; for HOT also m.sLam, m.sPerm and m.sHx
 // = exclusive prefix of the loads in line order) at threshold tau; 1024
@@ -195,48 +253,60 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
     const int Ptot = wave_excl_scan_lds<kMaxE / kWave>(sX, E);
     const bool consistent = (long long)Ptot == (long long)R * SK;
     int maxT = 0, nOverE = 0;
-    for (int e = lane; e < E; e += kWave) {
-      const int r = e / nh;
-      const int T = sT[e];
-      int h;
-      if (HOT) {
-        // shed L_r - tau from the hottest experts: o_e = clamp(L_r - tau - HP_e, 0, T_e)
-        // with HP_e the load of the experts hotter than e in its rank
-        const int L = sX[(r + 1) * nh] - sX[r * nh];
-        const int HP = sHx[sLam[e]] - sHx[r * nh];
-        h = T - min(max(L - tau - HP, 0), T);
-      } else {
-        const int Pe = sX[e] - sX[r * nh];      // position in r's home stream
-        h = min(max(tau - Pe, 0), T);
-      }
-      if (!consistent) h = 0;
-      sH[e] = h;
-      sO[lam(e)] = consistent ? T - h : 0;
-      maxT = max(maxT, T);
-      nOverE += (consistent && T - h > 0);
-    }
+    if (E <= 4 * kWave) keep_and_overflow<4, HOT>(m, d, tau, consistent, lane, maxT, nOverE);
+    else keep_and_overflow<kMaxE / kWave, HOT>(m, d, tau, consistent, lane, maxT, nOverE);
     int maxL = 0, nOverR = 0;
-    for (int r = lane; r < R; r += kWave) {
-      const int L = sX[(r + 1) * nh] - sX[r * nh];
-      const int def = consistent ? tau - min(L, tau) : 0;
-      sL[r] = L;
-      sDef[r] = def;
-      sD[r] = def;
-      sCidx[r] = def > 0;
-      sRep[r] = 0;
-      maxL = max(maxL, L);
-      nOverR += (L > tau);
+    if (R <= kWave) {
+      // lane r holds rank r: the deficit prefix D and the compact deficit
+      // index come straight from register scans
+      const int r = lane;
+      const int rc = r < R ? r : 0;
+      const int L = r < R ? sX[(rc + 1) * nh] - sX[rc * nh] : 0;
+      const int def = (r < R && consistent) ? tau - min(L, tau) : 0;
+      const int has = def > 0;
+      const int d_in = wave_incl_scan_dpp(def), c_in = wave_incl_scan_dpp(has);
+      const int d_tot = __builtin_amdgcn_readlane(d_in, kWave - 1);
+      const int c_tot = __builtin_amdgcn_readlane(c_in, kWave - 1);
+      if (r < R) {
+        sL[r] = L;
+        sDef[r] = def;
+        sD[r] = d_in - def;
+        sCidx[r] = c_in - has;
+        sRep[r] = 0;
+      }
+      if (r == 0) {
+        sD[R] = d_tot;
+        sCidx[R] = c_tot;
+      }
+      if (has) {
+        sDl[c_in - 1] = r;
+        sDc[c_in - 1] = d_in - def;
+      }
+      maxL = L;
+      nOverR = r < R && L > tau;
+    } else {
+      for (int r = lane; r < R; r += kWave) {
+        const int L = sX[(r + 1) * nh] - sX[r * nh];
+        const int def = consistent ? tau - min(L, tau) : 0;
+        sL[r] = L;
+        sDef[r] = def;
+        sD[r] = def;
+        sCidx[r] = def > 0;
+        sRep[r] = 0;
+        maxL = max(maxL, L);
+        nOverR += (L > tau);
+      }
+      __builtin_amdgcn_wave_barrier();
+      wave_excl_scan_lds<kMaxR / kWave>(sD, R);
+      wave_excl_scan_lds<kMaxR / kWave>(sCidx, R);
+      for (int r = lane; r < R; r += kWave)
+        if (sDef[r] > 0) {
+          sDl[sCidx[r]] = r;
+          sDc[sCidx[r]] = sD[r];
+        }
     }
     __builtin_amdgcn_wave_barrier();
     const int totOv = wave_excl_scan_lds<kMaxE / kWave>(sO, E);
-    wave_excl_scan_lds<kMaxR / kWave>(sD, R);
-    wave_excl_scan_lds<kMaxR / kWave>(sCidx, R);
-    for (int r = lane; r < R; r += kWave)
-      if (sDef[r] > 0) {
-        sDl[sCidx[r]] = r;
-        sDc[sCidx[r]] = sD[r];
-      }
-    __builtin_amdgcn_wave_barrier();
     const int nDef = sCidx[R];
     if (E <= 4 * kWave) count_pieces<4, HOT>(m, E, nDef, consistent, lane);
     else count_pieces<kMaxE / kWave, HOT>(m, E, nDef, consistent, lane);
@@ -266,10 +336,8 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
       sPj[g] = jj;
       sF[dd * nh + sRep[dd] + nh + jj] = pad_to(sPc[g], blk);
     }
-    for (int e = lane; e < E; e += kWave) {
-      const int r = e / nh;
-      sF[r * nh + sRep[r] + (e - r * nh)] = pad_to(sH[e], blk);
-    }
+    if (E <= 4 * kWave) home_lengths<4>(m, d, lane);
+    else home_lengths<kMaxE / kWave>(m, d, lane);
     __builtin_amdgcn_wave_barrier();
     wave_excl_scan_lds<(kMaxE + kMaxPieces) / kWave>(sF, E + nP);
     // wave-wide reductions of the statistics
@@ -329,7 +397,7 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
 
   // 3. every wave: write the blob from LDS
   for (int e = tid; e < E; e += kPlanThreads) {
-    const int r = e / nh;
+    const int r = div_nh(e, d);
     const int fb = r * nh + sRep[r];
     P[pl.T + e] = sT[e];
     P[pl.h + e] = sH[e];

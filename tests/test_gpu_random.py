@@ -129,3 +129,21 @@ def test_small_batches(seed):
     gu.check_plan(res["plan_fields"], ref["plan"], w.P)
     gu.check_align(res, ref, w.R, res["sizes"]["C"])
     _full_move_check(w, res, ref, activations(w, 0))
+
+
+@pytest.mark.parametrize("planner", ["fixed", "quota"])
+@pytest.mark.parametrize("blk", [3, 12, 96])
+def test_block_sizes_not_powers_of_two(blk, planner):
+    """Alignment blocks that are not powers of two (segment padding by
+    division rather than by mask), DSV3 routing at S = 100."""
+    from workloads import router_logits
+    w = WORKLOADS["dsv3"].with_(S=100, H=64, blk=blk, B=4)
+    tau_max = 2 * w.SK if planner == "quota" else 0
+    print(f"[random] blk={blk} {planner}", flush=True)
+    logits = router_logits(w, 0)
+    res = gu.run_front(gu.shape_of(w, tau_max=tau_max), logits, planner=planner)
+    ref = gu.run_oracle(w, logits, planner=planner, tau_max=tau_max)
+    gu.check_route(res, ref)
+    gu.check_plan(res["plan_fields"], ref["plan"], w.P)
+    gu.check_align(res, ref, w.R, res["sizes"]["C"])
+    _full_move_check(w, res, ref, activations(w, 0))

@@ -160,10 +160,10 @@ def decode_latency(path, buf, w, x, n_steps, dev, planner="fixed"):
     whole step (route -> plan -> align -> dispatch -> combine) and for the
     step without the combine.
 
-    Every routing is resident in HBM; each variant is captured once in a HIP
-    graph whose first node gathers routing number ``idx`` (a device counter
-    the graph advances), so each replay runs on new router logits with no
-    host work in between."""
+    Every routing is resident in HBM before timing starts.  Step i is
+    captured as its own HIP graph, bound to routing i where it lies, and the
+    graphs are replayed in order: each replay runs the path on new router
+    logits with no gather, copy or host work inside the timed region."""
     import numpy as np
     import torch
     from workloads import router_logits
@@ -171,51 +171,44 @@ def decode_latency(path, buf, w, x, n_steps, dev, planner="fixed"):
     all_logits = torch.empty((n_steps, w.N, w.E), dtype=torch.float32, device=dev)
     for i in range(n_steps):
         all_logits[i] = torch.from_numpy(router_logits(w, i)).to(dev)
-    idx = torch.zeros(1, dtype=torch.int64, device=dev)
-    cur = torch.empty((1, w.N, w.E), dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     plan_fn = path.plan_balance if planner == "fixed" else path.plan_quota
 
-    def full():
-        torch.index_select(all_logits, 0, idx, out=cur)
-        path.step(cur[0], x, buf, planner=planner)
-        idx.add_(1)
+    def full(i):
+        path.step(all_logits[i], x, buf, planner=planner)
 
-    def no_combine():
-        torch.index_select(all_logits, 0, idx, out=cur)
-        path.route_topk(cur[0], buf["ids"], buf["gates"], buf["counts"], buf["work"])
+    def no_combine(i):
+        path.route_topk(all_logits[i], buf["ids"], buf["gates"], buf["counts"], buf["work"])
         plan_fn(buf["counts"], buf["plan"], buf["status"])
         path.align_sort(buf["ids"], buf["work"], buf["plan"], buf["slot"], buf["sorted_ids"],
                         buf["block_wrow"], buf["block_expert"], buf["status"])
         path.dispatch(x, buf["slot"], buf["recv"])
-        idx.add_(1)
 
     def replay(body):
-        # routing numbers 0, 1, 2 for the warm-up, then 0 .. n_steps - 1 for
-        # the replays: the counter starts from zero for every variant
-        assert n_steps >= 3
-        idx.zero_()
-        with torch.cuda.stream(stream):        # warm up outside the graph
-            for _ in range(3):
-                body()
+        with torch.cuda.stream(stream):        # warm up outside the graphs
+            for i in range(min(3, n_steps)):
+                body(i)
         torch.cuda.current_stream().wait_stream(stream)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            body()
-        idx.zero_()
+        graphs = []
+        for i in range(n_steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                body(i)
+            graphs.append(g)
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(n_steps)]
         t0 = time.perf_counter()
-        for a, b in evs:
+        for (a, b), g in zip(evs, graphs):
             a.record()
             g.replay()
             b.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         lat = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        del graphs
         # the last replay's routing, checked for a clean status
         return lat, wall, int(buf["status"].item())
 
@@ -225,7 +218,7 @@ def decode_latency(path, buf, w, x, n_steps, dev, planner="fixed"):
             "mean_us": float(lat.mean()), "steps": n_steps, "wall_s": wall, "status": status,
             "without_combine": {"p50_us": float(np.percentile(lat_nc, 50)),
                                 "p99_us": float(np.percentile(lat_nc, 99)), "status": st_nc},
-            "note": "graph replay incl. the gather of fresh router logits"}
+            "note": "one HIP graph per step, each on its own resident routing"}
 
 
 def planner_report(lbt, torch, w, counts, B, tau_max, dev, ids=None, work=None):

@@ -48,7 +48,11 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(const int32_t* __res
 // One wave per expert column: exclusive prefix over the sub-tiles, written
 // at each 128-token tile's first sub-tile (tile-major, for the align step),
 // and per-source-rank sums (the load matrix) as differences of the prefix at
-// the ranks' first sub-tiles (sub-tiles never cross ranks).
+// the ranks' first sub-tiles (sub-tiles never cross ranks).  The column is
+// read in coalesced 64-wide chunks, kScanBatch chunks in flight per batch;
+// each chunk is scanned across the wave and carried into the next.
+constexpr int kScanBatch = 4;
+
 __global__ __launch_bounds__(256) void k_tile_scan(Dims d, int32_t* __restrict__ work,
                                                    int32_t* __restrict__ counts) {
   __shared__ int sPre[4][kMaxR + 1];   // per wave: prefix at each rank's first sub-tile, then the total
@@ -56,32 +60,43 @@ __global__ __launch_bounds__(256) void k_tile_scan(Dims d, int32_t* __restrict__
   const int e = blockIdx.x * 4 + w;
   if (e >= d.E) return;
   const int lane = lane_id();
-  const int ns = d.n_sub, spr = d.spr, tpr = d.tpr;
+  const int ns = d.n_sub, spr = d.spr, tpr = d.tpr, E = d.E;
   const int32_t* col = work + (long long)e * ns;
   int32_t* base = work + work_tile_base(d);
-  const int per = (ns + kWave - 1) / kWave;
-  const int lo = min(ns, lane * per), hi = min(ns, lo + per);
-  int local = 0;
-  for (int t = lo; t < hi; ++t) local += col[t];
-  const int incl = wave_incl_scan(local);
-  int run = incl - local;
   for (int r = lane; r <= d.R; r += kWave) sPre[w][r] = 0;   // ranks without tokens (S = 0) sum to 0
-  if (lo < hi) {
-    int r = lo / spr, j = lo - r * spr;          // rank and sub-tile within it of position t
-    for (int t = lo; t < hi; ++t) {
-      if (j == 0) sPre[w][r] = run;
-      if (j % kSubTiles == 0) base[(long long)(r * tpr + j / kSubTiles) * d.E + e] = run;
-      run += col[t];
-      if (++j == spr) {
-        j = 0;
-        ++r;
+  __builtin_amdgcn_wave_barrier();
+  // rank and sub-tile within it of this lane's current element, advanced by 64 per chunk
+  int r = spr > 0 ? lane / spr : 0, j = spr > 0 ? lane - r * spr : 0;
+  int carry = 0;
+  for (int c0 = 0; c0 < ns; c0 += kScanBatch * kWave) {
+    int v[kScanBatch];
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      const int i = c0 + u * kWave + lane;
+      v[u] = i < ns ? col[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      const int i = c0 + u * kWave + lane;
+      const int incl = wave_incl_scan_dpp(v[u]);
+      const int excl = carry + incl - v[u];
+      if (i < ns) {
+        if (j == 0) sPre[w][r] = excl;
+        if (j % kSubTiles == 0) base[(long long)(r * tpr + j / kSubTiles) * E + e] = excl;
+      }
+      carry += __builtin_amdgcn_readlane(incl, kWave - 1);
+      j += kWave;
+      if (j >= spr) {                  // crossed into a later rank (spr > 0 here)
+        const int q = j / spr;
+        r += q;
+        j -= q * spr;
       }
     }
   }
-  if (lane == 0) sPre[w][d.R] = __builtin_amdgcn_readlane(incl, kWave - 1);
+  if (lane == 0) sPre[w][d.R] = carry;
   __builtin_amdgcn_wave_barrier();
-  for (int r = lane; r < d.R; r += kWave)
-    counts[(long long)r * d.E + e] = sPre[w][r + 1] - sPre[w][r];
+  for (int rr = lane; rr < d.R; rr += kWave)
+    counts[(long long)rr * E + e] = sPre[w][rr + 1] - sPre[w][rr];
 }
 
 hipError_t launch_route(const Dims& d, const float* logits, const float* bias, int32_t* ids,

@@ -13,7 +13,7 @@ from tests import gpu_util as gu
 from tests.test_gpu_parity import _full_move_check
 
 pytestmark = pytest.mark.gpu
-N_CASES = 120
+N_CASES = 600
 
 
 @pytest.fixture(scope="module", autouse=True)

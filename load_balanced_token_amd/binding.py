@@ -79,6 +79,12 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise LbtError(f"{LIB_PATH} is missing: build it with "
                            "`python -m load_balanced_token_amd.build`")
+        # torch first: it ships its own HIP runtime under the soname the
+        # library links against, so loading torch before the library makes
+        # both use that one runtime.  Loaded the other way round, the library
+        # would bind to the system runtime and torch would load a second
+        # copy, whose streams and memory the library's launches cannot use.
+        _torch()
         L = ctypes.CDLL(LIB_PATH)
         P = ctypes.c_void_p
         I = ctypes.c_int

@@ -131,3 +131,23 @@ def test_binding_structs_follow_the_header():
     for name, val in re.findall(r"#define LBT_HDR_(\w+) (\d+)", h):
         if name != "WORDS":
             assert getattr(b, "HDR_" + name) == int(val), name
+
+
+def test_one_hip_runtime_when_the_library_loads_before_torch():
+    """Loading the library first (a size query before any torch call) must
+    still leave a single HIP runtime in the process: torch's, which the
+    library then shares (two copies would make every launch on a torch
+    stream fail)."""
+    import subprocess
+    import sys
+    code = (
+        "import load_balanced_token_amd as lbt\n"
+        "lbt.query_sizes(lbt.Shape(E=8, K=2, R=4, S=8, H=64, B=1, blk=16))\n"
+        "import torch\n"
+        "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+        "print(len(paths), sorted(paths))\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr
+    n = int(r.stdout.split()[0])
+    assert n == 1, r.stdout

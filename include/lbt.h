@@ -321,6 +321,11 @@ int lbt_dispatch_bwd(const lbt_shape* s, const uint16_t* d_recv, const int32_t* 
 /* Text for a return code. */
 const char* lbt_strerror(int code);
 
+/* Name of the HIP error behind the calling thread's most recent LBT_EHIP
+ * (for example "hipErrorInvalidHandle"), or "hipSuccess" if that thread has
+ * had none.  The string is static; the call launches nothing. */
+const char* lbt_last_hip_error(void);
+
 /* LBT_VERSION of the built library. */
 int lbt_version(void);
 

@@ -18,6 +18,11 @@ SIGMOID = 1
 Y_F32 = 0
 Y_BF16 = 1
 
+OK = 0                   # return codes (LBT_OK, LBT_E*)
+EINVAL = -1
+EHIP = -2
+EUNSUPPORTED = -3
+
 ST_BADCOUNT = 1
 ST_CAPACITY = 2
 ST_BADID = 4
@@ -42,7 +47,7 @@ HDR_LOCAL = 12
 EXPORTS = ("lbt_query_sizes", "lbt_route_topk", "lbt_histogram", "lbt_plan_balance",
            "lbt_plan_quota", "lbt_align_sort", "lbt_dispatch", "lbt_combine",
            "lbt_prefetch_weights", "lbt_reduce_grad", "lbt_combine_bwd", "lbt_dispatch_bwd",
-           "lbt_strerror", "lbt_version")
+           "lbt_strerror", "lbt_last_hip_error", "lbt_version")
 
 
 class LbtShape(ctypes.Structure):
@@ -103,9 +108,11 @@ def lib() -> ctypes.CDLL:
         L.lbt_dispatch_bwd.argtypes = [SP, P, P, ctypes.c_int32, P, P]
         L.lbt_strerror.argtypes = [I]
         L.lbt_strerror.restype = ctypes.c_char_p
+        L.lbt_last_hip_error.argtypes = []
+        L.lbt_last_hip_error.restype = ctypes.c_char_p
         L.lbt_version.argtypes = []
         for n in EXPORTS:
-            if n != "lbt_strerror":
+            if n not in ("lbt_strerror", "lbt_last_hip_error"):
                 getattr(L, n).restype = I
         if L.lbt_version() != ABI_VERSION:
             raise LbtError(f"{LIB_PATH} is ABI version {L.lbt_version()}, this binding expects "
@@ -116,7 +123,10 @@ def lib() -> ctypes.CDLL:
 
 def _check(rc: int, what: str) -> None:
     if rc != 0:
-        raise LbtError(f"{what}: {lib().lbt_strerror(rc).decode()} (code {rc})")
+        msg = f"{what}: {lib().lbt_strerror(rc).decode()} (code {rc}"
+        if rc == EHIP:
+            msg += f", {lib().lbt_last_hip_error().decode()}"
+        raise LbtError(msg + ")")
 
 
 @dataclasses.dataclass(frozen=True)

@@ -102,7 +102,14 @@ int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z) {
   return LBT_OK;
 }
 
-static int hip_rc(hipError_t e) { return e == hipSuccess ? LBT_OK : LBT_EHIP; }
+// The HIP error behind this thread's most recent LBT_EHIP.
+static thread_local hipError_t g_last_hip_error = hipSuccess;
+
+static int hip_rc(hipError_t e) {
+  if (e == hipSuccess) return LBT_OK;
+  g_last_hip_error = e;
+  return LBT_EHIP;
+}
 
 }  // namespace lbt
 
@@ -111,6 +118,8 @@ using namespace lbt;
 extern "C" {
 
 int lbt_version(void) { return LBT_VERSION; }
+
+const char* lbt_last_hip_error(void) { return hipGetErrorName(g_last_hip_error); }
 
 const char* lbt_strerror(int code) {
   switch (code) {

@@ -37,7 +37,8 @@
   do {                                                                           \
     int r_ = (call);                                                             \
     if (r_ != LBT_OK) {                                                          \
-      fprintf(stderr, "%s failed: %s\n", #call, lbt_strerror(r_));               \
+      fprintf(stderr, "%s failed: %s%s%s\n", #call, lbt_strerror(r_),             \
+              r_ == LBT_EHIP ? ", " : "", r_ == LBT_EHIP ? lbt_last_hip_error() : ""); \
       return 3;                                                                  \
     }                                                                            \
   } while (0)

@@ -131,6 +131,20 @@ def test_binding_structs_follow_the_header():
     for name, val in re.findall(r"#define LBT_HDR_(\w+) (\d+)", h):
         if name != "WORDS":
             assert getattr(b, "HDR_" + name) == int(val), name
+    codes = dict(re.findall(r"#define LBT_(OK|E[A-Z]+) \(?(-?\d+)\)?", h))
+    assert codes and {k: int(v) for k, v in codes.items()} == \
+        {k: getattr(b, k) for k in codes}
+
+
+def test_last_hip_error_starts_clean():
+    """Before any failed launch the calling thread's HIP error is hipSuccess
+    (a string lookup: no device needed)."""
+    import threading
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(lbt.lib().lbt_last_hip_error().decode()))
+    t.start()
+    t.join()
+    assert seen == ["hipSuccess"]
 
 
 def test_one_hip_runtime_when_the_library_loads_before_torch():

@@ -96,65 +96,10 @@ __device__ __forceinline__ int div_nh(int e, const Dims& d) {
 }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
-
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
-  return x;
-}
-
 __device__ __forceinline__ int wave_max(int x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, kWave));
   return x;
-}
-
-// In-place exclusive prefix sum of arr[0..n) in LDS by the whole workgroup
-// (blockDim.x = NT threads, n <= IPT * NT); arr[n] receives the total, which
-// is also returned.  tmp needs NT/64 + 1 ints.  Contains barriers: every
-// thread of the workgroup must call it.
-template <int NT, int IPT>
-__device__ int block_excl_scan(int* arr, int n, int* tmp) {
-  constexpr int NW = NT / kWave;
-  const int tid = threadIdx.x;
-  int v[IPT];
-  int local = 0;
-#pragma unroll
-  for (int i = 0; i < IPT; ++i) {
-    const int idx = tid * IPT + i;
-    v[i] = idx < n ? arr[idx] : 0;
-    local += v[i];
-  }
-  const int incl = wave_incl_scan(local);
-  if (lane_id() == kWave - 1) tmp[wave_id()] = incl;
-  __syncthreads();
-  if (tid < kWave) {
-    const int w = tid < NW ? tmp[tid] : 0;
-    const int wi = wave_incl_scan(w);
-    if (tid < NW) tmp[tid] = wi - w;
-    if (tid == NW - 1) tmp[NW] = wi;
-  }
-  __syncthreads();
-  int run = incl - local + tmp[wave_id()];
-  const int total = tmp[NW];
-#pragma unroll
-  for (int i = 0; i < IPT; ++i) {
-    const int idx = tid * IPT + i;
-    if (idx < n) arr[idx] = run;
-    run += v[i];
-  }
-  if (tid == 0) arr[n] = total;
-  __syncthreads();
-  return total;
 }
 
 // Inclusive prefix sum across a wave64 with DPP: Hillis-Steele steps inside

@@ -24,10 +24,11 @@
 namespace lbt {
 
 // T_e = column sums of the load matrix into sT and sX (all threads of the
-// workgroup; eight independent loads in flight per thread).
+// workgroup; eight independent loads in flight per thread); with sCnt, the
+// matrix itself is kept in LDS too.
 template <int NT>
 __device__ __forceinline__ void column_sums(const int32_t* __restrict__ counts, int E, int R,
-                                            int* sT, int* sX) {
+                                            int* sT, int* sX, int* sCnt = nullptr) {
   for (int e = threadIdx.x; e < E; e += NT) {
     int s = 0;
     for (int r0 = 0; r0 < R; r0 += 8) {
@@ -35,7 +36,10 @@ __device__ __forceinline__ void column_sums(const int32_t* __restrict__ counts, 
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = r0 + i < R ? counts[(long long)(r0 + i) * E + e] : 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s += v[i];
+      for (int i = 0; i < 8; ++i) {
+        s += v[i];
+        if (sCnt != nullptr && r0 + i < R) sCnt[(r0 + i) * E + e] = v[i];
+      }
     }
     sT[e] = s;
     if (sX != nullptr) sX[e] = s;
@@ -44,8 +48,8 @@ __device__ __forceinline__ void column_sums(const int32_t* __restrict__ counts, 
 
 // Position of expert e in its rank's shedding order: load descending, ties
 // to the lower index.
-__device__ __forceinline__ int hot_position(const int* sT, int e, int nh) {
-  const int r0 = (e / nh) * nh, T = sT[e];
+__device__ __forceinline__ int hot_position(const int* sT, int e, const Dims& d) {
+  const int nh = d.nh, r0 = div_nh(e, d) * nh, T = sT[e];
   int pos = 0;
 #pragma unroll 8
   for (int x = r0; x < r0 + nh; ++x) {
@@ -62,7 +66,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict
   if (threadIdx.x < 12) m.sStat[threadIdx.x] = 0;
   column_sums<kPlanThreads>(counts, d.E, d.R, m.sT, m.sX);
   __syncthreads();
-  plan_core<false>(d, m, d.SK, counts, plan, status);
+  plan_core<false>(d, m, d.SK, counts, nullptr, plan, status);
 }
 
 // ---- quota plan ---------------------------------------------------------------
@@ -156,29 +160,36 @@ __device__ __forceinline__ bool tau_fits_wave(int tau, const int* sQ, const int*
   return !bad;
 }
 
+// The quota plan keeps the load matrix in LDS when it has at most this many
+// entries (DSV3, MoonEP and decode shapes), so the locality counts of the
+// blob come from LDS instead of dependent global loads.
+constexpr int kQuotaCountsLds = 4096;
+
 __global__ __launch_bounds__(kPlanThreads) void k_plan_quota(const int32_t* __restrict__ counts,
                                                             Dims d, int32_t* __restrict__ plan,
                                                             int32_t* __restrict__ status) {
   __shared__ PlanSmem m;
   __shared__ int sQ[kMaxE];     // per-rank inclusive prefix of the loads in shedding order
   __shared__ int sLr[kMaxR];    // L_r
-  __shared__ int sTmp[kPlanThreads / kWave + 1];
+  __shared__ int sCnt[kQuotaCountsLds];   // the load matrix, when it fits
   __shared__ int sOvOff[kPlanThreads / kWave][kWave + 1];   // per-wave scratch of the first stage
   __shared__ int sNvOff[kPlanThreads / kWave][kWave + 1];
   const int E = d.E, R = d.R, nh = d.nh, tid = threadIdx.x;
   // [10]: smallest qualifying tau, [11]: max_r L_r
   if (tid < 12) m.sStat[tid] = tid == 10 ? INT_MAX : 0;
-  column_sums<kPlanThreads>(counts, E, R, m.sT, m.sX);
+  const bool keep = (long long)R * E <= kQuotaCountsLds;
+  column_sums<kPlanThreads>(counts, E, R, m.sT, m.sX, keep ? sCnt : nullptr);
   __syncthreads();
   for (int e = tid; e < E; e += kPlanThreads) {
-    const int g = (e / nh) * nh + hot_position(m.sT, e, nh);
+    const int g = div_nh(e, d) * nh + hot_position(m.sT, e, d);
     m.sLam[e] = g;
     m.sPerm[g] = e;
     m.sHx[g] = m.sT[e];
   }
   __syncthreads();
-  block_excl_scan<kPlanThreads, kMaxE / kPlanThreads + 1>(m.sHx, E, sTmp);
-  for (int g = tid; g < E; g += kPlanThreads) sQ[g] = m.sHx[g + 1] - m.sHx[(g / nh) * nh];
+  if (wave_id() == 0) wave_excl_scan_lds<kMaxE / kWave>(m.sHx, E);
+  __syncthreads();
+  for (int g = tid; g < E; g += kPlanThreads) sQ[g] = m.sHx[g + 1] - m.sHx[div_nh(g, d) * nh];
   int maxL = 0;
   for (int r = tid; r < R; r += kPlanThreads) {
     sLr[r] = m.sHx[(r + 1) * nh] - m.sHx[r * nh];
@@ -214,7 +225,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_quota(const int32_t* __re
     if (found != INT_MAX) break;
   }
   const int tau = m.sStat[10] == INT_MAX ? d.tau_max : m.sStat[10];
-  plan_core<true>(d, m, tau, counts, plan, status);
+  plan_core<true>(d, m, tau, counts, keep ? sCnt : nullptr, plan, status);
 }
 
 hipError_t launch_plan(const Dims& d, const int32_t* counts, int32_t* plan, int32_t* status,

@@ -69,7 +69,7 @@ struct PlanSmem {
   alignas(16) int sF[kMaxE + kMaxPieces + 1];  // flat segment padded lengths -> starts
   int sLam[kMaxE];                      // quota rule: line position of expert e inside its rank block
   int sPerm[kMaxE];                     // quota rule: expert at line position
-  int sHx[kMaxE + 1];                   // quota rule: loads in line order, then exclusive prefix
+  alignas(16) int sHx[kMaxE + 1];       // quota rule: loads in line order, then exclusive prefix
   // max_T, max_L, over ranks, over experts, status, nP, totOv, Ptot, tau, max replicas
   int sStat[12];
 };
@@ -226,12 +226,16 @@ __device__ __forceinline__ void home_lengths(PlanSmem& m, const Dims& d, const i
 // The plan from T_e (in m.sT and m.sX, written and made visible by a
 // workgroup barrier before the call; for HOT also m.sLam, m.sPerm and m.sHx
 // = exclusive prefix of the loads in line order) at threshold tau; 1024
-// threads; writes the whole blob and *status.
+// threads; writes the whole blob and *status.  The locality counts (HOT)
+// read the load matrix from sCnt when given (an LDS copy), else from counts.
 template <bool HOT>
 __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int tau,
                                           const int32_t* __restrict__ counts,
-                                          int32_t* __restrict__ plan,
+                                          const int* sCnt, int32_t* __restrict__ plan,
                                           int32_t* __restrict__ status) {
+  auto count_of = [&](int r, int e) {
+    return sCnt != nullptr ? sCnt[r * d.E + e] : counts[(long long)r * d.E + e];
+  };
   auto& sT = m.sT; auto& sX = m.sX; auto& sH = m.sH; auto& sO = m.sO; auto& sNp = m.sNp;
   auto& sDlo = m.sDlo; auto& sL = m.sL; auto& sDef = m.sDef; auto& sD = m.sD;
   auto& sCidx = m.sCidx; auto& sDl = m.sDl; auto& sDc = m.sDc; auto& sRep = m.sRep;
@@ -402,7 +406,7 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
     P[pl.T + e] = sT[e];
     P[pl.h + e] = sH[e];
     // quota rule: the part of the home quota its own rank's tokens take
-    P[pl.home_local + e] = HOT ? min(sH[e], counts[(long long)r * E + e]) : 0;
+    P[pl.home_local + e] = HOT ? min(sH[e], count_of(r, e)) : 0;
     P[pl.O + e] = sO[lam(e)];
     P[pl.home_row + e] = sF[fb + (e - r * nh)] - sF[fb];
   }
@@ -458,7 +462,7 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
       const int fb = dd * nh + sRep[dd];
       row = sF[fb + nh + sPj[g]] - sF[fb];
       wrow = sPj[g] < B ? E + sPj[g] : ex;
-      if (HOT) loc = min(cnt, counts[(long long)dd * E + ex]);   // its own rank's tokens
+      if (HOT) loc = min(cnt, count_of(dd, ex));   // its own rank's tokens
     }
     P[pl.piece_local + g] = loc;
     P[pl.piece_wrow + g] = wrow;

@@ -358,6 +358,33 @@ def test_histogram_of_caller_ids_and_bad_ids():
     assert buf["status"].item() & lbt.ST_BADID
 
 
+@pytest.mark.parametrize("S", [1, 33, 100, 300])
+def test_histogram_path_ragged_sizes(S):
+    """Caller-supplied ids through lbt_histogram (one workgroup per 32-token
+    sub-tile), the plan and align, at sizes with a ragged last sub-tile and
+    several 128-token tiles per rank: load matrix, plan and placement equal
+    the oracle's."""
+    import load_balanced_token_amd as lbt
+    t = gu.torch()
+    w = WORKLOADS["dsv3"].with_(S=S, H=64)
+    logits = router_logits(w, 0)
+    ref = gu.run_oracle(w, logits)
+    path = lbt.Path(gu.shape_of(w))
+    buf = path.alloc()
+    buf["status"].zero_()
+    d = gu.h2d(ref["ids"].astype(np.int32))
+    path.histogram(d, buf["counts"], buf["work"], buf["status"])
+    path.plan_balance(buf["counts"], buf["plan"], buf["status"])
+    path.align_sort(d, buf["work"], buf["plan"], buf["slot"], buf["sorted_ids"],
+                    buf["block_wrow"], buf["block_expert"], buf["status"])
+    t.cuda.synchronize()
+    got = {k: gu.d2h(v) for k, v in buf.items()}
+    assert np.array_equal(got["counts"], ref["counts"])
+    pf = lbt.plan_fields(got["plan"], path.sizes, w.R, w.E)
+    gu.check_plan(pf, ref["plan"], w.P)
+    gu.check_align(got, ref, w.R, path.sizes["C"])
+
+
 def test_duplicate_ids_flagged():
     import load_balanced_token_amd as lbt
     t = gu.torch()

@@ -587,15 +587,23 @@ def test_route_width_ladder(E, K, R):
 
 
 @pytest.mark.parametrize("case,planner", [("E512_K64", "fixed"), ("E512_K64", "quota"),
-                                          ("R512", "fixed"), ("R512", "quota")])
+                                          ("R512", "fixed"), ("R512", "quota"),
+                                          ("R65", "fixed"), ("R65", "quota"),
+                                          ("R128", "fixed"), ("R128", "quota")])
 def test_maximum_sizes(case, planner):
     """The library's limits: E = 512 with K = 64 (64 top-K rounds per token,
     every lane list refilled many times), and R = E = 512 (one expert per
-    rank, up to E + R replica pieces), through either planner."""
+    rank, up to E + R replica pieces), through either planner; and rank
+    counts past one wave (65, 128), where the plan's per-rank prefixes come
+    from LDS scans instead of one lane per rank."""
     if case == "E512_K64":
         w = WORKLOADS["dsv3"].with_(E=512, K=64, R=8, S=64, H=64, B=4, blk=16)
-    else:
+    elif case == "R512":
         w = WORKLOADS["dsv3"].with_(E=512, R=512, K=8, S=4, H=64, B=2, blk=4)
+    elif case == "R65":
+        w = WORKLOADS["dsv3"].with_(E=130, R=65, K=8, S=24, H=64, B=3, blk=8)
+    else:
+        w = WORKLOADS["dsv3"].with_(E=256, R=128, K=8, S=16, H=64, B=2, blk=16)
     print(f"[parity] limits {case} {planner}", flush=True)
     logits = router_logits(w, 0)
     res = gu.run_front(gu.shape_of(w), logits, planner=planner)

@@ -223,7 +223,7 @@ def decode_latency(path, buf, w, x, n_steps, dev, planner="fixed"):
 
 def planner_report(lbt, torch, w, counts, B, tau_max, dev, ids=None, work=None):
     """Both planners on the same load matrix: latency (median of 20 back-to-back
-    calls; the quota planner is its search launch plus its plan launch), the
+    calls; either planner is one launch), the
     threshold, replica segments, the most on one rank, remote replicas, and
     (given the step's ids and workspace) how many pairs each plan serves on
     their own token's rank -- the pairs a multi-GPU run would not send."""
@@ -338,6 +338,213 @@ def training_report(lbt, torch, w, path, buf, dev, Hp, reps):
     return out
 
 
+class StepRunner:
+    """Buffers and inputs of one workload, resident in HBM, and the timed step
+    (route -> plan -> align -> dispatch -> combine) over them."""
+
+    def __init__(self, lbt, torch, w, dev, planner="fixed", tau_max=0, x_on_device=False):
+        import numpy as np
+        from workloads.gen import X_CHUNK, x_chunk
+        self.torch, self.w, self.dev, self.planner = torch, w, dev, planner
+        shape = lbt.Shape(E=w.E, K=w.K, R=w.R, S=w.S, H=w.H, B=w.B, blk=w.blk,
+                          score_fn=lbt.SOFTMAX if w.score == "softmax" else lbt.SIGMOID,
+                          tau_max=tau_max if planner == "quota" else 0)
+        self.path = lbt.Path(shape)
+        self.C = self.path.sizes["C"]
+        self.buf = self.path.alloc(dev)
+        print(f"[bench] {w.name}: E={w.E} K={w.K} R={w.R} S={w.S} H={w.H} B={w.B} blk={w.blk} "
+              f"C={self.C}; generating inputs", file=sys.stderr, flush=True)
+        if x_on_device:
+            # N(0,1) rounded to bf16, drawn on the device (the values of x do
+            # not change what the path does or how long it takes)
+            g = torch.Generator(device=dev)
+            g.manual_seed(w.seed)
+            x = torch.randn((w.N, w.H), generator=g, device=dev, dtype=torch.float32)
+            self.x = x.to(torch.bfloat16).view(torch.int16)
+            del x
+        else:
+            self.x = torch.empty((w.N, w.H), dtype=torch.int16, device=dev)
+            for c in range((w.N + X_CHUNK - 1) // X_CHUNK):
+                blk = x_chunk(w, 0, c)
+                self.x[c * X_CHUNK: c * X_CHUNK + blk.shape[0]] = \
+                    torch.from_numpy(blk.view(np.int16)).to(dev)
+        self.buf["status"].zero_()
+        torch.cuda.synchronize()
+        self.stream = torch.cuda.current_stream()
+        self.plan_fn = self.path.plan_balance if planner == "fixed" else self.path.plan_quota
+
+    names = ["route", "plan", "align", "dispatch", "combine"]
+
+    def step(self, logits, evs=None):
+        path, buf, stream = self.path, self.buf, self.stream
+        rec = (lambda i: evs[i].record(stream)) if evs is not None else (lambda i: None)
+        rec(0)
+        path.route_topk(logits, buf["ids"], buf["gates"], buf["counts"], buf["work"])
+        rec(1)
+        self.plan_fn(buf["counts"], buf["plan"], buf["status"])
+        rec(2)
+        path.align_sort(buf["ids"], buf["work"], buf["plan"], buf["slot"], buf["sorted_ids"],
+                        buf["block_wrow"], buf["block_expert"], buf["status"])
+        rec(3)
+        path.dispatch(self.x, buf["slot"], buf["recv"])
+        rec(4)
+        path.combine(buf["recv"], buf["slot"], buf["gates"], buf["y"])
+        rec(5)
+
+    def timed(self, logits, steps, warmup):
+        """Warm up, then time ``steps`` steps: wall seconds, mean per-kernel
+        event times (us) and each step's device time (us)."""
+        import numpy as np
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(logits)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.names) + 1)]
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(logits, evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = {n: [] for n in self.names}
+        for e in evs:
+            for j, n in enumerate(self.names):
+                per[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)   # microseconds
+        return (wall, {n: float(np.mean(v)) for n, v in per.items()},
+                [e[0].elapsed_time(e[-1]) * 1e3 for e in evs])
+
+    def plan_alone_us(self, reps=20):
+        """The planner alone: median of back-to-back launches on the step's
+        load matrix (checked equal to the step's plan)."""
+        import numpy as np
+        torch, buf = self.torch, self.buf
+        plan2 = torch.empty_like(buf["plan"])
+        pev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        for _ in range(3):
+            self.plan_fn(buf["counts"], plan2)
+        pev[0].record(self.stream)
+        for i in range(reps):
+            self.plan_fn(buf["counts"], plan2)
+            pev[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        assert torch.equal(plan2, buf["plan"]), "standalone plan differs from the step's"
+        return float(np.median([pev[i].elapsed_time(pev[i + 1]) * 1e3 for i in range(reps)]))
+
+    def summary(self, wall, avg_us, step_dev_us, steps):
+        """Throughput and HBM fractions of a timed run."""
+        import numpy as np
+        w = self.w
+        ab = algorithmic_bytes(w, self.C)
+        hdr = self.buf["plan"][:16].cpu().numpy()
+        gb = lambda n, us: ab[n] / (us * 1e-6) / 1e9   # noqa: E731
+        dc = (ab["dispatch"] + ab["combine"]) / ((avg_us["dispatch"] + avg_us["combine"]) * 1e-6) / 1e9
+        ms = wall / steps * 1e3
+        return {
+            "ms_per_step": ms,
+            "token_slots_per_s": w.P * steps / wall,
+            "step_hbm_gbps": sum(ab.values()) / (ms * 1e-3) / 1e9,
+            "dispatch_combine_gbps": dc,
+            "dispatch_combine_frac_peak": dc / HBM_PEAK_GBPS,
+            "dispatch_frac_peak": gb("dispatch", avg_us["dispatch"]) / HBM_PEAK_GBPS,
+            "combine_frac_peak": gb("combine", avg_us["combine"]) / HBM_PEAK_GBPS,
+            "route_frac_peak": gb("route", avg_us["route"]) / HBM_PEAK_GBPS,
+            "align_frac_peak": gb("align", avg_us["align"]) / HBM_PEAK_GBPS,
+            "kernel_us": avg_us,
+            "step_device_us_median": float(np.median(step_dev_us)),
+            "step_device_us_min": float(np.min(step_dev_us)),
+            "max_vio": float(hdr[1]) * w.E / w.P - 1.0,
+            "rank_imbalance_before": float(hdr[2]) / w.SK - 1.0,
+            "replica_segments": int(hdr[0]),
+            "max_replicas_per_rank": int(hdr[10]),
+            "status": int(self.buf["status"].item()),
+        }
+
+    def free(self):
+        del self.buf, self.x, self.path
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
+
+
+def workloads_block(lbt, torch, dev, steps, warmup, decode_steps):
+    """Every other workload at its full shape, each in its own guard so that
+    a failure records an error and keeps the line: WideEP and Kimi-K3 (step
+    time, dispatch + combine fraction, route / plan / align times in the
+    step, plan alone), decode S = 1, 16, 128 (eager step plus the p50/p99 of
+    one HIP graph per step over fresh routings), and the MoonEP max_vio
+    sweep (E=384, S=8192, max_vio 0.2, 1, 10, 20)."""
+    from workloads import WORKLOADS, router_logits
+    from workloads.gen import MAXVIO_SWEEP
+    out = {}
+
+    def one(name, fn):
+        t0 = time.perf_counter()
+        print(f"[bench] workloads block: {name}", file=sys.stderr, flush=True)
+        try:
+            out[name] = fn()
+        except Exception as e:  # keep the line: record what failed
+            out[name] = {"error": f"{type(e).__name__}: {e}"[:400]}
+        out[name]["wall_s"] = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+    def big(name):
+        def fn():
+            w = WORKLOADS[name]
+            run = StepRunner(lbt, torch, w, dev, x_on_device=True)
+            try:
+                logits = torch.from_numpy(router_logits(w, 0)).to(dev)
+                wall, us, dev_us = run.timed(logits, steps, warmup)
+                res = run.summary(wall, us, dev_us, steps)
+                res["plan_us"] = run.plan_alone_us()
+                res["x"] = "N(0,1) bf16 drawn on the device"
+                return res
+            finally:
+                run.free()
+        return fn
+
+    def decode(name):
+        def fn():
+            w = WORKLOADS[name]
+            run = StepRunner(lbt, torch, w, dev)
+            try:
+                logits = torch.from_numpy(router_logits(w, 0)).to(dev)
+                wall, us, dev_us = run.timed(logits, steps, warmup)
+                res = run.summary(wall, us, dev_us, steps)
+                res["plan_us"] = run.plan_alone_us()
+                res["decode_latency"] = decode_latency(run.path, run.buf, w, run.x, decode_steps,
+                                                       dev)
+                return res
+            finally:
+                run.free()
+        return fn
+
+    def sweep():
+        w = WORKLOADS["moonep"]
+        run = StepRunner(lbt, torch, w, dev, x_on_device=True)
+        try:
+            pts = []
+            for v in MAXVIO_SWEEP:
+                lg = torch.from_numpy(router_logits(w.with_(vio=v), 0)).to(dev)
+                wall, us, dev_us = run.timed(lg, steps, warmup)
+                res = run.summary(wall, us, dev_us, steps)
+                res["vio"] = v
+                pts.append(res)
+                del lg
+            ms = [p["ms_per_step"] for p in pts]
+            return {"points": pts, "ms_per_step_max_over_min": max(ms) / min(ms),
+                    "x": "N(0,1) bf16 drawn on the device"}
+        finally:
+            run.free()
+
+    one("wideep", big("wideep"))
+    one("kimi", big("kimi"))
+    for name in ("decode1", "decode16", "decode128"):
+        one(name, decode(name))
+    one("moonep_maxvio_sweep", sweep)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -348,7 +555,7 @@ def main():
                     help="tokens per rank of the oracle sample (default: up to 32768 tokens in all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1000,
-                    help="fresh-routing graph replays for the decode workloads")
+                    help="fresh-routing graph replays for the decode workloads (0: none)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--planner", choices=("fixed", "quota"), default="fixed",
@@ -364,6 +571,10 @@ def main():
                     help="expert intermediate size H' of the prefetched weights")
     ap.add_argument("--maxvio-sweep", action="store_true",
                     help="moonep: also time the step at max_vio 0.2, 1, 10, 20 (same buffers)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the block of the other workloads (run with the default dsv3 only)")
+    ap.add_argument("--x-device", action="store_true",
+                    help="draw x on the device (N(0,1) bf16, torch's generator) instead of the host")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -376,7 +587,6 @@ def main():
 
     import load_balanced_token_amd as lbt
     from workloads import WORKLOADS, router_logits
-    from workloads.gen import X_CHUNK, x_chunk
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -388,63 +598,9 @@ def main():
     if args.vio >= 0:
         w = w.with_(vio=args.vio)
     tau_max = int(round(args.tau_max_x * w.SK))
-    shape = lbt.Shape(E=w.E, K=w.K, R=w.R, S=w.S, H=w.H, B=w.B, blk=w.blk,
-                      score_fn=lbt.SOFTMAX if w.score == "softmax" else lbt.SIGMOID,
-                      tau_max=tau_max if args.planner == "quota" else 0)
-    path = lbt.Path(shape)
-    C = path.sizes["C"]
-    buf = path.alloc(dev)
-    print(f"[bench] {w.name}: E={w.E} K={w.K} R={w.R} S={w.S} H={w.H} B={w.B} blk={w.blk} "
-          f"C={C}; generating inputs", file=sys.stderr, flush=True)
+    run = StepRunner(lbt, torch, w, dev, args.planner, tau_max, x_on_device=args.x_device)
+    path, buf, x, C = run.path, run.buf, run.x, run.C
 
-    # inputs resident in HBM before timing
-    x = torch.empty((w.N, w.H), dtype=torch.int16, device=dev)
-    for c in range((w.N + X_CHUNK - 1) // X_CHUNK):
-        blk = x_chunk(w, 0, c)
-        x[c * X_CHUNK: c * X_CHUNK + blk.shape[0]] = torch.from_numpy(blk.view(np.int16)).to(dev)
-    buf["status"].zero_()
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-    names = ["route", "plan", "align", "dispatch", "combine"]
-    plan_fn = path.plan_balance if args.planner == "fixed" else path.plan_quota
-
-    def step(logits, evs=None):
-        rec = (lambda i: evs[i].record(stream)) if evs is not None else (lambda i: None)
-        rec(0)
-        path.route_topk(logits, buf["ids"], buf["gates"], buf["counts"], buf["work"])
-        rec(1)
-        plan_fn(buf["counts"], buf["plan"], buf["status"])
-        rec(2)
-        path.align_sort(buf["ids"], buf["work"], buf["plan"], buf["slot"], buf["sorted_ids"],
-                        buf["block_wrow"], buf["block_expert"], buf["status"])
-        rec(3)
-        path.dispatch(x, buf["slot"], buf["recv"])
-        rec(4)
-        path.combine(buf["recv"], buf["slot"], buf["gates"], buf["y"])
-        rec(5)
-
-    def timed(logits):
-        """Warm up, then time args.steps steps; mean per-kernel event times (us)."""
-        for _ in range(args.warmup):
-            step(logits)
-        torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-               for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(logits, evs[i])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        per = {n: [] for n in names}
-        for e in evs:
-            for j, n in enumerate(names):
-                per[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)   # microseconds
-        return (wall, {n: float(np.mean(v)) for n, v in per.items()},
-                [e[0].elapsed_time(e[-1]) * 1e3 for e in evs])
-
-    ab = algorithmic_bytes(w, C)
     sweep = []
     if args.maxvio_sweep:
         if w.skew != "maxvio":
@@ -452,21 +608,14 @@ def main():
             sys.exit(2)
         from workloads.gen import MAXVIO_SWEEP
         for v in MAXVIO_SWEEP:
-            wv = w.with_(vio=v)
             print(f"[bench] max_vio sweep: vio={v}", file=sys.stderr, flush=True)
-            lg = torch.from_numpy(router_logits(wv, 0)).to(dev)
-            wall_v, us_v, _ = timed(lg)
-            hdr_v = buf["plan"][:16].cpu().numpy()
-            sweep.append({
-                "vio": v, "max_vio": float(hdr_v[1]) * w.E / w.P - 1.0,
-                "rank_imbalance_before": float(hdr_v[2]) / w.SK - 1.0,
-                "ms_per_step": wall_v / args.steps * 1e3, "kernel_us": us_v,
-                "dispatch_combine_frac_peak": (ab["dispatch"] + ab["combine"]) /
-                ((us_v["dispatch"] + us_v["combine"]) * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-                "replica_segments": int(hdr_v[0]), "max_replicas_per_rank": int(hdr_v[10]),
-                "remote_replicas": int(buf["plan"][path.sizes["off_n_remote"]:
-                                                   path.sizes["off_n_remote"] + w.R].sum().item()),
-                "status": int(buf["status"].item())})
+            lg = torch.from_numpy(router_logits(w.with_(vio=v), 0)).to(dev)
+            wall_v, us_v, dev_v = run.timed(lg, args.steps, args.warmup)
+            pt = run.summary(wall_v, us_v, dev_v, args.steps)
+            pt["vio"] = v
+            pt["remote_replicas"] = int(buf["plan"][path.sizes["off_n_remote"]:
+                                                    path.sizes["off_n_remote"] + w.R].sum().item())
+            sweep.append(pt)
             del lg
             torch.cuda.synchronize()
 
@@ -474,23 +623,10 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr,
           flush=True)
-    wall, avg_us, step_dev_us = timed(logits)
+    wall, avg_us, step_dev_us = run.timed(logits, args.steps, args.warmup)
+    plan_alone_us = run.plan_alone_us()
+    summ = run.summary(wall, avg_us, step_dev_us, args.steps)
 
-    # the planner alone (back-to-back launches on the same load matrix)
-    plan2 = torch.empty_like(buf["plan"])
-    pev = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
-    for _ in range(3):
-        plan_fn(buf["counts"], plan2)
-    pev[0].record(stream)
-    for i in range(20):
-        plan_fn(buf["counts"], plan2)
-        pev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    plan_alone_us = float(np.median([pev[i].elapsed_time(pev[i + 1]) * 1e3 for i in range(20)]))
-    assert torch.equal(plan2, buf["plan"]), "standalone plan differs from the fused one"
-
-    status = int(buf["status"].item())
-    hdr = buf["plan"][:16].cpu().numpy()
     planners = planner_report(lbt, torch, w, buf["counts"], w.B, tau_max, dev,
                               ids=buf["ids"], work=buf["work"])
     training = None
@@ -503,22 +639,19 @@ def main():
         for _ in range(3):
             b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
 
-    step_bytes = sum(ab.values())
-    ms_per_step = wall / args.steps * 1e3
-    slots_per_s = w.P * args.steps / wall
+    ab = algorithmic_bytes(w, C)
     comb_gbps = ab["combine"] / (avg_us["combine"] * 1e-6) / 1e9
-    disp_gbps = ab["dispatch"] / (avg_us["dispatch"] * 1e-6) / 1e9
-    dc_gbps = (ab["dispatch"] + ab["combine"]) / ((avg_us["dispatch"] + avg_us["combine"]) * 1e-6) / 1e9
     traffic = measured_traffic("combine", w.name)
     result = {
         "metric": "token-slots/s",
-        "value": slots_per_s,
+        "value": summ["token_slots_per_s"],
         "unit": "token-slots/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": summ["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -534,31 +667,39 @@ def main():
                      "achieved": comb_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": comb_gbps / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": ab["combine"]},
-        "step_hbm_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
-        "step_pct_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "dispatch_combine_gbps": dc_gbps,
-        "dispatch_combine_frac_peak": dc_gbps / HBM_PEAK_GBPS,
-        "dispatch_gbps": disp_gbps,
+        "step_hbm_gbps": summ["step_hbm_gbps"],
+        "step_pct_hbm_peak": summ["step_hbm_gbps"] / HBM_PEAK_GBPS,
+        "dispatch_combine_gbps": summ["dispatch_combine_gbps"],
+        "dispatch_combine_frac_peak": summ["dispatch_combine_frac_peak"],
+        "dispatch_gbps": summ["dispatch_frac_peak"] * HBM_PEAK_GBPS,
         "kernel_us": avg_us,
+        "kernels": {n: {"us": avg_us[n], "algorithmic_bytes": ab[n],
+                        "frac_peak": ab[n] / (avg_us[n] * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+                    for n in ("route", "align", "dispatch", "combine")},
         "plan_us": plan_alone_us,
         "plan_in_step_us": avg_us["plan"],
-        "step_device_us_median": float(np.median(step_dev_us)),
-        "step_device_us_min": float(np.min(step_dev_us)),
-        "max_vio": float(hdr[1]) * w.E / w.P - 1.0,
-        "rank_imbalance_before": float(hdr[2]) / w.SK - 1.0,
-        "replica_segments": int(hdr[0]),
+        "step_device_us_median": summ["step_device_us_median"],
+        "step_device_us_min": summ["step_device_us_min"],
+        "max_vio": summ["max_vio"],
+        "rank_imbalance_before": summ["rank_imbalance_before"],
+        "replica_segments": summ["replica_segments"],
         "planners": planners,
         **({"maxvio_sweep": sweep} if sweep else {}),
         **({"training": training} if training else {}),
-        "status": status,
+        "status": summ["status"],
         "device": torch.cuda.get_device_name(0),
         "device_info": device_report(torch, 0),
     }
-    if w.name.startswith("decode"):
+    if w.name.startswith("decode") and args.decode_steps > 0:
         print(f"[bench] decode latency over {args.decode_steps} fresh routings (HIP graph)",
               file=sys.stderr, flush=True)
         result["decode_latency"] = decode_latency(path, buf, w, x, args.decode_steps, dev,
                                                   args.planner)
+    del path, buf, x, logits
+    run.free()
+    if args.workload == "dsv3" and not args.no_workloads:
+        result["workloads"] = workloads_block(lbt, torch, dev, args.steps, args.warmup,
+                                              args.decode_steps)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         sample_S = args.cpu_sample_S or max(1, min(w.S, 32768 // w.R))

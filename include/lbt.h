@@ -21,7 +21,11 @@
  *     default stream) and never synchronises the host.
  *   - Arguments are checked on the host: a call returns LBT_OK (0) or a
  *     negative LBT_E* code and then launches nothing.  LBT_EHIP reports a
- *     failed launch.  Data-dependent problems (inconsistent counts, an id
+ *     failed launch of this call: the calling thread's HIP last-error state
+ *     is cleared before the call's first launch, so an error left by an
+ *     earlier HIP call is never reported as this call's; kernels the call
+ *     queued before the failing launch stay queued, later ones are not
+ *     launched.  Data-dependent problems (inconsistent counts, an id
  *     out of range, a rank needing more rows than the capacity) are reported
  *     through the device status word (LBT_ST_* bits) that plan_balance
  *     writes and align_sort / histogram OR into; the caller reads it when it
@@ -44,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LBT_VERSION 3
+#define LBT_VERSION 4
 
 /* return codes */
 #define LBT_OK 0
@@ -190,6 +194,20 @@ int lbt_histogram(const lbt_shape* s, const int32_t* ids, int32_t* counts, int32
 int lbt_plan_balance(const lbt_shape* s, const int32_t* counts, int32_t* plan, int32_t* status,
                      void* stream);
 
+/* Route, histogram and fixed-rule plan in one call: the outputs of
+ * lbt_route_topk (ids, gates, counts, work) followed by lbt_plan_balance
+ * (plan, status), bit for bit.  [MoonEP-GR] section "Online planning, zero
+ * copy και στατικά σχήματα" (the plan is made online from the current router
+ * output, on the GPU, with no host round trip).  Batches of at most 32
+ * tokens (with R * ceil(S / 32) * E <= 16384) run as one workgroup that
+ * keeps the load matrix in LDS and plans from it -- one launch where the
+ * two calls make two; larger batches make the same launches as the two
+ * calls.  Arguments as for the two calls; plan [plan_words] int32 out,
+ * status int32 out (may be NULL). */
+int lbt_route_plan(const lbt_shape* s, const float* logits, const float* sel_bias, int32_t* ids,
+                   float* gates, int32_t* counts, int32_t* work, int32_t* plan, int32_t* status,
+                   void* stream);
+
 /* Quota plan with a searched threshold: same blob layout and meaning as
  * lbt_plan_balance, so lbt_align_sort, lbt_dispatch and lbt_combine take it
  * unchanged.  [UltraEP] section "その仕組みは高速なエキスパート複製に依存する"
@@ -272,7 +290,7 @@ int lbt_combine(const lbt_shape* s, const uint16_t* out, const int32_t* slot, co
  * row index; the pool is process-global, shared by the layers; replicas
  * beyond the slots read home weights).  For every replica segment of the plan
  * with weight row E + j on rank d: slots[d][j] = weights[expert], a bit copy
- * streamed in 32 KiB tiles.  Slots the plan does not use are not written.
+ * streamed in 4 KiB tiles.  Slots the plan does not use are not written.
  *   plan      blob from lbt_plan_balance / lbt_plan_quota
  *   weights   [E][row_bytes] home weight rows (rows 0..E-1 of the pool), 16-byte aligned
  *   slots     [R][B][row_bytes] each rank's prefetch slots, 16-byte aligned

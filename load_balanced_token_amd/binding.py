@@ -28,7 +28,7 @@ ST_CAPACITY = 2
 ST_BADID = 4
 ST_DUPID = 8
 
-ABI_VERSION = 3          # LBT_VERSION of include/lbt.h this binding's structs follow
+ABI_VERSION = 4          # LBT_VERSION of include/lbt.h this binding's structs follow
 
 HDR_N_PIECES = 0
 HDR_MAX_T = 1
@@ -45,6 +45,7 @@ HDR_FEASIBLE = 11
 HDR_LOCAL = 12
 
 EXPORTS = ("lbt_query_sizes", "lbt_route_topk", "lbt_histogram", "lbt_plan_balance",
+           "lbt_route_plan",
            "lbt_plan_quota", "lbt_align_sort", "lbt_dispatch", "lbt_combine",
            "lbt_prefetch_weights", "lbt_reduce_grad", "lbt_combine_bwd", "lbt_dispatch_bwd",
            "lbt_strerror", "lbt_last_hip_error", "lbt_version")
@@ -99,6 +100,7 @@ def lib() -> ctypes.CDLL:
         L.lbt_histogram.argtypes = [SP, P, P, P, P, P]
         L.lbt_plan_balance.argtypes = [SP, P, P, P, P]
         L.lbt_plan_quota.argtypes = [SP, P, P, P, P]
+        L.lbt_route_plan.argtypes = [SP, P, P, P, P, P, P, P, P, P]
         L.lbt_align_sort.argtypes = [SP, P, P, P, P, P, P, P, P, P]
         L.lbt_dispatch.argtypes = [SP, P, P, P, P]
         L.lbt_combine.argtypes = [SP, P, P, P, ctypes.c_int32, P, P]
@@ -272,6 +274,24 @@ class Path:
             _stream(stream))
         _check(rc, "lbt_plan_balance")
 
+    # a1 + a2 + a3 in one call (one launch for small batches)
+    def route_plan(self, logits, ids, gates, counts, work, plan, status=None, sel_bias=None,
+                   stream=None):
+        torch = _torch()
+        s, z = self.shape, self.sizes
+        rc = lib().lbt_route_plan(
+            ctypes.byref(self._c),
+            _ptr(logits, torch.float32, s.N * s.E, "logits"),
+            _ptr(sel_bias, torch.float32, s.E, "sel_bias"),
+            _ptr(ids, torch.int32, s.N * s.K, "ids"),
+            _ptr(gates, torch.float32, s.N * s.K, "gates"),
+            _ptr(counts, torch.int32, s.R * s.E, "counts"),
+            _ptr(work, torch.int32, z["work_words"], "work"),
+            _ptr(plan, torch.int32, z["plan_words"], "plan"),
+            _ptr(status, torch.int32, 1, "status"),
+            _stream(stream))
+        _check(rc, "lbt_route_plan")
+
     # a3, quota variant
     def plan_quota(self, counts, plan, status=None, stream=None):
         torch = _torch()
@@ -394,10 +414,13 @@ class Path:
         (lbt_plan_quota).  Returns nothing; results land in ``buf``."""
         if planner not in ("fixed", "quota"):
             raise LbtError(f"unknown planner {planner!r}")
-        self.route_topk(logits, buf["ids"], buf["gates"], buf["counts"], buf["work"],
-                        sel_bias=sel_bias, stream=stream)
-        plan = self.plan_balance if planner == "fixed" else self.plan_quota
-        plan(buf["counts"], buf["plan"], buf["status"], stream=stream)
+        if planner == "fixed":
+            self.route_plan(logits, buf["ids"], buf["gates"], buf["counts"], buf["work"],
+                            buf["plan"], buf["status"], sel_bias=sel_bias, stream=stream)
+        else:
+            self.route_topk(logits, buf["ids"], buf["gates"], buf["counts"], buf["work"],
+                            sel_bias=sel_bias, stream=stream)
+            self.plan_quota(buf["counts"], buf["plan"], buf["status"], stream=stream)
         self.align_sort(buf["ids"], buf["work"], buf["plan"], buf["slot"], buf["sorted_ids"],
                         buf["block_wrow"], buf["block_expert"], buf["status"], stream=stream)
         self.dispatch(x, buf["slot"], buf["recv"], stream=stream)

@@ -23,22 +23,21 @@
 
 namespace lbt {
 
-// Threads per token.  Measured on MI355X (align alone, in the step):
-// 1 / 2 / 4 / 8 threads per token took DSV3 15.7 / 11.6 / 9.5 / 8.9 us and
-// Kimi-K3 62 / 49 / 37 / 36 us; 4 keeps every thread busy for K = 4 and 8.
-constexpr int kAlignTPT = 4;
-constexpr int kAlignThreads = kTileTokens * kAlignTPT;
+// Threads of a tile workgroup.  The tile's pairs f = t0*K + p are taken in
+// flat order, thread tid placing p = tid, tid + 512, ..., so consecutive
+// lanes read consecutive ids and write consecutive slots.  (Measured on
+// MI355X with 1 / 2 / 4 / 8 threads per token instead, each taking every
+// 1st / 2nd / 4th / 8th pair of its token: DSV3 15.7 / 11.6 / 9.5 / 8.9 us,
+// Kimi-K3 62 / 49 / 37 / 36 us.)
+constexpr int kAlignThreads = 512;
 constexpr int kBlockWaves = kAlignThreads / kWave;   // blocks handled per workgroup
 
-// Thread tid serves token tid % kTileTokens of the tile and its pairs
-// k = part, part + TPT, ... with part = tid / kTileTokens.
-template <int TPT>
-__global__ __launch_bounds__(kTileTokens * TPT) void k_align(
+template <int NT>
+__global__ __launch_bounds__(NT) void k_align(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ work,
     const int32_t* __restrict__ plan, Dims d, int32_t* __restrict__ slot,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_wrow,
     int32_t* __restrict__ block_expert, int32_t* __restrict__ status) {
-  constexpr int NT = kTileTokens * TPT;
   if ((int)blockIdx.x >= d.n_tiles) {
     const long long gb = (long long)(blockIdx.x - d.n_tiles) * (NT / kWave) + wave_id();
     if (gb < (long long)d.R * d.n_blocks) align_blocks(plan, d, gb, sorted_ids, block_wrow, block_expert);
@@ -86,18 +85,18 @@ __global__ __launch_bounds__(kTileTokens * TPT) void k_align(
   const int32_t* tbase = work + work_tile_base(d) + (long long)tile * E;
   const int32_t* rbase = work + work_tile_base(d) + (long long)r * d.tpr * E;   // rank r's first tile
   const int tid = threadIdx.x;
-  const int ti = tid % kTileTokens, part = tid / kTileTokens;
-  const long long t = (long long)t0 + ti;
+  const long long f0 = (long long)t0 * K;   // first pair of the tile
+  const int np = len * K;                   // pairs of the tile
 
-  // the thread's first kPre expert ids (k = part + j * TPT), loaded before
+  // the thread's first kPre expert ids (pairs tid + j * NT), loaded before
   // the plan so that the two latencies overlap (for K <= 8 no id is read
   // twice)
-  constexpr int kPre = (8 + TPT - 1) / TPT;
+  constexpr int kPre = (kTileTokens * 8 + NT - 1) / NT;
   int idp[kPre];
 #pragma unroll
-  for (int j = 0; j < kPre; ++j) {
-    const int k = part + j * TPT;
-    idp[j] = (ti < len && k < K) ? ids[t * K + k] : -1;
+  for (int u = 0; u < kPre; ++u) {
+    const int p = tid + u * NT;
+    idp[u] = p < np ? ids[f0 + p] : -1;
   }
 
   for (int e = tid; e < E; e += NT) {
@@ -155,19 +154,21 @@ __global__ __launch_bounds__(kTileTokens * TPT) void k_align(
   }
 
   int flags = 0;
-  const int sub = ti / kSubTokens;
-  const uint32_t bit = 1u << (ti % kSubTokens);
-  auto mark = [&](int e) {
+  // token (within the tile) of pair p: p / K by one multiply-high
+  auto token_of = [&](int p) { return d.K == 1 ? p : (int)__umulhi((uint32_t)p, d.k_magic); };
+  auto mark = [&](int p, int e) {
     if (e < 0 || e >= E) return;
-    const uint32_t old = atomicOr(&sMask[sub * E + e], bit);
+    const int ti = token_of(p);
+    const uint32_t bit = 1u << (ti % kSubTokens);
+    const uint32_t old = atomicOr(&sMask[(ti / kSubTokens) * E + e], bit);
     if (old & bit) flags |= LBT_ST_DUPID;
   };
-  if (ti < len) {
 #pragma unroll
-    for (int j = 0; j < kPre; ++j)
-      if (part + j * TPT < K) mark(idp[j]);
-    for (int k = part + kPre * TPT; k < K; k += TPT) mark(ids[t * K + k]);
+  for (int u = 0; u < kPre; ++u) {
+    const int p = tid + u * NT;
+    if (p < np) mark(p, idp[u]);
   }
+  for (int p = tid + kPre * NT; p < np; p += NT) mark(p, ids[f0 + p]);
   __syncthreads();
   for (int e = tid; e < E; e += NT) {
     int run = 0;
@@ -179,13 +180,16 @@ __global__ __launch_bounds__(kTileTokens * TPT) void k_align(
   }
   __syncthreads();
 
-  auto place = [&](int k, int e) {
-    const long long f = t * K + k;
+  auto place = [&](int p, int e) {
+    const long long f = f0 + p;
     if (e < 0 || e >= E) {
       flags |= LBT_ST_BADID;
       slot[f] = -1;
       return;
     }
+    const int ti = token_of(p);
+    const int sub = ti / kSubTokens;
+    const uint32_t bit = 1u << (ti % kSubTokens);
     const int q = sBase[e] + sSub[sub * E + e] + __popc(sMask[sub * E + e] & (bit - 1u));
     const int h = sH[e];
     int dd, row;
@@ -235,12 +239,12 @@ __global__ __launch_bounds__(kTileTokens * TPT) void k_align(
     slot[f] = (int)dst;
     sorted_ids[dst] = (int)f;
   };
-  if (ti < len) {
 #pragma unroll
-    for (int j = 0; j < kPre; ++j)
-      if (part + j * TPT < K) place(part + j * TPT, idp[j]);
-    for (int k = part + kPre * TPT; k < K; k += TPT) place(k, ids[t * K + k]);
+  for (int u = 0; u < kPre; ++u) {
+    const int p = tid + u * NT;
+    if (p < np) place(p, idp[u]);
   }
+  for (int p = tid + kPre * NT; p < np; p += NT) place(p, ids[f0 + p]);
   if (flags && status != nullptr) atomicOr(status, flags);
 }
 
@@ -257,7 +261,7 @@ hipError_t launch_align(const Dims& d, const int32_t* ids, const int32_t* work, 
   const long long nblk = (long long)d.R * d.n_blocks;
   const long long grid = d.n_tiles + (nblk + kBlockWaves - 1) / kBlockWaves;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_align<kAlignTPT>, dim3((unsigned)grid), dim3(kAlignThreads),
+  hipLaunchKernelGGL(k_align<kAlignThreads>, dim3((unsigned)grid), dim3(kAlignThreads),
                      align_lds_bytes(d), st, ids, work, plan, d, slot, sorted_ids, block_wrow,
                      block_expert, status);
   return hipGetLastError();

@@ -76,6 +76,7 @@ int make_dims(const lbt_shape* s, Dims* d, lbt_sizes* z) {
     d->blk = (int)blk; d->score_fn = s->score_fn; d->renorm = s->renorm;
     d->nh = (int)nh;
     d->nh_magic = nh >= 2 ? (uint32_t)(((1ULL << 32) + nh - 1) / nh) : 0u;
+    d->k_magic = K >= 2 ? (uint32_t)(((1ULL << 32) + K - 1) / K) : 0u;
     d->N = (int)N; d->P = P; d->SK = (int)SK; d->tau_max = (int)tmax; d->C = (int)C;
     d->n_blocks = (int)(C / blk); d->tpr = (int)tpr; d->n_tiles = (int)nt;
     d->spr = (int)spr; d->n_sub = (int)(R * spr); d->pl = pl;
@@ -111,6 +112,15 @@ static int hip_rc(hipError_t e) {
   return LBT_EHIP;
 }
 
+// Clear the calling thread's HIP last-error state before a call's first
+// launch, so that the launchers' hipGetLastError() checks see only errors
+// raised by this call's own launches, never one left by an earlier HIP call
+// of the application.
+static hipStream_t begin_launches(void* stream) {
+  (void)hipGetLastError();
+  return static_cast<hipStream_t>(stream);
+}
+
 }  // namespace lbt
 
 using namespace lbt;
@@ -142,7 +152,7 @@ int lbt_route_topk(const lbt_shape* s, const float* logits, const float* sel_bia
   const int rc = make_dims(s, &d, nullptr);
   if (rc) return rc;
   if (counts == nullptr || (d.N > 0 && (!logits || !ids || !gates || !work))) return LBT_EINVAL;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipStream_t st = begin_launches(stream);
   return hip_rc(launch_route_and_scan(d, logits, sel_bias, ids, gates, work, counts, st));
 }
 
@@ -152,7 +162,7 @@ int lbt_histogram(const lbt_shape* s, const int32_t* ids, int32_t* counts, int32
   const int rc = make_dims(s, &d, nullptr);
   if (rc) return rc;
   if (counts == nullptr || (d.N > 0 && (!ids || !work))) return LBT_EINVAL;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipStream_t st = begin_launches(stream);
   hipError_t e = launch_histogram(d, ids, work, status, st);
   if (e == hipSuccess) e = launch_tile_scan(d, work, counts, st);
   return hip_rc(e);
@@ -164,7 +174,7 @@ int lbt_plan_balance(const lbt_shape* s, const int32_t* counts, int32_t* plan, i
   const int rc = make_dims(s, &d, nullptr);
   if (rc) return rc;
   if (!counts || !plan) return LBT_EINVAL;
-  return hip_rc(launch_plan(d, counts, plan, status, static_cast<hipStream_t>(stream)));
+  return hip_rc(launch_plan(d, counts, plan, status, begin_launches(stream)));
 }
 
 int lbt_plan_quota(const lbt_shape* s, const int32_t* counts, int32_t* plan, int32_t* status,
@@ -173,7 +183,20 @@ int lbt_plan_quota(const lbt_shape* s, const int32_t* counts, int32_t* plan, int
   const int rc = make_dims(s, &d, nullptr);
   if (rc) return rc;
   if (!counts || !plan) return LBT_EINVAL;
-  return hip_rc(launch_plan_quota(d, counts, plan, status, static_cast<hipStream_t>(stream)));
+  return hip_rc(launch_plan_quota(d, counts, plan, status, begin_launches(stream)));
+}
+
+int lbt_route_plan(const lbt_shape* s, const float* logits, const float* sel_bias, int32_t* ids,
+                   float* gates, int32_t* counts, int32_t* work, int32_t* plan, int32_t* status,
+                   void* stream) {
+  Dims d;
+  const int rc = make_dims(s, &d, nullptr);
+  if (rc) return rc;
+  if (counts == nullptr || plan == nullptr ||
+      (d.N > 0 && (!logits || !ids || !gates || !work)))
+    return LBT_EINVAL;
+  const hipStream_t st = begin_launches(stream);
+  return hip_rc(launch_route_plan(d, logits, sel_bias, ids, gates, work, counts, plan, status, st));
 }
 
 int lbt_align_sort(const lbt_shape* s, const int32_t* ids, const int32_t* work, const int32_t* plan,
@@ -185,7 +208,7 @@ int lbt_align_sort(const lbt_shape* s, const int32_t* ids, const int32_t* work, 
   if (!plan || !sorted_ids || !block_wrow || !block_expert) return LBT_EINVAL;
   if (d.N > 0 && (!ids || !work || !slot)) return LBT_EINVAL;
   return hip_rc(launch_align(d, ids, work, plan, slot, sorted_ids, block_wrow, block_expert, status,
-                             static_cast<hipStream_t>(stream)));
+                             begin_launches(stream)));
 }
 
 int lbt_dispatch(const lbt_shape* s, const uint16_t* x, const int32_t* slot, uint16_t* recv,
@@ -194,7 +217,7 @@ int lbt_dispatch(const lbt_shape* s, const uint16_t* x, const int32_t* slot, uin
   const int rc = make_dims(s, &d, nullptr);
   if (rc) return rc;
   if (d.N > 0 && (!x || !slot || !recv || !aligned16(x) || !aligned16(recv))) return LBT_EINVAL;
-  return hip_rc(launch_dispatch(d, x, slot, recv, static_cast<hipStream_t>(stream)));
+  return hip_rc(launch_dispatch(d, x, slot, recv, begin_launches(stream)));
 }
 
 int lbt_combine(const lbt_shape* s, const uint16_t* out, const int32_t* slot, const float* gates,
@@ -205,7 +228,7 @@ int lbt_combine(const lbt_shape* s, const uint16_t* out, const int32_t* slot, co
   if (y_dtype != LBT_Y_F32 && y_dtype != LBT_Y_BF16) return LBT_EINVAL;
   if (d.N > 0 && (!out || !slot || !gates || !y || !aligned16(out) || !aligned16(y)))
     return LBT_EINVAL;
-  return hip_rc(launch_combine(d, out, slot, gates, y_dtype, y, static_cast<hipStream_t>(stream)));
+  return hip_rc(launch_combine(d, out, slot, gates, y_dtype, y, begin_launches(stream)));
 }
 
 int lbt_prefetch_weights(const lbt_shape* s, const int32_t* plan, const void* weights, void* slots,
@@ -215,7 +238,7 @@ int lbt_prefetch_weights(const lbt_shape* s, const int32_t* plan, const void* we
   if (rc) return rc;
   if (!plan || row_bytes <= 0 || row_bytes % 16 != 0) return LBT_EINVAL;
   if (d.B > 0 && (!weights || !slots || !aligned16(weights) || !aligned16(slots))) return LBT_EINVAL;
-  return hip_rc(launch_prefetch(d, plan, weights, slots, row_bytes, static_cast<hipStream_t>(stream)));
+  return hip_rc(launch_prefetch(d, plan, weights, slots, row_bytes, begin_launches(stream)));
 }
 
 int lbt_reduce_grad(const lbt_shape* s, const int32_t* plan, float* slot_grads, float* grads,
@@ -227,7 +250,7 @@ int lbt_reduce_grad(const lbt_shape* s, const int32_t* plan, float* slot_grads, 
   if (d.B > 0 && (!slot_grads || !grads || !aligned16(slot_grads) || !aligned16(grads)))
     return LBT_EINVAL;
   return hip_rc(launch_reduce_grad(d, plan, slot_grads, grads, row_elems,
-                                   static_cast<hipStream_t>(stream)));
+                                   begin_launches(stream)));
 }
 
 int lbt_combine_bwd(const lbt_shape* s, const uint16_t* out, const int32_t* slot,
@@ -241,7 +264,7 @@ int lbt_combine_bwd(const lbt_shape* s, const uint16_t* out, const int32_t* slot
                   !aligned16(dy) || !aligned16(d_out)))
     return LBT_EINVAL;
   return hip_rc(launch_combine_bwd(d, out, slot, gates, dy_dtype, dy, d_out, d_gates,
-                                   static_cast<hipStream_t>(stream)));
+                                   begin_launches(stream)));
 }
 
 int lbt_dispatch_bwd(const lbt_shape* s, const uint16_t* d_recv, const int32_t* slot,
@@ -253,7 +276,7 @@ int lbt_dispatch_bwd(const lbt_shape* s, const uint16_t* d_recv, const int32_t* 
   if (d.N > 0 && (!d_recv || !slot || !dx || !aligned16(d_recv) || !aligned16(dx)))
     return LBT_EINVAL;
   return hip_rc(launch_combine(d, d_recv, slot, nullptr, dx_dtype, dx,
-                               static_cast<hipStream_t>(stream)));
+                               begin_launches(stream)));
 }
 
 }  // extern "C"

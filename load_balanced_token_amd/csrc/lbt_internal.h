@@ -33,6 +33,7 @@ struct Dims {
   int E, K, R, S, H, B, blk, score_fn, renorm;
   int nh;        // E / R home experts per rank
   uint32_t nh_magic;   // ceil(2^32 / nh) for nh >= 2: e / nh = umulhi(e, nh_magic) for e < 2^16
+  uint32_t k_magic;    // ceil(2^32 / K) for K >= 2: p / K = umulhi(p, k_magic) for p < 2^16
   int N;         // R * S tokens
   long long P;   // N * K pairs
   int SK;        // S * K
@@ -60,6 +61,10 @@ hipError_t launch_route_and_scan(const Dims& d, const float* logits, const float
                                  hipStream_t st);
 hipError_t launch_plan(const Dims& d, const int32_t* counts, int32_t* plan, int32_t* status,
                        hipStream_t st);
+// route + histogram + fixed-rule plan (one launch for small batches)
+hipError_t launch_route_plan(const Dims& d, const float* logits, const float* bias, int32_t* ids,
+                             float* gates, int32_t* work, int32_t* counts, int32_t* plan,
+                             int32_t* status, hipStream_t st);
 hipError_t launch_plan_quota(const Dims& d, const int32_t* counts, int32_t* plan,
                              int32_t* status, hipStream_t st);
 hipError_t launch_align(const Dims& d, const int32_t* ids, const int32_t* work, const int32_t* plan,

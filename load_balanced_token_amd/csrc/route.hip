@@ -7,14 +7,29 @@
 
 namespace lbt {
 
-template <int V>
+template <int V, bool FULL>
 __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict__ logits,
                                                          const float* __restrict__ bias, Dims d,
                                                          int vec, int32_t* __restrict__ ids,
                                                          float* __restrict__ gates,
                                                          int32_t* __restrict__ sub_counts) {
   __shared__ RouteSmem sm;
-  route_sub<V>(logits, bias, d, vec, blockIdx.x, ids, gates, sub_counts, sm);
+  route_sub<V, FULL>(logits, bias, d, vec, blockIdx.x, ids, gates, sub_counts, sm);
+}
+
+// The same with the register budget of eight waves per SIMD (a few scalar
+// registers spill to vector lanes), so that four 512-thread workgroups fit
+// on a CU: at 32K tokens the 1024 sub-tile workgroups then run in one round
+// instead of 768 plus a tail of 256 (the compiler's own allocation, 104
+// scalar registers at V = 16, leaves room for seven waves).  Used for
+// V <= 16; wider lanes would spill vector registers.
+template <int V, bool FULL>
+__global__ __launch_bounds__(kRouteThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void k_route_o8(const float* __restrict__ logits, const float* __restrict__ bias, Dims d, int vec,
+                int32_t* __restrict__ ids, float* __restrict__ gates,
+                int32_t* __restrict__ sub_counts) {
+  __shared__ RouteSmem sm;
+  route_sub<V, FULL>(logits, bias, d, vec, blockIdx.x, ids, gates, sub_counts, sm);
 }
 
 // Histogram of caller-supplied ids, one thread per token of a sub-tile.
@@ -45,43 +60,56 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(const int32_t* __res
     sub_counts[(long long)e * d.n_sub + sub] = hist[e];
 }
 
-// One wave per expert column: exclusive prefix over the sub-tiles, written
-// at each 128-token tile's first sub-tile (tile-major, for the align step),
-// and per-source-rank sums (the load matrix) as differences of the prefix at
-// the ranks' first sub-tiles (sub-tiles never cross ranks).  The column is
-// read in coalesced 64-wide chunks, kScanBatch chunks in flight per batch;
-// each chunk is scanned across the wave and carried into the next.
-constexpr int kScanBatch = 4;
+// One wave per expert column (one workgroup each, so the columns spread over
+// the CUs): exclusive prefix over the sub-tiles, written at each 128-token
+// tile's first sub-tile (tile-major, for the align step), and per-source-rank
+// sums (the load matrix) as differences of the prefix at the ranks' first
+// sub-tiles (sub-tiles never cross ranks).  The column is read in coalesced
+// 64-wide chunks, kScanBatch chunks per batch, the next batch's loads issued
+// before the current batch is scanned; each chunk is scanned across the wave
+// and carried into the next.  Measured on MI355X (DSV3, 1024 sub-tiles per
+// column): four 64-wide chunks per batch and four columns per workgroup took
+// 6.3 us.
+constexpr int kScanBatch = 16;
 
-__global__ __launch_bounds__(256) void k_tile_scan(Dims d, int32_t* __restrict__ work,
-                                                   int32_t* __restrict__ counts) {
-  __shared__ int sPre[4][kMaxR + 1];   // per wave: prefix at each rank's first sub-tile, then the total
-  const int w = wave_id();
-  const int e = blockIdx.x * 4 + w;
-  if (e >= d.E) return;
+__global__ __launch_bounds__(kWave) void k_tile_scan(Dims d, int32_t* __restrict__ work,
+                                                     int32_t* __restrict__ counts) {
+  __shared__ int sPre[kMaxR + 1];   // prefix at each rank's first sub-tile, then the total
+  const int e = blockIdx.x;
   const int lane = lane_id();
   const int ns = d.n_sub, spr = d.spr, tpr = d.tpr, E = d.E;
   const int32_t* col = work + (long long)e * ns;
   int32_t* base = work + work_tile_base(d);
-  for (int r = lane; r <= d.R; r += kWave) sPre[w][r] = 0;   // ranks without tokens (S = 0) sum to 0
+  for (int r = lane; r <= d.R; r += kWave) sPre[r] = 0;   // ranks without tokens (S = 0) sum to 0
   __builtin_amdgcn_wave_barrier();
   // rank and sub-tile within it of this lane's current element, advanced by 64 per chunk
   int r = spr > 0 ? lane / spr : 0, j = spr > 0 ? lane - r * spr : 0;
   int carry = 0;
+  int nxt[kScanBatch];
+#pragma unroll
+  for (int u = 0; u < kScanBatch; ++u) {
+    const int i = u * kWave + lane;
+    nxt[u] = i < ns ? col[i] : 0;
+  }
   for (int c0 = 0; c0 < ns; c0 += kScanBatch * kWave) {
     int v[kScanBatch];
 #pragma unroll
-    for (int u = 0; u < kScanBatch; ++u) {
-      const int i = c0 + u * kWave + lane;
-      v[u] = i < ns ? col[i] : 0;
+    for (int u = 0; u < kScanBatch; ++u) v[u] = nxt[u];
+    if (c0 + kScanBatch * kWave < ns) {
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) {
+        const int i = c0 + (kScanBatch + u) * kWave + lane;
+        nxt[u] = i < ns ? col[i] : 0;
+      }
     }
 #pragma unroll
     for (int u = 0; u < kScanBatch; ++u) {
       const int i = c0 + u * kWave + lane;
+      if (c0 + u * kWave >= ns) break;       // wave-uniform
       const int incl = wave_incl_scan_dpp(v[u]);
       const int excl = carry + incl - v[u];
       if (i < ns) {
-        if (j == 0) sPre[w][r] = excl;
+        if (j == 0) sPre[r] = excl;
         if (j % kSubTiles == 0) base[(long long)(r * tpr + j / kSubTiles) * E + e] = excl;
       }
       carry += __builtin_amdgcn_readlane(incl, kWave - 1);
@@ -93,10 +121,10 @@ __global__ __launch_bounds__(256) void k_tile_scan(Dims d, int32_t* __restrict__
       }
     }
   }
-  if (lane == 0) sPre[w][d.R] = carry;
+  if (lane == 0) sPre[d.R] = carry;
   __builtin_amdgcn_wave_barrier();
   for (int rr = lane; rr < d.R; rr += kWave)
-    counts[(long long)rr * E + e] = sPre[w][rr + 1] - sPre[w][rr];
+    counts[(long long)rr * E + e] = sPre[rr + 1] - sPre[rr];
 }
 
 hipError_t launch_route(const Dims& d, const float* logits, const float* bias, int32_t* ids,
@@ -105,13 +133,24 @@ hipError_t launch_route(const Dims& d, const float* logits, const float* bias, i
   const int vec = route_vec(logits, d.E);
   const dim3 grid(d.n_sub), block(kRouteThreads);
   const int V = (d.E + kRowLanes - 1) / kRowLanes;
-  if (V <= 1) hipLaunchKernelGGL(k_route<1>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
-  else if (V <= 2) hipLaunchKernelGGL(k_route<2>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
-  else if (V <= 4) hipLaunchKernelGGL(k_route<4>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
-  else if (V <= 8) hipLaunchKernelGGL(k_route<8>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
-  else if (V <= 16) hipLaunchKernelGGL(k_route<16>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
-  else if (V <= 24) hipLaunchKernelGGL(k_route<24>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
-  else hipLaunchKernelGGL(k_route<32>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work);
+  // FULL: every lane holds V real experts (E = 16 V), no per-key bounds test
+#define LBT_ROUTE(KERN, VV)                                                                   \
+  do {                                                                                        \
+    if (d.E == kRowLanes * (VV))                                                              \
+      hipLaunchKernelGGL((KERN<VV, true>), grid, block, 0, st, logits, bias, d, vec, ids,     \
+                         gates, work);                                                        \
+    else                                                                                      \
+      hipLaunchKernelGGL((KERN<VV, false>), grid, block, 0, st, logits, bias, d, vec, ids,    \
+                         gates, work);                                                        \
+  } while (0)
+  if (V <= 1) LBT_ROUTE(k_route_o8, 1);
+  else if (V <= 2) LBT_ROUTE(k_route_o8, 2);
+  else if (V <= 4) LBT_ROUTE(k_route_o8, 4);
+  else if (V <= 8) LBT_ROUTE(k_route_o8, 8);
+  else if (V <= 16) LBT_ROUTE(k_route_o8, 16);
+  else if (V <= 24) LBT_ROUTE(k_route, 24);
+  else LBT_ROUTE(k_route, 32);
+#undef LBT_ROUTE
   return hipGetLastError();
 }
 
@@ -123,7 +162,7 @@ hipError_t launch_histogram(const Dims& d, const int32_t* ids, int32_t* work, in
 }
 
 hipError_t launch_tile_scan(const Dims& d, int32_t* work, int32_t* counts, hipStream_t st) {
-  hipLaunchKernelGGL(k_tile_scan, dim3((d.E + 3) / 4), dim3(256), 0, st, d, work, counts);
+  hipLaunchKernelGGL(k_tile_scan, dim3(d.E), dim3(kWave), 0, st, d, work, counts);
   return hipGetLastError();
 }
 
@@ -141,7 +180,7 @@ static bool small_batch(const Dims& d) {
   return d.N >= 1 && d.N <= kSmallTokens && (long long)d.n_sub * d.E <= kSmallHist;
 }
 
-template <int V>
+template <int V, bool FULL>
 __global__ __launch_bounds__(kRouteThreads) void k_route_small(const float* __restrict__ logits,
                                                                const float* __restrict__ bias,
                                                                Dims d, int vec,
@@ -153,20 +192,20 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_small(const float* __re
   __shared__ int hist[kSmallHist];     // [sub-tile][E]
   const int E = d.E, ns = d.n_sub, S = d.S, spr = d.spr, tpr = d.tpr;
   for (int i = threadIdx.x; i < ns * E; i += kRouteThreads) hist[i] = 0;
-  route_span<V>(logits, bias, d, vec, 0, d.N, ids, gates, rs, [&](long long t, int id) {
+  route_span<V, FULL>(logits, bias, d, vec, 0, d.N, ids, gates, rs, [&](long long t, int id) {
     const int r = (int)(t / S), j = (int)(t - (long long)r * S) / kSubTokens;
     atomicAdd(&hist[(r * spr + j) * E + id], 1);
   });
   __syncthreads();
+  // the tile prefixes align reads and the load matrix (the per-sub-tile
+  // counts are an intermediate of the two-launch path and are not written)
   int32_t* base = work + work_tile_base(d);
   for (int e = threadIdx.x; e < E; e += kRouteThreads) {
     int run = 0;
     for (int r = 0; r < d.R; ++r) {
       int sum = 0;
       for (int j = 0; j < spr; ++j) {
-        const int sub = r * spr + j;
-        const int c = hist[sub * E + e];
-        work[(long long)e * ns + sub] = c;
+        const int c = hist[(r * spr + j) * E + e];
         if (j % kSubTiles == 0) base[(long long)(r * tpr + j / kSubTiles) * E + e] = run;
         run += c;
         sum += c;
@@ -188,7 +227,15 @@ hipError_t launch_route_and_scan(const Dims& d, const float* logits, const float
   const int vec = route_vec(logits, d.E);
   const dim3 grid(1), block(kRouteThreads);
   const int V = (d.E + kRowLanes - 1) / kRowLanes;
-#define LBT_SMALL(VV) hipLaunchKernelGGL(k_route_small<VV>, grid, block, 0, st, logits, bias, d, vec, ids, gates, work, counts)
+#define LBT_SMALL(VV)                                                                      \
+  do {                                                                                     \
+    if (d.E == kRowLanes * (VV))                                                           \
+      hipLaunchKernelGGL((k_route_small<VV, true>), grid, block, 0, st, logits, bias, d,   \
+                         vec, ids, gates, work, counts);                                   \
+    else                                                                                   \
+      hipLaunchKernelGGL((k_route_small<VV, false>), grid, block, 0, st, logits, bias, d,  \
+                         vec, ids, gates, work, counts);                                   \
+  } while (0)
   if (V <= 1) LBT_SMALL(1);
   else if (V <= 2) LBT_SMALL(2);
   else if (V <= 4) LBT_SMALL(4);

@@ -27,12 +27,12 @@ constexpr int kRouteTokens = kRouteWaves * kRowsPerWave;   // tokens per pass
 constexpr int kRoutePasses = kSubTokens / kRouteTokens;
 static_assert(kRoutePasses * kRouteTokens == kSubTokens, "whole passes per sub-tile");
 
-// Order-preserving map of a finite fp32 value to u32; -0.0 maps like +0.0 so
-// the two tie (IEEE equality).  Every finite value maps above 0x007FFFFF.
+// Order-preserving map of an fp32 value (not NaN) to u32; adding +0.0 turns
+// -0.0 into +0.0 so the two tie (IEEE equality).  -inf maps to 0x007FFFFF,
+// every larger value above it.
 __device__ __forceinline__ uint32_t ordered_key(float v) {
-  uint32_t u = __float_as_uint(v);
-  if (v == 0.0f) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(v + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 // DPP lane permutations inside a 16-lane row.
@@ -46,14 +46,30 @@ __device__ __forceinline__ int dpp(int v) {
   return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
 }
 
+// The same permutation with the old value set to an identity of the
+// operation that consumes it (every lane of the row has a source, so the
+// old value is never used): the compiler then folds the move into that
+// operation as a DPP operand, one instruction per step.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_or(uint32_t v, uint32_t identity) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, 0xF, 0xF, false);
+}
+
 // Row-wide (16-lane) reductions; every lane of the row receives the result.
 __device__ __forceinline__ uint32_t row_max_u32(uint32_t x) {
-  int v = (int)x;
-  v = (int)max((uint32_t)v, (uint32_t)dpp<kDppQuadXor1>(v));
-  v = (int)max((uint32_t)v, (uint32_t)dpp<kDppQuadXor2>(v));
-  v = (int)max((uint32_t)v, (uint32_t)dpp<kDppHalfMirror>(v));
-  v = (int)max((uint32_t)v, (uint32_t)dpp<kDppRowMirror>(v));
-  return (uint32_t)v;
+  x = max(x, dpp_or<kDppQuadXor1>(x, 0u));
+  x = max(x, dpp_or<kDppQuadXor2>(x, 0u));
+  x = max(x, dpp_or<kDppHalfMirror>(x, 0u));
+  x = max(x, dpp_or<kDppRowMirror>(x, 0u));
+  return x;
+}
+
+__device__ __forceinline__ uint32_t row_min_u32(uint32_t x) {
+  x = min(x, dpp_or<kDppQuadXor1>(x, 0xFFFFFFFFu));
+  x = min(x, dpp_or<kDppQuadXor2>(x, 0xFFFFFFFFu));
+  x = min(x, dpp_or<kDppHalfMirror>(x, 0xFFFFFFFFu));
+  x = min(x, dpp_or<kDppRowMirror>(x, 0xFFFFFFFFu));
+  return x;
 }
 
 __device__ __forceinline__ float row_max_f32(float x) {
@@ -82,8 +98,9 @@ __device__ __forceinline__ double row_sum_f64(double x) {
 }
 
 // Load lane's V logits [j*V, j*V+V) of one row (j = lane within its
-// 16-lane row); vec = 4, 2 or 1 is the widest aligned load.
-template <int V>
+// 16-lane row); vec = 4, 2 or 1 is the widest aligned load.  FULL: the row
+// has 16 V logits, so no load needs a bounds test.
+template <int V, bool FULL>
 __device__ __forceinline__ void load_row(const float* __restrict__ row, int E, int e0, int vec,
                                          float (&raw)[V]) {
   if constexpr (V % 4 == 0) {
@@ -91,7 +108,7 @@ __device__ __forceinline__ void load_row(const float* __restrict__ row, int E, i
 #pragma unroll
       for (int v = 0; v < V; v += 4) {
         float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (e0 + v < E) q = *reinterpret_cast<const float4*>(row + e0 + v);
+        if (FULL || e0 + v < E) q = *reinterpret_cast<const float4*>(row + e0 + v);
         raw[v] = q.x; raw[v + 1] = q.y; raw[v + 2] = q.z; raw[v + 3] = q.w;
       }
       return;
@@ -102,38 +119,39 @@ __device__ __forceinline__ void load_row(const float* __restrict__ row, int E, i
 #pragma unroll
       for (int v = 0; v < V; v += 2) {
         float2 q = make_float2(0.f, 0.f);
-        if (e0 + v < E) q = *reinterpret_cast<const float2*>(row + e0 + v);
+        if (FULL || e0 + v < E) q = *reinterpret_cast<const float2*>(row + e0 + v);
         raw[v] = q.x; raw[v + 1] = q.y;
       }
       return;
     }
   }
 #pragma unroll
-  for (int v = 0; v < V; ++v) raw[v] = (e0 + v < E) ? row[e0 + v] : 0.f;
+  for (int v = 0; v < V; ++v) raw[v] = (FULL || e0 + v < E) ? row[e0 + v] : 0.f;
 }
 
-// Winners of each round: expert per wave, token row and k.
+// Winners of each round per wave, token row and k: expert and its key.
 struct RouteScratch {
   int s_id[kRouteWaves][kRowsPerWave][kMaxK];
+  float s_key[kRouteWaves][kRowsPerWave][kMaxK];
 };
 
 // The lane's best T keys among those that come after (tk, tv) in the order
 // (key descending, local index ascending) -- all keys when !AFTER -- sorted
-// in that order into lk/lv; unused entries hold key 0 (below every valid
-// key, which is > 0x007FFFFF).  Strict '>' keeps the lower index first on
-// equal keys.
+// in that order into lk/lv; unused entries hold -inf, below every key (keys
+// are > -inf).  Float comparison makes -0.0 and +0.0 equal; strict '>'
+// keeps the lower index first on equal keys.
 template <int V, int T, bool AFTER>
-__device__ __forceinline__ void build_list(const uint32_t (&key)[V], uint32_t tk, int tv,
-                                           uint32_t (&lk)[T], int (&lv)[T]) {
+__device__ __forceinline__ void build_list(const float (&key)[V], float tk, int tv, float (&lk)[T],
+                                           int (&lv)[T]) {
 #pragma unroll
   for (int j = 0; j < T; ++j) {
-    lk[j] = 0u;
+    lk[j] = -INFINITY;
     lv[j] = 0;
   }
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    uint32_t x = key[v];
-    if constexpr (AFTER) x = (x < tk || (x == tk && v > tv)) ? x : 0u;
+    float x = key[v];
+    if constexpr (AFTER) x = (x < tk || (x == tk && v > tv)) ? x : -INFINITY;
     bool c[T];
 #pragma unroll
     for (int j = 0; j < T; ++j) c[j] = x > lk[j];
@@ -153,17 +171,20 @@ struct RouteSmem {
   RouteScratch rs;
 };
 
-// Route tokens [t0, t0 + len), len <= kSubTokens, with kRouteThreads threads; for every
-// chosen (token, expert) pair call hist_add(t, expert).  Contains one
-// workgroup barrier (after the row loads), so state the caller set up before
-// the call (a zeroed histogram) is visible to hist_add.
-template <int V, typename HistAdd>
+// Route tokens [t0, t0 + len), len <= kSubTokens, with the first kRouteThreads
+// threads of the workgroup; for every chosen (token, expert) pair call
+// hist_add(t, expert).  Contains one workgroup barrier (after the row loads),
+// which every thread of the workgroup meets (threads past kRouteThreads do
+// nothing else), so state the caller set up before the call (a zeroed
+// histogram) is visible to hist_add.
+template <int V, bool FULL, typename HistAdd>
 __device__ __forceinline__ void route_span(const float* __restrict__ logits,
                                            const float* __restrict__ bias, const Dims& d, int vec,
                                            int t0, int len, int32_t* __restrict__ ids,
                                            float* __restrict__ gates, RouteScratch& sm,
                                            HistAdd hist_add) {
   auto& s_id = sm.s_id;
+  auto& s_key = sm.s_key;
   const int E = d.E, K = d.K;
 
   const int lane = lane_id(), wv = wave_id();
@@ -171,18 +192,20 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
   const int e0 = rl * V;
 
   // all rows of this wave first (one memory latency), then the rounds
+  const bool active = wv < kRouteWaves;
   float rows[kRoutePasses][V];
 #pragma unroll
   for (int u = 0; u < kRoutePasses; ++u) {
     const int i = (u * kRouteWaves + wv) * kRowsPerWave + row;
-    if (i < len) {
-      load_row<V>(logits + ((long long)t0 + i) * E, E, e0, vec, rows[u]);
+    if (active && i < len) {
+      load_row<V, FULL>(logits + ((long long)t0 + i) * E, E, e0, vec, rows[u]);
     } else {
 #pragma unroll
       for (int v = 0; v < V; ++v) rows[u][v] = 0.f;
     }
   }
   __syncthreads();   // the caller's histogram set-up is visible
+  if (!active) return;
 
 #pragma unroll
   for (int u = 0; u < kRoutePasses; ++u) {
@@ -191,14 +214,14 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
     if (!__any(valid)) continue;
     // keys only from here on: gates and the softmax re-read the row, so the
     // raw values do not stay live through the rounds
-    uint32_t key[V];
+    float key[V];
     if (bias != nullptr) {
 #pragma unroll
       for (int v = 0; v < V; ++v)
-        key[v] = (valid && e0 + v < E) ? ordered_key(rows[u][v] + bias[e0 + v]) : 0u;
+        key[v] = (FULL || e0 + v < E) ? rows[u][v] + bias[e0 + v] : -INFINITY;
     } else {
 #pragma unroll
-      for (int v = 0; v < V; ++v) key[v] = (valid && e0 + v < E) ? ordered_key(rows[u][v]) : 0u;
+      for (int v = 0; v < V; ++v) key[v] = (FULL || e0 + v < E) ? rows[u][v] : -INFINITY;
     }
     // Each lane keeps its best T keys sorted (key desc, local index asc);
     // a round compares list heads across the row and the winner pops.  A
@@ -206,45 +229,39 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
     // gave up last, so the order of choices is exactly the K rounds of
     // "largest untaken key, lowest expert on ties".
     constexpr int T = V < 4 ? V : 4;
-    uint32_t lk[T];
+    float lk[T];
     int lv[T];
-    build_list<V, T, false>(key, 0u, 0, lk, lv);
-    bool more = V > T && lk[T - 1] != 0u;   // the lane may hold keys past its list
+    build_list<V, T, false>(key, 0.f, 0, lk, lv);
+    bool more = V > T && lk[T - 1] != -INFINITY;   // the lane may hold keys past its list
     for (int k = 0; k < K; ++k) {
-      const uint32_t head = lk[0];
+      // the row max runs on order-preserving bits of the list heads
+      const uint32_t head = ordered_key(lk[0]);
       const uint32_t rmax = row_max_u32(head);
       const bool cand = valid && head == rmax;
-      const unsigned long long m = __ballot(cand);
-      // candidates below this lane in the wave, minus those in lower rows
-      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const int p1 = __popcll(m & 0xFFFFull), p2 = __popcll(m & 0xFFFFFFFFull),
-                p3 = __popcll(m & 0xFFFFFFFFFFFFull);
-      const int lower = row == 0 ? 0 : row == 1 ? p1 : row == 2 ? p2 : p3;
-      bool dry = false;
-      if (cand && below == lower) {        // lowest lane of the row = lowest expert
-        const uint32_t tk = lk[0];
-        const int tv = lv[0];
+      // the lowest candidate lane of the row holds the lowest expert
+      const uint32_t first = row_min_u32(cand ? (uint32_t)rl : (uint32_t)kRowLanes);
+      const bool win = cand && (uint32_t)rl == first;
+      // the winner records its expert and pops its head
+      const float tk = lk[0];
+      const int tv = lv[0];
+      if (win) {
         s_id[wv][row][k] = e0 + tv;
+        s_key[wv][row][k] = tk;
 #pragma unroll
         for (int j = 0; j + 1 < T; ++j) {
           lk[j] = lk[j + 1];
           lv[j] = lv[j + 1];
         }
-        lk[T - 1] = 0u;
-        if constexpr (V > T) {
-          dry = more && lk[0] == 0u;
-          if (dry) {
-            lk[0] = tk;                    // remember the threshold for the refill
-            lv[0] = tv;
-          }
-        }
+        lk[T - 1] = -INFINITY;
       }
       if constexpr (V > T) {
+        // a lane whose list ran dry while it may hold more keys refills
+        // from the keys after the one it just gave up (rare)
+        const bool dry = win && more && lk[0] == -INFINITY;
         if (__any(dry)) {
           if (dry) {
-            build_list<V, T, true>(key, lk[0], lv[0], lk, lv);
-            more = lk[T - 1] != 0u;
+            build_list<V, T, true>(key, tk, tv, lk, lv);
+            more = lk[T - 1] != -INFINITY;
           }
         }
       }
@@ -252,28 +269,40 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
     __builtin_amdgcn_wave_barrier();
 
     const long long t = (long long)t0 + i;
-    // raw logits are read back from the row just loaded (cache hits)
+    // Without a selection bias the keys are the raw logits, so the gates
+    // need no second read of the row; with one, the raw values are read
+    // back from the row just loaded (cache hits).
     const float* lrow = logits + (valid ? t : (long long)t0) * E;
+    const bool raw_keys = bias == nullptr;
+    auto logit_of = [&](int kk) -> double {
+      return raw_keys ? (double)s_key[wv][row][kk] : (double)lrow[s_id[wv][row][kk]];
+    };
     double mx = 0.0, denom = 1.0;
     if (d.score_fn == LBT_SOFTMAX) {
       float raw[V];
-      load_row<V>(lrow, E, e0, vec, raw);
+      if (raw_keys) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) raw[v] = key[v];   // -inf past E
+      } else {
+        load_row<V, FULL>(lrow, E, e0, vec, raw);
+#pragma unroll
+        for (int v = 0; v < V; ++v) raw[v] = (FULL || e0 + v < E) ? raw[v] : -INFINITY;
+      }
       float m = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < V; ++v)
-        if (e0 + v < E) m = fmaxf(m, raw[v]);
+      for (int v = 0; v < V; ++v) m = fmaxf(m, raw[v]);
       mx = (double)row_max_f32(m);
       double s = 0.0;
 #pragma unroll
       for (int v = 0; v < V; ++v)
-        if (e0 + v < E) s += exp((double)raw[v] - mx);
+        if (FULL || e0 + v < E) s += exp((double)raw[v] - mx);
       denom = row_sum_f64(s);
     }
     double gsum = 1.0;
     if (d.renorm) {
       double part = 0.0;
       for (int kk = rl; kk < K; kk += kRowLanes) {
-        const double lg = valid ? (double)lrow[s_id[wv][row][kk]] : 0.0;
+        const double lg = valid ? logit_of(kk) : 0.0;
         part += d.score_fn == LBT_SIGMOID ? 1.0 / (1.0 + exp(-lg)) : exp(lg - mx) / denom;
       }
       gsum = row_sum_f64(part);
@@ -281,7 +310,7 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
     if (valid) {
       for (int kk = rl; kk < K; kk += kRowLanes) {
         const int id = s_id[wv][row][kk];
-        const double lg = (double)lrow[id];
+        const double lg = logit_of(kk);
         double g = d.score_fn == LBT_SIGMOID ? 1.0 / (1.0 + exp(-lg)) : exp(lg - mx) / denom;
         if (d.renorm) g = g / gsum;
         ids[t * K + kk] = id;
@@ -295,7 +324,7 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
 
 // Route the tokens of sub-tile `sub` (kRouteThreads threads) and write its
 // expert histogram to sub_counts[e][sub].
-template <int V>
+template <int V, bool FULL>
 __device__ __forceinline__ void route_sub(const float* __restrict__ logits,
                                           const float* __restrict__ bias, const Dims& d, int vec,
                                           int sub, int32_t* __restrict__ ids,
@@ -306,7 +335,7 @@ __device__ __forceinline__ void route_sub(const float* __restrict__ logits,
   const int t0 = r * d.S + j * kSubTokens;
   const int len = min(kSubTokens, d.S - j * kSubTokens);
   for (int e = threadIdx.x; e < d.E; e += kRouteThreads) hist[e] = 0;
-  route_span<V>(logits, bias, d, vec, t0, len, ids, gates, sm.rs,
+  route_span<V, FULL>(logits, bias, d, vec, t0, len, ids, gates, sm.rs,
                 [&](long long, int id) { atomicAdd(&hist[id], 1); });
   __syncthreads();
   for (int e = threadIdx.x; e < d.E; e += kRouteThreads)

@@ -12,131 +12,196 @@
 // reduce_grad adds them into the home parameter gradients and clears them).
 // [AlignSort] (the gradient of unpermute is a permute).
 //
-// All three kernels are HBM-bound streams.  Prefetch reads each rank's
-// slotted replicas from its segment table (n_slots, seg_expert); reduce_grad
-// walks the replica-segment table (piece_*), whose weight-row column marks
-// the slotted replicas; every index taken from the plan is bounds-checked
-// before it addresses memory.
+// All three kernels are HBM-bound streams.  Prefetch and reduce_grad walk
+// the replica-segment table (piece_*), whose weight-row column marks the
+// slotted replicas, grouped by expert so that each home row is read once;
+// every index taken from the plan is bounds-checked before it addresses
+// memory.
 #include "rows.h"
 
 namespace lbt {
 
 constexpr int kCopyThreads = 256;
-constexpr int kRedUnroll = 4;                                       // float4 per thread
-constexpr long long kRedTile = (long long)kCopyThreads * kRedUnroll * 4;       // 4096 floats
-constexpr int kStreamGroups = 2048;                                 // persistent grid
-constexpr int kMaxSlots = 1024;                                     // slots per rank (B) held in LDS
+constexpr int kCopyWaves = kCopyThreads / kWave;
+
+// ---- the slotted replicas, grouped by expert --------------------------------
+// Replica segments are in line order, and an expert's overflow is one
+// interval of the line, so all segments of one expert are consecutive: a
+// "run".  A segment is slotted when its weight row is E + j with j < B.  The
+// first slotted segment of each run is its head; the workgroup of rank y
+// handles the heads that lie on rank y.  Every index taken from the plan is
+// checked before it addresses memory.
+struct SlotRuns {
+  int pe[kMaxPieces], pr[kMaxPieces], pw[kMaxPieces];
+  int head[kMaxPieces];
+  int wcnt[kCopyWaves];
+};
+
+__device__ __forceinline__ bool slotted(const SlotRuns& s, int p, const Dims& d) {
+  const int w = s.pw[p], r = s.pr[p], e = s.pe[p];
+  return w >= d.E && w < d.E + d.B && r >= 0 && r < d.R && e >= 0 && e < d.E;
+}
+
+// Load the segment table and list, in ascending segment order, the heads on
+// rank y (the same list in every workgroup of rank y).  Returns the head
+// count; *nP_out receives the number of segments.
+__device__ __forceinline__ int slotted_heads(const int32_t* __restrict__ plan, const Dims& d, int y,
+                                             SlotRuns& s, int* nP_out) {
+  const PlanLayout& pl = d.pl;
+  const int mp = pl.max_pieces;
+  const int nP = min(max(plan[pl.hdr + LBT_HDR_N_PIECES], 0), mp);
+  for (int g = threadIdx.x; g < mp; g += kCopyThreads) {   // every entry: no wait on nP
+    s.pe[g] = plan[pl.piece_expert + g];
+    s.pr[g] = plan[pl.piece_rank + g];
+    s.pw[g] = plan[pl.piece_wrow + g];
+  }
+  __syncthreads();
+  int n = 0;
+  for (int g0 = 0; g0 < nP; g0 += kCopyThreads) {
+    const int g = g0 + threadIdx.x;
+    bool h = g < nP && s.pr[g] == y && slotted(s, g, d);
+    if (h) {
+      const int e = s.pe[g];
+      for (int p = g - 1; p >= 0 && s.pe[p] == e; --p)
+        if (slotted(s, p, d)) {
+          h = false;
+          break;
+        }
+    }
+    const unsigned long long m = __ballot(h);
+    if (lane_id() == 0) s.wcnt[wave_id()] = __popcll(m);
+    __syncthreads();
+    int before = n, total = 0;
+#pragma unroll
+    for (int w = 0; w < kCopyWaves; ++w) {
+      before += w < wave_id() ? s.wcnt[w] : 0;
+      total += s.wcnt[w];
+    }
+    if (h)
+      s.head[before + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = g;
+    n += total;
+    __syncthreads();
+  }
+  *nP_out = nP;
+  return n;
+}
 
 // ---- prefetch -----------------------------------------------------------------
-// Grid (4 KiB tile of a weight row, rank r): the workgroup copies that tile
-// of every slotted replica of rank r -- slot j < n_slots[r] holds the
-// expert at entry E/R + j of r's segment table -- one 16-byte chunk per
-// thread per slot, two slots in flight.  Sized without the slot count
-// (unknown on the host), a rank with few slots costs only short
-// workgroups.  Measured on MI355X against the earlier persistent grid of
-// 32 KiB items: DSV3 418 -> 405 us, Kimi-K3 607 -> 549 us.
-constexpr int kPrefetchTile = 4096;
-constexpr int kPrefetchUnroll = 2;
+// Grid (4 KiB tile of a weight row, rank y * subs + sub): the workgroup takes
+// heads sub, sub + subs, ... of rank y; for each it reads the tile of the
+// expert's home row once (16 bytes per thread) and stores it into every
+// slotted segment of the run, so a home row replicated on several ranks is
+// read once.  One 16-byte chunk per thread per head: short-lived waves with
+// one load each are the fastest copy shape measured on MI355X.
+constexpr int kPrefetchTile = kCopyThreads * 16;
 
 __global__ __launch_bounds__(kCopyThreads) void k_prefetch(const int32_t* __restrict__ plan, Dims d,
+                                                           int subs,
                                                            const char* __restrict__ weights,
                                                            char* __restrict__ slots,
                                                            long long row_bytes) {
-  __shared__ int sE[kMaxSlots];
-  const PlanLayout pl = d.pl;
-  const int r = blockIdx.y;
-  const int n = min(max(plan[pl.n_slots + r], 0), min(d.B, pl.max_seg - d.nh));
-  for (int j = threadIdx.x; j < n; j += kCopyThreads)
-    sE[j] = plan[pl.seg_expert + (long long)r * pl.max_seg + d.nh + j];
-  __syncthreads();
-  const long long off = (long long)blockIdx.x * kPrefetchTile + threadIdx.x * 16;
-  if (off + 16 > row_bytes) return;
-  for (int j0 = 0; j0 < n; j0 += kPrefetchUnroll) {
-    u32x4 v[kPrefetchUnroll];
+  __shared__ SlotRuns s;
+  const int y = blockIdx.y / subs, sub = blockIdx.y - y * subs;
+  int nP;
+  const int nh = slotted_heads(plan, d, y, s, &nP);
+  const long long tile0 = (long long)blockIdx.x * kPrefetchTile;
+  const uint32_t lo = threadIdx.x * 16u;
+  if (tile0 + lo + 16 > row_bytes) return;
+  for (int i = sub; i < nh; i += 2 * subs) {
+    const int h0 = s.head[i];
+    const int h1 = i + subs < nh ? s.head[i + subs] : -1;
+    const u32x4 v0 = *at_bytes<u32x4>(weights + (long long)s.pe[h0] * row_bytes + tile0, lo);
+    u32x4 v1 = {0u, 0u, 0u, 0u};
+    if (h1 >= 0) v1 = *at_bytes<u32x4>(weights + (long long)s.pe[h1] * row_bytes + tile0, lo);
 #pragma unroll
-    for (int u = 0; u < kPrefetchUnroll; ++u) {
-      const int e = j0 + u < n ? sE[j0 + u] : -1;
-      if (e >= 0 && e < d.E) v[u] = *at_bytes<u32x4>(weights + (long long)e * row_bytes, off);
-    }
-#pragma unroll
-    for (int u = 0; u < kPrefetchUnroll; ++u) {
-      const int e = j0 + u < n ? sE[j0 + u] : -1;
-      if (e >= 0 && e < d.E)
-        *at_bytes<u32x4>(slots + ((long long)r * d.B + j0 + u) * row_bytes, off) = v[u];
+    for (int u = 0; u < 2; ++u) {
+      const int h = u == 0 ? h0 : h1;
+      if (h < 0) continue;
+      const int e = s.pe[h];
+      for (int p = h; p < nP && s.pe[p] == e; ++p) {
+        if (!slotted(s, p, d)) continue;
+        char* dst = slots + ((long long)s.pr[p] * d.B + (s.pw[p] - d.E)) * row_bytes + tile0;
+        *at_bytes<u32x4>(dst, lo) = u == 0 ? v0 : v1;
+      }
     }
   }
 }
+
+// Workgroups per (tile, rank).  More than one spreads a rank's heads over
+// several workgroups, but every workgroup pays the segment-table prologue:
+// measured on MI355X (DSV3, 38 slots) with 8 per rank, prefetch 565 us and
+// reduce_grad 1886 us against about 400 and 1710 with one.
+static int copy_subs(const Dims&) { return 1; }
 
 hipError_t launch_prefetch(const Dims& d, const int32_t* plan, const void* weights, void* slots,
                            long long row_bytes, hipStream_t st) {
   if (d.B == 0 || d.R == 0) return hipSuccess;
   const long long tiles = (row_bytes + kPrefetchTile - 1) / kPrefetchTile;
-  if (tiles > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_prefetch, dim3((unsigned)tiles, (unsigned)d.R), dim3(kCopyThreads), 0, st,
-                     plan, d, static_cast<const char*>(weights), static_cast<char*>(slots),
-                     row_bytes);
+  const int subs = copy_subs(d);
+  if (tiles > 0x7FFFFFFFLL || (long long)d.R * subs > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_prefetch, dim3((unsigned)tiles, (unsigned)(d.R * subs)), dim3(kCopyThreads),
+                     0, st, plan, d, subs, static_cast<const char*>(weights),
+                     static_cast<char*>(slots), row_bytes);
   return hipGetLastError();
 }
 
 // ---- reduce_grad --------------------------------------------------------------
-// Work item = (replica segment g that starts its expert's run on the line,
-// tile of 4096 floats).  The run's slotted segments are added to the home
-// gradient in line order and cleared; a run with no slotted segment writes
-// nothing.
+// Grid (tile of 1024 floats, rank y * subs + sub), heads taken as in the
+// prefetch: for each expert run, the tile of the home gradient and of the
+// run's slotted segments (up to kRedBatch at a time, all loads in flight)
+// are loaded, added in line order (one fp32 addition each, so the result is
+// the oracle's bit for bit), the slots cleared and the sum stored.
+constexpr long long kRedTile = (long long)kCopyThreads * 4;   // floats
+constexpr int kRedBatch = 4;
+
 __global__ __launch_bounds__(kCopyThreads) void k_reduce_grad(const int32_t* __restrict__ plan,
-                                                              Dims d, float* __restrict__ slot_grads,
+                                                              Dims d, int subs,
+                                                              float* __restrict__ slot_grads,
                                                               float* __restrict__ grads,
-                                                              long long row_elems, long long tiles) {
-  const PlanLayout pl = d.pl;
-  const int nP = min(plan[pl.hdr + LBT_HDR_N_PIECES], pl.max_pieces);
-  const long long items = (long long)nP * tiles;
-  for (long long it = blockIdx.x; it < items; it += gridDim.x) {
-    const int g = (int)(it / tiles);
-    const long long off = (it - (long long)g * tiles) * kRedTile;
-    const int e = plan[pl.piece_expert + g];
-    if (e < 0 || e >= d.E) continue;
-    if (g > 0 && plan[pl.piece_expert + g - 1] == e) continue;   // not the first of its run
-    const long long n = min(kRedTile, row_elems - off);
-    float* home = grads + (long long)e * row_elems + off;
-    f32x4 acc[kRedUnroll];
+                                                              long long row_elems) {
+  __shared__ SlotRuns s;
+  const int y = blockIdx.y / subs, sub = blockIdx.y - y * subs;
+  int nP;
+  const int nh = slotted_heads(plan, d, y, s, &nP);
+  const long long tile0 = (long long)blockIdx.x * kRedTile;
+  const uint32_t lo = threadIdx.x * 16u;
+  if (tile0 + threadIdx.x * 4 + 4 > row_elems) return;
+  for (int i = sub; i < nh; i += subs) {
+    const int h = s.head[i];
+    const int e = s.pe[h];
+    float* home = grads + (long long)e * row_elems + tile0;
+    f32x4 acc = *at_bytes<f32x4>(home, lo);
+    int p = h;
+    while (p < nP && s.pe[p] == e) {
+      float* sg[kRedBatch];
+      int n = 0;
+      for (; p < nP && s.pe[p] == e && n < kRedBatch; ++p)
+        if (slotted(s, p, d))
+          sg[n++] = slot_grads + ((long long)s.pr[p] * d.B + (s.pw[p] - d.E)) * row_elems + tile0;
+      f32x4 v[kRedBatch];
 #pragma unroll
-    for (int u = 0; u < kRedUnroll; ++u) {
-      const uint32_t q = (uint32_t)(u * kCopyThreads + threadIdx.x) * 4u;
-      acc[u] = q < n ? *at_bytes<f32x4>(home, q * 4u) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    bool any = false;
-    for (int p = g; p < nP && plan[pl.piece_expert + p] == e; ++p) {
-      const int j = plan[pl.piece_wrow + p] - d.E;
-      const int r = plan[pl.piece_rank + p];
-      if (j < 0 || j >= d.B || r < 0 || r >= d.R) continue;       // remote: no slot
-      float* sg = slot_grads + ((long long)r * d.B + j) * row_elems + off;
+      for (int u = 0; u < kRedBatch; ++u)
+        if (u < n) v[u] = *at_bytes<f32x4>(sg[u], lo);
 #pragma unroll
-      for (int u = 0; u < kRedUnroll; ++u) {
-        const uint32_t q = (uint32_t)(u * kCopyThreads + threadIdx.x) * 4u;
-        if (q < n) {
-          acc[u] += *at_bytes<f32x4>(sg, q * 4u);
-          *at_bytes<f32x4>(sg, q * 4u) = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < kRedBatch; ++u)
+        if (u < n) {
+          acc += v[u];
+          *at_bytes<f32x4>(sg[u], lo) = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-      }
-      any = true;
     }
-    if (!any) continue;
-#pragma unroll
-    for (int u = 0; u < kRedUnroll; ++u) {
-      const uint32_t q = (uint32_t)(u * kCopyThreads + threadIdx.x) * 4u;
-      if (q < n) *at_bytes<f32x4>(home, q * 4u) = acc[u];
-    }
+    *at_bytes<f32x4>(home, lo) = acc;
   }
 }
 
 hipError_t launch_reduce_grad(const Dims& d, const int32_t* plan, float* slot_grads, float* grads,
                               long long row_elems, hipStream_t st) {
-  if (d.B == 0) return hipSuccess;
+  if (d.B == 0 || d.R == 0) return hipSuccess;
   const long long tiles = (row_elems + kRedTile - 1) / kRedTile;
-  const long long items = (long long)d.pl.max_pieces * tiles;
-  const int grid = (int)(items < kStreamGroups ? items : kStreamGroups);
-  hipLaunchKernelGGL(k_reduce_grad, dim3(grid), dim3(kCopyThreads), 0, st, plan, d, slot_grads,
-                     grads, row_elems, tiles);
+  const int subs = copy_subs(d);
+  if (tiles > 0x7FFFFFFFLL || (long long)d.R * subs > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_reduce_grad, dim3((unsigned)tiles, (unsigned)(d.R * subs)),
+                     dim3(kCopyThreads), 0, st, plan, d, subs, slot_grads, grads, row_elems);
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(binding.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.lbt_version() == 3
+    assert L.lbt_version() == 4
 
 
 def test_sizes_match_oracle_capacity_for_every_workload():
@@ -84,6 +84,10 @@ def test_host_checks_reject_bad_pointers_before_any_launch():
     assert L.lbt_plan_quota(ctypes.byref(sh), None, P(0x1000), None, None) == -1
     assert L.lbt_plan_quota(ctypes.byref(sh), P(0x1000), None, None, None) == -1
     assert L.lbt_route_topk(ctypes.byref(sh), None, None, P(1), P(2), P(3), P(4), None) == -1
+    assert L.lbt_route_plan(ctypes.byref(sh), P(1), None, P(1), P(2), P(3), P(4), None, None,
+                            None) == -1
+    assert L.lbt_route_plan(ctypes.byref(sh), None, None, P(1), P(2), P(3), P(4), P(5), None,
+                            None) == -1
     assert L.lbt_align_sort(ctypes.byref(sh), P(1), P(2), None, P(3), P(4), P(5), P(6), None, None) == -1
     assert L.lbt_histogram(None, P(1), P(2), P(3), None, None) == -1
     # training side: row sizes, null and misaligned pointers

@@ -135,47 +135,84 @@ def test_dispatch_combine_parity_full_rows(name, S):
 
 
 @pytest.mark.parametrize("name", ["dsv3", "wideep", "kimi", "moonep"])
-def test_dispatch_combine_full_size_sampled(name):
+def test_dispatch_combine_full_size_every_row(name):
     """Full-size dispatch + combine in the launch configuration the benchmark
-    times; the oracle recomputes sampled rows one by one."""
+    times.  Every one of the P dispatched rows is compared bitwise with its
+    source row x[f // K] by device-side gathers (torch's, not the library's),
+    every padding row below a rank's padded end keeps its sentinel, and every
+    one of the N*H combine outputs (identity expert) is checked against
+    x * sum_k g within 1e-6 * sum_k |g * out|; 256 sampled tokens are also
+    recomputed by the oracle from the host.  At the DSV3 shape the combine
+    is repeated on a random expert-output buffer, checked against the
+    oracle's combine on sampled tokens."""
     t = gu.torch()
     w = WORKLOADS[name]
-    print(f"[parity] sampled move {name}", flush=True)
+    print(f"[parity] full-size move {name}", flush=True)
     logits = router_logits(w, 0)
     res = gu.run_front(gu.shape_of(w), logits)
     ref = gu.run_oracle(w, logits)
     gu.check_align(res, ref, w.R, res["sizes"]["C"])
     path, C = res["path"], res["sizes"]["C"]
     x = t.empty((w.N, w.H), dtype=t.int16, device="cuda")
-    from workloads.gen import X_CHUNK, x_chunk
+    from workloads.gen import X_CHUNK, x_chunk, device_normal_bf16
     for c in range((w.N + X_CHUNK - 1) // X_CHUNK):
         blk = x_chunk(w, 0, c)
         x[c * X_CHUNK: c * X_CHUNK + blk.shape[0]] = gu.h2d(blk)
     recv = t.full((w.R * C, w.H), 0x7F7F, dtype=t.int16, device="cuda")
-    path.dispatch(x, res["dev"]["slot"], recv)
+    slot_d = res["dev"]["slot"]
+    path.dispatch(x, slot_d, recv)
     y = t.empty((w.N, w.H), dtype=t.float32, device="cuda")
     gates32 = ref["gates"].astype(np.float32)
-    path.combine(recv, res["dev"]["slot"], gu.h2d(gates32), y)
+    g_d = gu.h2d(gates32)
+    path.combine(recv, slot_d, g_d, y)
     t.cuda.synchronize()
+    slot = ref["align"]["slot"]
+    assert (slot >= 0).all()
+    # every dispatched row, bitwise, in chunks of pairs
+    step = 8192
+    for f0 in range(0, w.P, step):
+        f1 = min(w.P, f0 + step)
+        got = recv.index_select(0, slot_d[f0:f1].long())
+        src = t.arange(f0, f1, device="cuda", dtype=t.int64) // w.K
+        assert t.equal(got, x.index_select(0, src)), f"dispatch rows of pairs [{f0}, {f1})"
+    # every padding row below a rank's padded end is untouched
+    sid = ref["align"]["sorted_ids"]
+    pad_rows = np.nonzero(sid == w.P)[0]
+    for i0 in range(0, pad_rows.size, step):
+        rows = t.from_numpy(pad_rows[i0: i0 + step]).cuda()
+        assert bool((recv.index_select(0, rows) == 0x7F7F).all()), "padding row written"
+    assert (ref["plan"]["n_rows_padded"] <= C).all()
+    # every combine output: y = x * sum_k g (gates are sigmoid or softmax, so positive)
+    gsum = g_d.double().sum(dim=1)
+    for t0 in range(0, w.N, 2048):
+        t1 = min(w.N, t0 + 2048)
+        xb = (x[t0:t1].int() & 0xFFFF) << 16
+        want = xb.view(t.float32).double() * gsum[t0:t1, None]
+        err = (y[t0:t1].double() - want).abs()
+        assert bool((err <= gu.COMBINE_RTOL * want.abs() + 1e-30).all()), \
+            f"combine tokens [{t0}, {t1})"
+    # sampled tokens recomputed by the oracle from host copies of x
     rng = np.random.default_rng(123)
     tokens = np.sort(rng.choice(w.N, size=256, replace=False))
     xs = activation_rows(w, tokens, 0)
-    slot = ref["align"]["slot"]
     for i, tok in enumerate(tokens):
         rows = slot[tok * w.K:(tok + 1) * w.K]
         got = gu.d2h(recv[t.from_numpy(rows).cuda()])
         assert (got == xs[i][None, :]).all(), f"token {tok}"
-    # padding rows keep the sentinel
-    nrp = ref["plan"]["n_rows_padded"]
-    sid = ref["align"]["sorted_ids"]
-    pad_rows = np.nonzero(sid == w.P)[0]
-    if pad_rows.size:
-        pick = rng.choice(pad_rows, size=min(256, pad_rows.size), replace=False)
-        assert (gu.d2h(recv[t.from_numpy(pick).cuda()]) == 0x7F7F).all()
-    assert (nrp <= C).all()
     yh = y[t.from_numpy(tokens).cuda()].cpu().numpy().astype(np.float64)
     want = oracle.bf16_to_f64(xs) * gates32[tokens].astype(np.float64).sum(axis=1)[:, None]
     assert (np.abs(yh - want) <= gu.COMBINE_RTOL * np.abs(want) + 1e-30).all()
+    if name == "dsv3":
+        # a random expert output in the receive layout, drawn on the device
+        del x
+        out = device_normal_bf16((w.R * C, w.H), 11, "cuda")
+        path.combine(out, slot_d, g_d, y)
+        t.cuda.synchronize()
+        yref, mag = oracle.combine(lambda rows: gu.d2h(out[t.from_numpy(rows).cuda()]), slot,
+                                   gates32, w.K, tokens=tokens)
+        err = np.abs(y[t.from_numpy(tokens).cuda()].cpu().numpy().astype(np.float64) - yref)
+        assert (err <= gu.COMBINE_RTOL * mag + 1e-30).all(), \
+            f"combine (random out) max err/mag {(err / np.maximum(mag, 1e-30)).max()}"
 
 
 def test_recv_views_zero_copy_and_clones():
@@ -432,6 +469,44 @@ def test_bad_arguments_rejected():
         path.dispatch(xs, buf["slot"], buf["recv"])
 
 
+def test_stale_hip_error_is_not_reported_by_a_later_call():
+    """An error left in the thread's HIP last-error state by an earlier,
+    unrelated HIP call (here hipSetDevice on a device that does not exist,
+    made through the same HIP runtime the library uses) is not returned by
+    the next lbt call: route (two launches), plan and align launch and return
+    LBT_OK, and their outputs equal the oracle's.  Every buffer is allocated
+    before the error is left behind, so the library's call is the first HIP
+    call after it."""
+    import ctypes
+    t = gu.torch()
+    import load_balanced_token_amd as lbt
+    lbt.lib()
+    paths = sorted({l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l})
+    assert len(paths) == 1, paths
+    hip = ctypes.CDLL(paths[0])
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    w = WORKLOADS["dsv3"].with_(S=64, H=64)             # 16 sub-tiles: the two-launch route
+    logits = router_logits(w, 0)
+    path = lbt.Path(gu.shape_of(w))
+    buf = path.alloc()
+    buf["status"].zero_()
+    lg = gu.h2d(logits)
+    stream = t.cuda.current_stream()
+    t.cuda.synchronize()
+    assert hip.hipSetDevice(9999) != 0                  # leaves hipErrorInvalidDevice behind
+    path.route_topk(lg, buf["ids"], buf["gates"], buf["counts"], buf["work"], stream=stream)
+    path.plan_balance(buf["counts"], buf["plan"], buf["status"], stream=stream)
+    path.align_sort(buf["ids"], buf["work"], buf["plan"], buf["slot"], buf["sorted_ids"],
+                    buf["block_wrow"], buf["block_expert"], buf["status"], stream=stream)
+    t.cuda.synchronize()
+    assert lbt.lib().lbt_last_hip_error().decode() == "hipSuccess"
+    ref = gu.run_oracle(w, logits)
+    assert np.array_equal(gu.d2h(buf["ids"]), ref["ids"])
+    assert np.array_equal(gu.d2h(buf["counts"]), ref["counts"])
+    assert np.array_equal(gu.d2h(buf["slot"]), ref["align"]["slot"])
+    assert buf["status"].item() == 0
+
+
 def test_deterministic_rerun():
     t = gu.torch()
     w = WORKLOADS["wideep"]
@@ -448,8 +523,10 @@ def test_deterministic_rerun():
 
 
 def test_graph_capture_replays_match_eager():
-    """The whole step captured in a HIP graph: every replay (fresh routing
-    each time, eager work and syncs in between) equals the eager run."""
+    """The whole step captured in a HIP graph on a fixed input buffer: every
+    replay (fresh routing copied in before it, outside the graph, with eager
+    work and syncs in between) equals the eager run.  The routing of each
+    replay is chosen on the host, so no device-side index is involved."""
     import load_balanced_token_amd as lbt
     t = gu.torch()
     w = WORKLOADS["decode16"].with_(H=512)
@@ -457,30 +534,26 @@ def test_graph_capture_replays_match_eager():
     buf = path.alloc()
     buf["status"].zero_()
     n = 4
-    all_logits = t.stack([gu.h2d(router_logits(w, i)) for i in range(n)])
+    all_logits = [gu.h2d(router_logits(w, i)) for i in range(n)]
     x = gu.h2d(activations(w, 0))
-    idx = t.zeros(1, dtype=t.int64, device="cuda")
-    cur = t.empty((1, w.N, w.E), dtype=t.float32, device="cuda")
+    cur = t.empty((w.N, w.E), dtype=t.float32, device="cuda")
+    cur.copy_(all_logits[0])
     keys = ("ids", "gates", "counts", "plan", "slot", "block_wrow", "y")
-
-    def body():
-        t.index_select(all_logits, 0, idx, out=cur)
-        path.step(cur[0], x, buf)
-        idx.add_(1)
 
     s = t.cuda.Stream()
     s.wait_stream(t.cuda.current_stream())
     with t.cuda.stream(s):
-        body()
+        path.step(cur, x, buf)                          # warm-up outside the graph
     t.cuda.current_stream().wait_stream(s)
     t.cuda.synchronize()
     g = t.cuda.CUDAGraph()
     with t.cuda.graph(g, stream=s):
-        body()
-    idx.zero_()
+        path.step(cur, x, buf)
     t.cuda.synchronize()
     ref_path = lbt.Path(gu.shape_of(w))
     for i in range(n):
+        cur.copy_(all_logits[i])                        # host-chosen routing, outside the graph
+        t.cuda.synchronize()
         g.replay()
         t.cuda.synchronize()
         got = {k: buf[k].clone() for k in keys}
@@ -641,3 +714,56 @@ def test_corrupt_plan_is_flagged_not_followed(planner):
     assert int(st.item()) & ST_CAPACITY
     assert ((s == -1) | ((s >= 0) & (s < w.R * z["C"]))).all()
     assert (s == -1).any()
+
+
+# --------------------------------------------------------------------------- fused front
+@pytest.mark.parametrize("case", [
+    ("decode1", {}), ("decode1", {"E": 384, "R": 8}), ("decode1", {"E": 512, "R": 16, "K": 16}),
+    ("decode1", {"S": 4}), ("decode1", {"S": 3, "R": 4, "E": 40, "K": 6}),
+    ("tiny", {"S": 8}), ("tiny", {"S": 5, "R": 2}),
+    ("decode16", {}), ("tiny", {}),              # past 32 tokens: the separate launches
+])
+@pytest.mark.parametrize("variant", ["plain", "bias_renorm"])
+def test_route_plan_matches_separate_calls(case, variant):
+    """lbt_route_plan gives bit for bit the outputs of lbt_route_topk followed
+    by lbt_plan_balance (ids, gates, counts, the tile offsets align reads,
+    the whole plan blob and the status), for batches that take the one-launch
+    small-batch kernel and for larger ones, and both equal the oracle."""
+    import load_balanced_token_amd as lbt
+    t = gu.torch()
+    name, over = case
+    w = WORKLOADS[name].with_(**over)
+    renorm = 1 if variant == "bias_renorm" else 0
+    logits = router_logits(w, 3)
+    rng = np.random.default_rng(5)
+    bias = rng.standard_normal(w.E).astype(np.float32) if variant == "bias_renorm" else None
+    shape = gu.shape_of(w, renorm=renorm)
+    path = lbt.Path(shape)
+    a, b = path.alloc(), path.alloc()
+    for k in ("recv", "y"):
+        del a[k], b[k]
+    a["status"].zero_()
+    b["status"].fill_(-1)
+    lg = gu.h2d(logits)
+    sb = None if bias is None else gu.h2d(bias)
+    path.route_topk(lg, a["ids"], a["gates"], a["counts"], a["work"], sel_bias=sb)
+    path.plan_balance(a["counts"], a["plan"], a["status"])
+    path.route_plan(lg, b["ids"], b["gates"], b["counts"], b["work"], b["plan"], b["status"],
+                    sel_bias=sb)
+    t.cuda.synchronize()
+    for k in ("ids", "gates", "counts", "plan", "status"):
+        assert t.equal(a[k], b[k]), k
+    z = path.sizes
+    lo = w.E * w.R * -(-w.S // 32)                      # tile offsets follow the sub-tile counts
+    assert t.equal(a["work"][lo: lo + z["n_tiles"] * w.E], b["work"][lo: lo + z["n_tiles"] * w.E])
+    ref = gu.run_oracle(w, logits, sel_bias=bias, renorm=bool(renorm))
+    res = {"ids": gu.d2h(b["ids"]), "gates": gu.d2h(b["gates"]), "counts": gu.d2h(b["counts"])}
+    gu.check_route(res, ref)
+    pf = lbt.plan_fields(gu.d2h(b["plan"]), z, w.R, w.E)
+    gu.check_plan(pf, ref["plan"], w.P)
+    # and align on the fused outputs
+    path.align_sort(b["ids"], b["work"], b["plan"], b["slot"], b["sorted_ids"], b["block_wrow"],
+                    b["block_expert"], b["status"])
+    t.cuda.synchronize()
+    out = {k: gu.d2h(b[k]) for k in ("slot", "sorted_ids", "block_wrow", "block_expert", "status")}
+    gu.check_align(out, ref, w.R, z["C"])

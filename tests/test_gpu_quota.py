@@ -173,3 +173,26 @@ def test_quota_inconsistent_counts_flagged():
     path.plan_quota(counts, buf["plan"], buf["status"])
     t.cuda.synchronize()
     assert int(buf["status"].item()) & lbt.ST_BADCOUNT
+
+
+@pytest.mark.parametrize("E,R,S,B,x,layer", [
+    (130, 65, 24, 2, 4, 0),    # tau* = 470 > S*K = 192: found inside the first batch
+    (130, 65, 24, 1, 8, 0),    # tau* = 1353: more than 1024 candidates, found in the second batch
+    (130, 65, 24, 1, 8, 1),    # no qualifying tau up to 8*S*K: both batches, tau = tau_max
+    (256, 128, 16, 2, 2, 0),   # R = 128: tau* = 142
+    (256, 128, 16, 2, 2, 1),   # tau* = 210
+    (256, 128, 16, 1, 2, 0),   # infeasible: the whole range searched, remote fallback
+])
+def test_quota_search_past_one_wave_of_ranks(E, R, S, B, x, layer):
+    """More than 64 ranks, where the wave-per-candidate first stage is skipped
+    and the per-thread batches walk the ranks: thresholds above S*K, a search
+    longer than one batch of 1024 candidates, and a range with no qualifying
+    threshold; plan and placement bit-exact with the oracle."""
+    w = WORKLOADS["dsv3"].with_(E=E, R=R, K=8, S=S, H=64, blk=8)
+    w, res, ref = _quota_pair(w, B, x * w.SK, layer)
+    print(f"[quota] R={R} B={B} tau_max={x}SK layer={layer}: tau={ref['plan']['tau']}", flush=True)
+    assert ref["plan"]["tau"] > w.SK
+    gu.check_route(res, ref)
+    gu.check_plan(res["plan_fields"], ref["plan"], w.P)
+    gu.check_align(res, ref, w.R, res["sizes"]["C"])
+    _full_move_check(w, res, ref, activations(w, layer))

@@ -221,3 +221,20 @@ def random_expert_out(w: Workload, n_rows: int, H: int | None = None, seed: int 
     """bf16 bits of a random stand-in for an expert's output buffer."""
     H = w.H if H is None else H
     return f32_to_bf16_bits(_rng(w.seed, seed, 3).standard_normal((n_rows, H), dtype=np.float32))
+
+
+def device_normal_bf16(shape, seed: int, device):
+    """bf16 bits (as int16) of N(0,1) values drawn on the device with torch's
+    seeded generator and rounded to nearest even: a stand-in for buffers too
+    large to draw on the host (a full-size expert-output buffer)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = torch.empty(shape, dtype=torch.int16, device=device)
+    flat = out.view(-1)
+    step = 1 << 26
+    for lo in range(0, flat.numel(), step):
+        n = min(step, flat.numel() - lo)
+        v = torch.randn(n, generator=g, device=device, dtype=torch.float32)
+        flat[lo: lo + n] = v.to(torch.bfloat16).view(torch.int16)
+    return out

@@ -338,6 +338,43 @@ def training_report(lbt, torch, w, path, buf, dev, Hp, reps):
     return out
 
 
+def hbm_ceilings(torch, dev, nbytes, reps=10):
+    """Reference HBM streams (bench_ceiling.so): a plain read, write and copy
+    of ``nbytes`` each, median of ``reps`` launches timed with HIP events on
+    the current stream; GB/s counts the bytes read plus the bytes written."""
+    import ctypes
+    import numpy as np
+    path = os.path.join(ROOT, "bench_ceiling.so")
+    if not os.path.exists(path):
+        return {"error": "bench_ceiling.so is not built"}
+    L = ctypes.CDLL(path)
+    L.hbm_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong,
+                             ctypes.c_void_p]
+    L.hbm_stream.restype = ctypes.c_int
+    a = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(7)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    out = {"bytes_per_launch": nbytes}
+    for name, kind, moved in (("read", 0, nbytes), ("write", 1, nbytes), ("copy", 2, 2 * nbytes)):
+        bp = b.data_ptr() if kind != 1 else None
+        for _ in range(3):
+            assert L.hbm_stream(kind, ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(bp), nbytes, sp) == 0
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            L.hbm_stream(kind, ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(bp), nbytes, sp)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.median([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps)]))
+        gbps = moved / (us * 1e-6) / 1e9
+        out[name] = {"us": us, "gbps": gbps, "frac_peak": gbps / HBM_PEAK_GBPS}
+    del a, b
+    torch.cuda.synchronize()
+    return out
+
+
 class StepRunner:
     """Buffers and inputs of one workload, resident in HBM, and the timed step
     (route -> plan -> align -> dispatch -> combine) over them."""
@@ -573,6 +610,8 @@ def main():
                     help="moonep: also time the step at max_vio 0.2, 1, 10, 20 (same buffers)")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the block of the other workloads (run with the default dsv3 only)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="also time plain HBM read, write and copy streams (bench_ceiling.so)")
     ap.add_argument("--x-device", action="store_true",
                     help="draw x on the device (N(0,1) bf16, torch's generator) instead of the host")
     args = ap.parse_args()
@@ -641,6 +680,11 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    ceilings = None
+    if args.ceilings:
+        print("[bench] reference HBM streams", file=sys.stderr, flush=True)
+        ceilings = hbm_ceilings(torch, dev, w.P * w.H * 2)
+
     ab = algorithmic_bytes(w, C)
     comb_gbps = ab["combine"] / (avg_us["combine"] * 1e-6) / 1e9
     traffic = measured_traffic("combine", w.name)
@@ -686,6 +730,7 @@ def main():
         "planners": planners,
         **({"maxvio_sweep": sweep} if sweep else {}),
         **({"training": training} if training else {}),
+        **({"hbm_ceilings": ceilings} if ceilings else {}),
         "status": summ["status"],
         "device": torch.cuda.get_device_name(0),
         "device_info": device_report(torch, 0),

@@ -44,6 +44,24 @@ def _compile(src: str) -> str:
     return obj
 
 
+CEILING_SRC = os.path.join(ROOT, "bench_ceiling.hip")
+CEILING_LIB = os.path.join(ROOT, "bench_ceiling.so")
+
+
+def build_ceiling(verbose: bool = False) -> str:
+    """Compile the benchmark's reference HBM streams (bench_ceiling.so, beside
+    bench.py; not part of the path)."""
+    tmp = CEILING_LIB + ".tmp"
+    cmd = [hipcc(), *CFLAGS, "-shared", CEILING_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on bench_ceiling.hip:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, CEILING_LIB)
+    if verbose:
+        print(f"built {CEILING_LIB}")
+    return CEILING_LIB
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link liblbt.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
@@ -62,4 +80,5 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_ceiling(verbose=True)
     sys.exit(0)

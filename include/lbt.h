@@ -260,6 +260,23 @@ int lbt_align_sort(const lbt_shape* s, const int32_t* ids, const int32_t* work,
                    const int32_t* plan, int32_t* slot, int32_t* sorted_ids,
                    int32_t* block_wrow, int32_t* block_expert, int32_t* status, void* stream);
 
+/* lbt_histogram followed by lbt_align_sort without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The
+ * workspace -- per-sub-tile expert counts, per-tile prefix offsets and the
+ * load matrix -- lives in a static device array of 16 MiB that each GPU the
+ * library runs on holds until the process ends; the call allocates nothing
+ * and writes every word of it that it reads.  Shapes needing more than
+ * 4 Mi words, E * (R * ceil(S/32) + R * ceil(S/128)) + R * E, return
+ * LBT_EUNSUPPORTED (the Kimi-K3 prefill shape needs 3.95 Mi).  Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and must be ordered
+ * by the caller.  Arguments and outputs as for lbt_align_sort (ids as for
+ * lbt_histogram: out-of-range ids raise LBT_ST_BADID in *status). */
+int lbt_align_sort_noalloc(const lbt_shape* s, const int32_t* ids, const int32_t* plan,
+                           int32_t* slot, int32_t* sorted_ids, int32_t* block_wrow,
+                           int32_t* block_expert, int32_t* status, void* stream);
+
 /* Zero-copy dispatch: recv[slot[f]] = x[f / K], a bit copy of each bf16
  * row, straight into its final expert-grouped row of the static per-rank
  * buffer ([MoonEP-GR] "Online planning, zero copy και στατικά σχήματα").

@@ -46,7 +46,8 @@ HDR_LOCAL = 12
 
 EXPORTS = ("lbt_query_sizes", "lbt_route_topk", "lbt_histogram", "lbt_plan_balance",
            "lbt_route_plan",
-           "lbt_plan_quota", "lbt_align_sort", "lbt_dispatch", "lbt_combine",
+           "lbt_plan_quota", "lbt_align_sort", "lbt_align_sort_noalloc", "lbt_dispatch",
+           "lbt_combine",
            "lbt_prefetch_weights", "lbt_reduce_grad", "lbt_combine_bwd", "lbt_dispatch_bwd",
            "lbt_strerror", "lbt_last_hip_error", "lbt_version")
 
@@ -102,6 +103,7 @@ def lib() -> ctypes.CDLL:
         L.lbt_plan_quota.argtypes = [SP, P, P, P, P]
         L.lbt_route_plan.argtypes = [SP, P, P, P, P, P, P, P, P, P]
         L.lbt_align_sort.argtypes = [SP, P, P, P, P, P, P, P, P, P]
+        L.lbt_align_sort_noalloc.argtypes = [SP, P, P, P, P, P, P, P, P]
         L.lbt_dispatch.argtypes = [SP, P, P, P, P]
         L.lbt_combine.argtypes = [SP, P, P, P, ctypes.c_int32, P, P]
         L.lbt_prefetch_weights.argtypes = [SP, P, P, P, ctypes.c_int64, P]
@@ -321,6 +323,23 @@ class Path:
             _ptr(status, torch.int32, 1, "status"),
             _stream(stream))
         _check(rc, "lbt_align_sort")
+
+    # a2 + a4 with the library's static workspace (no allocation, no work buffer)
+    def align_sort_noalloc(self, ids, plan, slot, sorted_ids, block_wrow, block_expert,
+                           status=None, stream=None):
+        torch = _torch()
+        s, z = self.shape, self.sizes
+        rc = lib().lbt_align_sort_noalloc(
+            ctypes.byref(self._c),
+            _ptr(ids, torch.int32, s.N * s.K, "ids"),
+            _ptr(plan, torch.int32, z["plan_words"], "plan"),
+            _ptr(slot, torch.int32, z["P"], "slot"),
+            _ptr(sorted_ids, torch.int32, s.R * z["C"], "sorted_ids"),
+            _ptr(block_wrow, torch.int32, s.R * z["n_blocks"], "block_wrow"),
+            _ptr(block_expert, torch.int32, s.R * z["n_blocks"], "block_expert"),
+            _ptr(status, torch.int32, 1, "status"),
+            _stream(stream))
+        _check(rc, "lbt_align_sort_noalloc")
 
     # a5
     def dispatch(self, x, slot, recv, stream=None):

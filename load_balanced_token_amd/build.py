@@ -17,7 +17,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblbt.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "route.hip", "plan.hip", "front.hip", "align.hip", "move.hip", "train.hip"]
+SOURCES = ["api.hip", "route.hip", "plan.hip", "front.hip", "noalloc.hip", "align.hip", "move.hip", "train.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -211,6 +211,19 @@ int lbt_align_sort(const lbt_shape* s, const int32_t* ids, const int32_t* work, 
                              begin_launches(stream)));
 }
 
+int lbt_align_sort_noalloc(const lbt_shape* s, const int32_t* ids, const int32_t* plan,
+                           int32_t* slot, int32_t* sorted_ids, int32_t* block_wrow,
+                           int32_t* block_expert, int32_t* status, void* stream) {
+  Dims d;
+  const int rc = make_dims(s, &d, nullptr);
+  if (rc) return rc;
+  if (!plan || !sorted_ids || !block_wrow || !block_expert) return LBT_EINVAL;
+  if (d.N > 0 && (!ids || !slot)) return LBT_EINVAL;
+  if (!noalloc_fits(d)) return LBT_EUNSUPPORTED;
+  return hip_rc(launch_align_noalloc(d, ids, plan, slot, sorted_ids, block_wrow, block_expert,
+                                     status, begin_launches(stream)));
+}
+
 int lbt_dispatch(const lbt_shape* s, const uint16_t* x, const int32_t* slot, uint16_t* recv,
                  void* stream) {
   Dims d;

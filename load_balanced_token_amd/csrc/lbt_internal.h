@@ -74,6 +74,11 @@ hipError_t launch_dispatch(const Dims& d, const uint16_t* x, const int32_t* slot
                            hipStream_t st);
 hipError_t launch_combine(const Dims& d, const uint16_t* out, const int32_t* slot,
                           const float* gates, int y_dtype, void* y, hipStream_t st);
+// the align step with the library's static workspace (noalloc.hip)
+bool noalloc_fits(const Dims& d);
+hipError_t launch_align_noalloc(const Dims& d, const int32_t* ids, const int32_t* plan,
+                                int32_t* slot, int32_t* sorted_ids, int32_t* block_wrow,
+                                int32_t* block_expert, int32_t* status, hipStream_t st);
 // gates == nullptr: every gate is 1 (the backward of dispatch)
 hipError_t launch_prefetch(const Dims& d, const int32_t* plan, const void* weights, void* slots,
                            long long row_bytes, hipStream_t st);

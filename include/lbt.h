@@ -208,6 +208,21 @@ int lbt_route_plan(const lbt_shape* s, const float* logits, const float* sel_bia
                    float* gates, int32_t* counts, int32_t* work, int32_t* plan, int32_t* status,
                    void* stream);
 
+/* The front of the step in one call: route, histogram, fixed-rule plan and
+ * block-aligned sort -- the outputs of lbt_route_topk, lbt_plan_balance and
+ * lbt_align_sort, bit for bit (status: the plan's bits ORed with the align
+ * step's).  Batches of at most 32 tokens (with R * ceil(S / 32) * E <=
+ * 16384) run as one workgroup that keeps the routing, the load matrix and
+ * the plan in LDS and places every pair from them -- one launch where the
+ * three calls make three; larger batches make the same launches as the
+ * three calls.  [MoonEP-GR] section "Online planning, zero copy και στατικά
+ * σχήματα"; [AlignSort]; [UltraEP] section "その仕組みは...".  Arguments as
+ * for the three calls. */
+int lbt_front(const lbt_shape* s, const float* logits, const float* sel_bias, int32_t* ids,
+              float* gates, int32_t* counts, int32_t* work, int32_t* plan, int32_t* slot,
+              int32_t* sorted_ids, int32_t* block_wrow, int32_t* block_expert, int32_t* status,
+              void* stream);
+
 /* Quota plan with a searched threshold: same blob layout and meaning as
  * lbt_plan_balance, so lbt_align_sort, lbt_dispatch and lbt_combine take it
  * unchanged.  [UltraEP] section "その仕組みは高速なエキスパート複製に依存する"

@@ -45,7 +45,7 @@ HDR_FEASIBLE = 11
 HDR_LOCAL = 12
 
 EXPORTS = ("lbt_query_sizes", "lbt_route_topk", "lbt_histogram", "lbt_plan_balance",
-           "lbt_route_plan",
+           "lbt_route_plan", "lbt_front",
            "lbt_plan_quota", "lbt_align_sort", "lbt_align_sort_noalloc", "lbt_dispatch",
            "lbt_combine",
            "lbt_prefetch_weights", "lbt_reduce_grad", "lbt_combine_bwd", "lbt_dispatch_bwd",
@@ -102,6 +102,7 @@ def lib() -> ctypes.CDLL:
         L.lbt_plan_balance.argtypes = [SP, P, P, P, P]
         L.lbt_plan_quota.argtypes = [SP, P, P, P, P]
         L.lbt_route_plan.argtypes = [SP, P, P, P, P, P, P, P, P, P]
+        L.lbt_front.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P]
         L.lbt_align_sort.argtypes = [SP, P, P, P, P, P, P, P, P, P]
         L.lbt_align_sort_noalloc.argtypes = [SP, P, P, P, P, P, P, P, P]
         L.lbt_dispatch.argtypes = [SP, P, P, P, P]
@@ -294,6 +295,30 @@ class Path:
             _stream(stream))
         _check(rc, "lbt_route_plan")
 
+    # a1 + a2 + a3 + a4 in one call (one launch for small batches)
+    def front(self, logits, buf, sel_bias=None, stream=None):
+        """Route, histogram, fixed-rule plan and align into the buffers of
+        ``alloc()`` (ids, gates, counts, work, plan, slot, sorted_ids,
+        block_wrow, block_expert, status)."""
+        torch = _torch()
+        s, z = self.shape, self.sizes
+        rc = lib().lbt_front(
+            ctypes.byref(self._c),
+            _ptr(logits, torch.float32, s.N * s.E, "logits"),
+            _ptr(sel_bias, torch.float32, s.E, "sel_bias"),
+            _ptr(buf["ids"], torch.int32, s.N * s.K, "ids"),
+            _ptr(buf["gates"], torch.float32, s.N * s.K, "gates"),
+            _ptr(buf["counts"], torch.int32, s.R * s.E, "counts"),
+            _ptr(buf["work"], torch.int32, z["work_words"], "work"),
+            _ptr(buf["plan"], torch.int32, z["plan_words"], "plan"),
+            _ptr(buf["slot"], torch.int32, z["P"], "slot"),
+            _ptr(buf["sorted_ids"], torch.int32, s.R * z["C"], "sorted_ids"),
+            _ptr(buf["block_wrow"], torch.int32, s.R * z["n_blocks"], "block_wrow"),
+            _ptr(buf["block_expert"], torch.int32, s.R * z["n_blocks"], "block_expert"),
+            _ptr(buf["status"], torch.int32, 1, "status"),
+            _stream(stream))
+        _check(rc, "lbt_front")
+
     # a3, quota variant
     def plan_quota(self, counts, plan, status=None, stream=None):
         torch = _torch()
@@ -429,19 +454,20 @@ class Path:
 
     def step(self, logits, x, buf, sel_bias=None, out=None, stream=None, planner="fixed"):
         """One pass of the whole path; ``out`` defaults to recv (identity
-        expert); ``planner`` is "fixed" (lbt_plan_balance) or "quota"
-        (lbt_plan_quota).  Returns nothing; results land in ``buf``."""
+        expert); ``planner`` is "fixed" (route, plan and align in one
+        lbt_front call) or "quota" (lbt_route_topk, lbt_plan_quota,
+        lbt_align_sort).  Returns nothing; results land in ``buf``."""
         if planner not in ("fixed", "quota"):
             raise LbtError(f"unknown planner {planner!r}")
         if planner == "fixed":
-            self.route_plan(logits, buf["ids"], buf["gates"], buf["counts"], buf["work"],
-                            buf["plan"], buf["status"], sel_bias=sel_bias, stream=stream)
+            self.front(logits, buf, sel_bias=sel_bias, stream=stream)
         else:
             self.route_topk(logits, buf["ids"], buf["gates"], buf["counts"], buf["work"],
                             sel_bias=sel_bias, stream=stream)
             self.plan_quota(buf["counts"], buf["plan"], buf["status"], stream=stream)
-        self.align_sort(buf["ids"], buf["work"], buf["plan"], buf["slot"], buf["sorted_ids"],
-                        buf["block_wrow"], buf["block_expert"], buf["status"], stream=stream)
+            self.align_sort(buf["ids"], buf["work"], buf["plan"], buf["slot"],
+                            buf["sorted_ids"], buf["block_wrow"], buf["block_expert"],
+                            buf["status"], stream=stream)
         self.dispatch(x, buf["slot"], buf["recv"], stream=stream)
         self.combine(buf["recv"] if out is None else out, buf["slot"], buf["gates"], buf["y"],
                      stream=stream)

@@ -46,9 +46,10 @@ __global__ __launch_bounds__(NT) void k_align(
   // LDS, carved to the shape (align_lds_bytes): per expert sH, sO, sHome,
   // sBase and, for the locality step of quota plans, sHL (home local
   // count), sSrc0 (pairs of e from ranks below this tile's rank r), sPN
-  // (first piece << 16 | piece count), sLocCap / sLocRow (r's own instance
-  // of e: quota its tokens take, start row), sLP (local pairs of instances
-  // on ranks <= r); the sub-tile masks and prefix counts; per piece sPl,
+  // (first piece << 16 | piece count; without the locality step, sP0: the
+  // first piece), sLocCap / sLocRow (r's own instance of e: quota its tokens
+  // take, start row), sLP (local pairs of instances on ranks <= r); the
+  // sub-tile masks and prefix counts; per piece sPl,
   // sPd, sPr, sPe, sPc, sPLoc (local count) and sRem (start of its share of
   // the pairs left after the local step).
   extern __shared__ int smem[];
@@ -63,6 +64,7 @@ __global__ __launch_bounds__(NT) void k_align(
   int* sLocCap = sPN + Ea;
   int* sLocRow = sLocCap + Ea;
   int* sLP = sLocRow + Ea;
+  int* sP0 = sPN;   // plans without the locality step: first replica segment of e
   uint32_t* sMask = reinterpret_cast<uint32_t*>(sLP + Ea);   // [kSubTiles][E]
   int* sSub = reinterpret_cast<int*>(sMask + kSubTiles * Ea); // [kSubTiles][E]
   int* sPl = sSub + kSubTiles * Ea;
@@ -106,6 +108,7 @@ __global__ __launch_bounds__(NT) void k_align(
     sBase[e] = tbase[e];
     sHL[e] = plan[pl.home_local + e];
     sSrc0[e] = rbase[e];
+    sPN[e] = -1;
 #pragma unroll
     for (int s = 0; s < kSubTiles; ++s) sMask[s * E + e] = 0u;
   }
@@ -169,6 +172,14 @@ __global__ __launch_bounds__(NT) void k_align(
     if (p < np) mark(p, idp[u]);
   }
   for (int p = tid + kPre * NT; p < np; p += NT) mark(p, ids[f0 + p]);
+  // the first replica segment of each expert (an expert's segments are
+  // consecutive on the line), so a pair finds its segment by a short walk
+  // over its expert's few segments instead of a search over all of them
+  if (!local)
+    for (int g = tid; g < nP; g += NT) {
+      const int e = sPe[g];
+      if (e >= 0 && e < E && (g == 0 || sPe[g - 1] != e)) sP0[e] = g;
+    }
   __syncthreads();
   for (int e = tid; e < E; e += NT) {
     int run = 0;
@@ -223,9 +234,12 @@ __global__ __launch_bounds__(NT) void k_align(
       dd = e / nh;
       row = sHome[e] + q;
     } else {
+      // the last of e's segments starting at or below its line position o
       const int o = sO[e] + (q - h);
-      const int g = upper_bound(sPl, nP, o) - 1;
-      ok = o < totOv && g >= 0 && sPe[g] == e;
+      int g = sP0[e];
+      if (g >= 0)
+        while (g + 1 < nP && sPe[g + 1] == e && sPl[g + 1] <= o) ++g;
+      ok = o < totOv && g >= 0 && sPl[g] <= o;
       dd = ok ? sPd[g] : 0;
       row = ok ? sPr[g] + (o - sPl[g]) : 0;
     }

@@ -199,6 +199,21 @@ int lbt_route_plan(const lbt_shape* s, const float* logits, const float* sel_bia
   return hip_rc(launch_route_plan(d, logits, sel_bias, ids, gates, work, counts, plan, status, st));
 }
 
+int lbt_front(const lbt_shape* s, const float* logits, const float* sel_bias, int32_t* ids,
+              float* gates, int32_t* counts, int32_t* work, int32_t* plan, int32_t* slot,
+              int32_t* sorted_ids, int32_t* block_wrow, int32_t* block_expert, int32_t* status,
+              void* stream) {
+  Dims d;
+  const int rc = make_dims(s, &d, nullptr);
+  if (rc) return rc;
+  if (counts == nullptr || plan == nullptr || !sorted_ids || !block_wrow || !block_expert ||
+      (d.N > 0 && (!logits || !ids || !gates || !work || !slot)))
+    return LBT_EINVAL;
+  const hipStream_t st = begin_launches(stream);
+  return hip_rc(launch_front(d, logits, sel_bias, ids, gates, work, counts, plan, slot,
+                             sorted_ids, block_wrow, block_expert, status, st));
+}
+
 int lbt_align_sort(const lbt_shape* s, const int32_t* ids, const int32_t* work, const int32_t* plan,
                    int32_t* slot, int32_t* sorted_ids, int32_t* block_wrow, int32_t* block_expert,
                    int32_t* status, void* stream) {

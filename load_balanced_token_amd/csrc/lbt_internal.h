@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 #include "../../include/lbt.h"
@@ -65,6 +66,11 @@ hipError_t launch_plan(const Dims& d, const int32_t* counts, int32_t* plan, int3
 hipError_t launch_route_plan(const Dims& d, const float* logits, const float* bias, int32_t* ids,
                              float* gates, int32_t* work, int32_t* counts, int32_t* plan,
                              int32_t* status, hipStream_t st);
+// route + histogram + fixed-rule plan + align (one launch for small batches)
+hipError_t launch_front(const Dims& d, const float* logits, const float* bias, int32_t* ids,
+                        float* gates, int32_t* work, int32_t* counts, int32_t* plan,
+                        int32_t* slot, int32_t* sorted_ids, int32_t* block_wrow,
+                        int32_t* block_expert, int32_t* status, hipStream_t st);
 hipError_t launch_plan_quota(const Dims& d, const int32_t* counts, int32_t* plan,
                              int32_t* status, hipStream_t st);
 hipError_t launch_align(const Dims& d, const int32_t* ids, const int32_t* work, const int32_t* plan,
@@ -106,10 +112,27 @@ __device__ __forceinline__ int div_nh(int e, const Dims& d) {
 }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 
+// Wave-wide max and sum, the same value in every lane, for a full wave: four
+// DPP steps inside each 16-lane row (each lane paired with one of the
+// other half of its quad, pair, half-row and row; the identity as the old
+// value lets the compiler fold every move into the max or add), then the
+// four row results read into scalars.  No LDS round trip.
 __device__ __forceinline__ int wave_max(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, kWave));
-  return x;
+  x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+  x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+  x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, 0x140, 0xF, 0xF, false));   // row_mirror
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);
+  return (__builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16)) +
+         (__builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48));
 }
 
 // Inclusive prefix sum across a wave64 with DPP: Hillis-Steele steps inside

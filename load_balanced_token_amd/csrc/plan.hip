@@ -25,7 +25,9 @@ namespace lbt {
 
 // T_e = column sums of the load matrix into sT and sX (all threads of the
 // workgroup; eight independent loads in flight per thread); with sCnt, the
-// matrix itself is kept in LDS too.
+// matrix itself is kept in LDS too.  (Splitting each column over two or
+// four lanes joined by cross-lane adds, so that a lane issues fewer loads,
+// measured slower on MI355X: 1.44 vs 0.88 us at 256 experts x 8 ranks.)
 template <int NT>
 __device__ __forceinline__ void column_sums(const int32_t* __restrict__ counts, int E, int R,
                                             int* sT, int* sX, int* sCnt = nullptr) {
@@ -44,19 +46,6 @@ __device__ __forceinline__ void column_sums(const int32_t* __restrict__ counts, 
     sT[e] = s;
     if (sX != nullptr) sX[e] = s;
   }
-}
-
-// Position of expert e in its rank's shedding order: load descending, ties
-// to the lower index.
-__device__ __forceinline__ int hot_position(const int* sT, int e, const Dims& d) {
-  const int nh = d.nh, r0 = div_nh(e, d) * nh, T = sT[e];
-  int pos = 0;
-#pragma unroll 8
-  for (int x = r0; x < r0 + nh; ++x) {
-    const int Tx = sT[x];
-    pos += (Tx > T) || (Tx == T && x < e);
-  }
-  return pos;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict__ counts, Dims d,
@@ -128,33 +117,56 @@ __device__ __forceinline__ bool tau_fits(int tau, const int* sQ, const int* sL, 
 // The same check for one tau by one wave, lanes over ranks (R <= 64): the
 // overflow, expert-count and deficit offsets of every rank come from wave
 // prefix sums; a deficit rank's interval [a, b) on the line touches experts
-// N(a) .. N(b-1), N(x) = index along the line of the expert holding x, found
-// by a search over the ranks' overflow offsets and one inside the rank.
-// Returns the same value in every lane.  ov_off / nv_off: R + 1 ints of LDS
-// owned by the wave.
+// N(a) .. N(b-1), N(x) = index along the line of the expert holding x.  The
+// rank holding x is the number of ranks whose overflow starts at or below
+// x, less one (broadcast reads of the rank offsets, four at a time), and
+// the expert inside it the number of its prefixes at or below the rest:
+// independent LDS reads, so a candidate costs a handful of LDS round trips
+// rather than chains of binary-search steps.  Returns the same value in
+// every lane.  ov_off / nv_off: kWave ints of LDS owned by the wave, ov_off
+// 16-byte aligned.
 __device__ __forceinline__ bool tau_fits_wave(int tau, const int* sQ, const int* sL, int R, int nh,
                                               int B, int* ov_off, int* nv_off) {
   const int r = lane_id();
   const int L = r < R ? sL[r] : 0;
   const int ov = r < R ? max(L - tau, 0) : 0;
   const int df = r < R ? max(tau - L, 0) : 0;
-  // experts of rank r that shed anything: those holding positions [0, ov)
-  const int nv = ov > 0 ? upper_bound(sQ + r * nh, nh, ov - 1) + 1 : 0;
+  // experts of rank r that shed anything: those holding positions [0, ov),
+  // i.e. the ones whose prefix is below ov and the first that reaches it
+  int nv = 0;
+  if (ov > 0) {
+    const int* q = sQ + r * nh;
+#pragma unroll 8
+    for (int j = 0; j < nh; ++j) nv += q[j] < ov;
+    ++nv;
+  }
   const int ov_in = wave_incl_scan_dpp(ov), nv_in = wave_incl_scan_dpp(nv);
   const int df_ex = wave_incl_scan_dpp(df) - df;
   const int tot = __builtin_amdgcn_readlane(ov_in, kWave - 1);
-  if (r < R) {
-    ov_off[r] = ov_in - ov;
-    nv_off[r] = nv_in - nv;
-  }
-  if (r == 0) ov_off[R] = tot;
+  ov_off[r] = r < R ? ov_in - ov : INT_MAX;   // lanes past R pad the four-wide reads
+  nv_off[r] = nv_in - nv;
   __builtin_amdgcn_wave_barrier();
-  auto line_expert = [&](int x) {       // index along the line of the expert holding x
-    const int rx = upper_bound(ov_off, R, x) - 1;
-    return nv_off[rx] + upper_bound(sQ + rx * nh, nh, x - ov_off[rx]);
-  };
   const int a = df_ex, b = min(df_ex + df, tot);
-  const int pieces = (df > 0 && a < b) ? line_expert(b - 1) - line_expert(a) + 1 : 0;
+  const bool need = df > 0 && a < b;
+  const int xa = a, xb = b - 1;
+  int ca = 0, cb = 0;
+  for (int r0 = 0; r0 < R; r0 += 4) {        // r0 + 3 < kWave since R <= kWave
+    const int4 v = *reinterpret_cast<const int4*>(ov_off + r0);
+    ca += (v.x <= xa) + (v.y <= xa) + (v.z <= xa) + (v.w <= xa);
+    cb += (v.x <= xb) + (v.y <= xb) + (v.z <= xb) + (v.w <= xb);
+  }
+  // clamped so lanes without an interval still read in bounds
+  const int ra = max(ca - 1, 0), rb = max(cb - 1, 0);
+  const int ya = xa - ov_off[ra], yb = xb - ov_off[rb];
+  const int* qa = sQ + ra * nh;
+  const int* qb = sQ + rb * nh;
+  int ja = 0, jb = 0;
+#pragma unroll 8
+  for (int j = 0; j < nh; ++j) {
+    ja += qa[j] <= ya;
+    jb += qb[j] <= yb;
+  }
+  const int pieces = need ? (nv_off[rb] + jb) - (nv_off[ra] + ja) + 1 : 0;
   const bool bad = __any(pieces > B);
   __builtin_amdgcn_wave_barrier();      // ov_off / nv_off may be rewritten next
   return !bad;
@@ -172,28 +184,41 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_quota(const int32_t* __re
   __shared__ int sQ[kMaxE];     // per-rank inclusive prefix of the loads in shedding order
   __shared__ int sLr[kMaxR];    // L_r
   __shared__ int sCnt[kQuotaCountsLds];   // the load matrix, when it fits
-  __shared__ int sOvOff[kPlanThreads / kWave][kWave + 1];   // per-wave scratch of the first stage
-  __shared__ int sNvOff[kPlanThreads / kWave][kWave + 1];
+  alignas(16) __shared__ int sOvOff[kPlanThreads / kWave][kWave];   // per-wave scratch of the first stage
+  __shared__ int sNvOff[kPlanThreads / kWave][kWave];
   const int E = d.E, R = d.R, nh = d.nh, tid = threadIdx.x;
-  // [10]: smallest qualifying tau, [11]: max_r L_r
+  __shared__ int sFound[2];   // smallest qualifying tau of the first two stages
+  // [10]: smallest qualifying tau of the batches, [11]: max_r L_r
   if (tid < 12) m.sStat[tid] = tid == 10 ? INT_MAX : 0;
+  if (tid < 2) sFound[tid] = INT_MAX;
   const bool keep = (long long)R * E <= kQuotaCountsLds;
   column_sums<kPlanThreads>(counts, E, R, m.sT, m.sX, keep ? sCnt : nullptr);
   __syncthreads();
+  // Shedding order in one pass over each rank's loads: expert e's position
+  // is the number of its rank's experts that are hotter (load descending,
+  // ties to the lower index), the load ahead of it their sum, so the
+  // per-rank prefix in that order needs no separate scan.  sHx[g] = the
+  // load ahead of line position g within its rank (0 at the rank's first
+  // position), sQ[g] = the same plus the load at g.
+  int maxL = 0;
   for (int e = tid; e < E; e += kPlanThreads) {
-    const int g = div_nh(e, d) * nh + hot_position(m.sT, e, d);
+    const int rr = div_nh(e, d), r0 = rr * nh, T = m.sT[e];
+    int pos = 0, ahead = 0, L = 0;
+#pragma unroll 8
+    for (int x = r0; x < r0 + nh; ++x) {
+      const int Tx = m.sT[x];
+      const bool hot = Tx > T || (Tx == T && x < e);
+      pos += hot;
+      ahead += hot ? Tx : 0;
+      L += Tx;
+    }
+    const int g = r0 + pos;
     m.sLam[e] = g;
     m.sPerm[g] = e;
-    m.sHx[g] = m.sT[e];
-  }
-  __syncthreads();
-  if (wave_id() == 0) wave_excl_scan_lds<kMaxE / kWave>(m.sHx, E);
-  __syncthreads();
-  for (int g = tid; g < E; g += kPlanThreads) sQ[g] = m.sHx[g + 1] - m.sHx[div_nh(g, d) * nh];
-  int maxL = 0;
-  for (int r = tid; r < R; r += kPlanThreads) {
-    sLr[r] = m.sHx[(r + 1) * nh] - m.sHx[r * nh];
-    maxL = max(maxL, sLr[r]);
+    m.sHx[g] = ahead;
+    sQ[g] = ahead + T;
+    if (e == r0) sLr[rr] = L;
+    maxL = max(maxL, L);
   }
   maxL = wave_max(maxL);
   if (lane_id() == 0 && maxL > 0) atomicMax(&m.sStat[11], maxL);
@@ -201,30 +226,43 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_quota(const int32_t* __re
 
   const int hi = min(m.sStat[11], d.tau_max);
   constexpr int kPlanWaves = kPlanThreads / kWave;
-  int first = d.SK;
+  int found = INT_MAX;   // smallest qualifying candidate of the stages below (uniform)
+  int next = d.SK;       // first candidate not checked yet
   if (R <= kWave) {
-    // first stage: the kPlanWaves smallest candidates, one per wave (low latency)
-    const int tau = d.SK + wave_id();
-    if (tau <= hi && tau_fits_wave(tau, sQ, sLr, R, nh, d.B, sOvOff[wave_id()], sNvOff[wave_id()]) &&
-        lane_id() == 0)
-      atomicMin(&m.sStat[10], tau);
+    // tau = S*K first, by wave 0 alone, so no other wave competes for the
+    // LDS (with the slot counts the pages use it qualifies; measured on
+    // MI355X at DSV3: 16 candidates at once, one per wave, took 3.7 us)
+    if (wave_id() == 0 && d.SK <= hi &&
+        tau_fits_wave(d.SK, sQ, sLr, R, nh, d.B, sOvOff[0], sNvOff[0]) && lane_id() == 0)
+      sFound[0] = d.SK;
     __syncthreads();
-    first = m.sStat[10] != INT_MAX ? INT_MAX : d.SK + kPlanWaves;
-    __syncthreads();   // every thread has read the result before the next stage writes
+    found = sFound[0];
+    next = d.SK + 1;
+    if (found == INT_MAX) {
+      // the next kPlanWaves candidates, one per wave
+      const int tau = next + wave_id();
+      if (tau <= hi &&
+          tau_fits_wave(tau, sQ, sLr, R, nh, d.B, sOvOff[wave_id()], sNvOff[wave_id()]) &&
+          lane_id() == 0)
+        atomicMin(&sFound[1], tau);
+      __syncthreads();
+      found = sFound[1];
+      next += kPlanWaves;
+    }
   }
   // then ascending batches, one candidate per thread (high throughput)
-  for (int base = first; base <= hi; base += kPlanThreads) {
+  for (int base = next; found == INT_MAX && base <= hi; base += kPlanThreads) {
     const int tau = base + tid;
     const bool ok = tau <= hi && tau_fits(tau, sQ, sLr, R, nh, d.B);
     const unsigned long long bal = __ballot(ok);
     // lanes hold ascending candidates: the lowest set lane has the wave's smallest
     if (bal != 0ull && lane_id() == __ffsll((long long)bal) - 1) atomicMin(&m.sStat[10], tau);
     __syncthreads();
-    const int found = m.sStat[10];
-    __syncthreads();
-    if (found != INT_MAX) break;
+    const int f = m.sStat[10];
+    __syncthreads();   // every thread has read it before the next batch writes
+    if (f != INT_MAX) found = f;
   }
-  const int tau = m.sStat[10] == INT_MAX ? d.tau_max : m.sStat[10];
+  const int tau = found == INT_MAX ? d.tau_max : found;
   plan_core<true>(d, m, tau, counts, keep ? sCnt : nullptr, plan, status);
 }
 

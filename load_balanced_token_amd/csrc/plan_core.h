@@ -65,11 +65,11 @@ struct PlanSmem {
   int sLb[kMaxE + 1];                   // deficit starts below O_g (line position g); [E]: below the overflow total
   alignas(16) int sRep[kMaxR + 1];      // replicas per rank, then first piece of rank
   int sPe[kMaxPieces], sPd[kMaxPieces], sPc[kMaxPieces], sPl[kMaxPieces],
-      sPj[kMaxPieces];
+      sPj[kMaxPieces], sPg[kMaxPieces];
   alignas(16) int sF[kMaxE + kMaxPieces + 1];  // flat segment padded lengths -> starts
   int sLam[kMaxE];                      // quota rule: line position of expert e inside its rank block
   int sPerm[kMaxE];                     // quota rule: expert at line position
-  alignas(16) int sHx[kMaxE + 1];       // quota rule: loads in line order, then exclusive prefix
+  int sHx[kMaxE];                       // quota rule: load ahead of line position g in its rank
   // max_T, max_L, over ranks, over experts, status, nP, totOv, Ptot, tau, max replicas
   int sStat[12];
 };
@@ -191,7 +191,7 @@ __device__ __forceinline__ void keep_and_overflow(PlanSmem& m, const Dims& d, co
     int h;
     if (HOT) {
       const int L = m.sX[r0 + nh] - m.sX[r0];
-      const int HP = m.sHx[m.sLam[ec]] - m.sHx[r0];
+      const int HP = m.sHx[m.sLam[ec]];
       h = T - min(max(L - tau - HP, 0), T);
     } else {
       const int Pe = m.sX[ec] - m.sX[r0];    // position in the rank's home stream
@@ -223,33 +223,25 @@ __device__ __forceinline__ void home_lengths(PlanSmem& m, const Dims& d, const i
   }
 }
 
-// The plan from T_e (in m.sT and m.sX, written and made visible by a
+// The plan in LDS from T_e (in m.sT and m.sX, written and made visible by a
 // workgroup barrier before the call; for HOT also m.sLam, m.sPerm and m.sHx
-// = exclusive prefix of the loads in line order) at threshold tau; 1024
-// threads; writes the whole blob and *status.  The locality counts (HOT)
-// read the load matrix from sCnt when given (an LDS copy), else from counts.
+// = the load ahead of each line position within its rank) at threshold
+// tau.  Called by all 1024 threads; wave 0 does the work, and the closing
+// workgroup barrier makes the plan visible to every wave.
 template <bool HOT>
-__device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int tau,
-                                          const int32_t* __restrict__ counts,
-                                          const int* sCnt, int32_t* __restrict__ plan,
-                                          int32_t* __restrict__ status) {
-  auto count_of = [&](int r, int e) {
-    return sCnt != nullptr ? sCnt[r * d.E + e] : counts[(long long)r * d.E + e];
-  };
+__device__ __forceinline__ void plan_build(const Dims& d, PlanSmem& m, const int tau) {
   auto& sT = m.sT; auto& sX = m.sX; auto& sH = m.sH; auto& sO = m.sO; auto& sNp = m.sNp;
   auto& sDlo = m.sDlo; auto& sL = m.sL; auto& sDef = m.sDef; auto& sD = m.sD;
   auto& sCidx = m.sCidx; auto& sDl = m.sDl; auto& sDc = m.sDc; auto& sRep = m.sRep;
   auto& sPe = m.sPe;
   auto& sPd = m.sPd; auto& sPc = m.sPc; auto& sPl = m.sPl; auto& sPj = m.sPj; auto& sF = m.sF;
+  auto& sPg = m.sPg;
   auto& sStat = m.sStat;
-  auto& sLam = m.sLam; auto& sPerm = m.sPerm; auto& sHx = m.sHx;
-  // line position of expert e, expert at line position g (identity for the fixed rule)
-  auto lam = [&](int e) { return HOT ? sLam[e] : e; };
+  auto& sPerm = m.sPerm;
+  // expert at line position g (identity for the fixed rule)
   auto perm = [&](int g) { return HOT ? sPerm[g] : g; };
   const int tid = threadIdx.x;
-  const int E = d.E, R = d.R, nh = d.nh, SK = d.SK, B = d.B, blk = d.blk, C = d.C;
-  const PlanLayout pl = d.pl;
-  const int ms = pl.max_seg;
+  const int E = d.E, R = d.R, nh = d.nh, SK = d.SK, blk = d.blk, C = d.C;
 
   // 2. wave 0 alone: the plan, with wave-level scans and no barriers
   if (tid < kWave) {
@@ -316,9 +308,15 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
     else count_pieces<kMaxE / kWave, HOT>(m, E, nDef, consistent, lane);
     __builtin_amdgcn_wave_barrier();
     const int nP = wave_excl_scan_lds<kMaxE / kWave>(sNp, E);
+    // line position of every piece: each position lists its own pieces
+    // (few per position), so a piece finds its position by one LDS read
+    // instead of a search over all E positions
+    for (int g0 = lane; g0 < E; g0 += kWave)
+      for (int g = sNp[g0]; g < sNp[g0 + 1]; ++g) sPg[g] = g0;
+    __builtin_amdgcn_wave_barrier();
     // one lane per replica segment ("piece"), in line order
     for (int g = lane; g < nP; g += kWave) {
-      const int ge = upper_bound(sNp, E, g) - 1;   // line position of the piece's expert
+      const int ge = sPg[g];                       // line position of the piece's expert
       const int e = perm(ge);
       const int jj = g - sNp[ge];
       const int dd = sDl[sDlo[ge] + jj];
@@ -345,12 +343,10 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
     __builtin_amdgcn_wave_barrier();
     wave_excl_scan_lds<(kMaxE + kMaxPieces) / kWave>(sF, E + nP);
     // wave-wide reductions of the statistics
-    for (int o = 32; o > 0; o >>= 1) {
-      maxT = max(maxT, __shfl_xor(maxT, o, kWave));
-      maxL = max(maxL, __shfl_xor(maxL, o, kWave));
-      nOverE += __shfl_xor(nOverE, o, kWave);
-      nOverR += __shfl_xor(nOverR, o, kWave);
-    }
+    maxT = wave_max(maxT);
+    maxL = wave_max(maxL);
+    nOverE = wave_sum(nOverE);
+    nOverR = wave_sum(nOverR);
     // replicas and padded rows per rank: the capacity check
     int maxRep = 0;
     bool over_cap = false;
@@ -374,13 +370,36 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
     }
   }
   __syncthreads();
+}
+
+// The header, *status and the blob from the plan in LDS (after plan_build),
+// by the nthr threads (a multiple of 64) whose index in that group is wt.
+// The locality counts (HOT) read the load matrix from sCnt when given (an
+// LDS copy), else from counts.
+template <bool HOT>
+__device__ __forceinline__ void plan_write(const Dims& d, const PlanSmem& m,
+                                           const int32_t* __restrict__ counts, const int* sCnt,
+                                           int32_t* __restrict__ plan,
+                                           int32_t* __restrict__ status, const int wt,
+                                           const int nthr) {
+  auto count_of = [&](int r, int e) {
+    return sCnt != nullptr ? sCnt[r * d.E + e] : counts[(long long)r * d.E + e];
+  };
+  auto& sT = m.sT; auto& sH = m.sH; auto& sO = m.sO; auto& sL = m.sL; auto& sDef = m.sDef;
+  auto& sD = m.sD; auto& sCidx = m.sCidx; auto& sRep = m.sRep; auto& sPe = m.sPe;
+  auto& sPd = m.sPd; auto& sPc = m.sPc; auto& sPl = m.sPl; auto& sPj = m.sPj; auto& sF = m.sF;
+  auto& sStat = m.sStat; auto& sLam = m.sLam;
+  auto lam = [&](int e) { return HOT ? sLam[e] : e; };
+  const int E = d.E, R = d.R, nh = d.nh, B = d.B;
+  const PlanLayout pl = d.pl;
+  const int ms = pl.max_seg;
   // rank r's flat entries are [fb(r), fb(r+1)) with fb(r) = r*nh + sRep[r]
   const int nP = sStat[5];
   int32_t* P = plan;
 
   // the header and the status word: everything they hold is in LDS already,
   // so no further barrier (which would also wait for the blob's stores)
-  if (tid == 0) {
+  if (wt == 0) {
     const int st = sStat[4];
     P[pl.hdr + LBT_HDR_N_PIECES] = nP;
     P[pl.hdr + LBT_HDR_MAX_T] = sStat[0];
@@ -399,8 +418,7 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
     if (status != nullptr) *status = st;
   }
 
-  // 3. every wave: write the blob from LDS
-  for (int e = tid; e < E; e += kPlanThreads) {
+  for (int e = wt; e < E; e += nthr) {
     const int r = div_nh(e, d);
     const int fb = r * nh + sRep[r];
     P[pl.T + e] = sT[e];
@@ -410,7 +428,7 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
     P[pl.O + e] = sO[lam(e)];
     P[pl.home_row + e] = sF[fb + (e - r * nh)] - sF[fb];
   }
-  for (int r = tid; r < R; r += kPlanThreads) {
+  for (int r = wt; r < R; r += nthr) {
     const int fb = r * nh + sRep[r];
     const int fe = (r + 1) * nh + sRep[r + 1];
     const int nrep = sRep[r + 1] - sRep[r];
@@ -423,36 +441,55 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
     P[pl.n_slots + r] = min(nrep, B);
     P[pl.n_remote + r] = nrep - min(nrep, B);
   }
-  if (tid == 0) P[pl.D + R] = sD[R];
-  // segment tables, one rank per wave at a time, entries across the lanes
-  constexpr int kPlanWaves = kPlanThreads / kWave;
-  for (int r = wave_id(); r < R; r += kPlanWaves) {
+  if (wt == 0) P[pl.D + R] = sD[R];
+  // segment tables, one rank per wave at a time, entries across the lanes.
+  // Ranks go to the waves from the last one down (the first waves also
+  // write the per-expert arrays and the pieces), and each lane handles
+  // kSegUnroll entries per trip with every LDS read issued before the
+  // stores, so a trip waits for one LDS round trip instead of one per
+  // 64 entries (DSV3: 256 entries per rank).
+  constexpr int kSegUnroll = 4;
+  const int nw = nthr / kWave;
+  for (int r = nw - 1 - wt / kWave; r < R; r += nw) {
     const int rep0 = sRep[r], nrep = sRep[r + 1] - rep0;
     const int fb = r * nh + rep0;
     const int nseg = nh + nrep;
     const int f0 = sF[fb];
     const long long row = (long long)r * ms;
-    for (int s = lane_id(); s < ms; s += kWave) {
-      int ex = -1, wr = -1, cnt = 0;
-      if (s < nh) {
-        ex = r * nh + s;
-        wr = ex;
-        cnt = sH[ex];
-      } else if (s < nseg) {
-        const int g = rep0 + (s - nh);
-        ex = sPe[g];
-        cnt = sPc[g];
-        wr = (s - nh < B) ? E + (s - nh) : ex;
-      }
-      P[pl.seg_expert + row + s] = ex;
-      P[pl.seg_wrow + row + s] = wr;
-      P[pl.seg_count + row + s] = cnt;
-    }
     const long long row1 = (long long)r * (ms + 1);
-    for (int s = lane_id(); s <= ms; s += kWave)
-      P[pl.seg_start + row1 + s] = (s < nseg ? sF[fb + s] : sF[fb + nseg]) - f0;
+    for (int s0 = lane_id(); s0 <= ms; s0 += kSegUnroll * kWave) {
+      int ex[kSegUnroll], wr[kSegUnroll], cnt[kSegUnroll], st[kSegUnroll];
+#pragma unroll
+      for (int u = 0; u < kSegUnroll; ++u) {
+        const int s = s0 + u * kWave;
+        ex[u] = -1;
+        wr[u] = -1;
+        cnt[u] = 0;
+        if (s < nh) {
+          ex[u] = r * nh + s;
+          wr[u] = ex[u];
+          cnt[u] = sH[ex[u]];
+        } else if (s < nseg) {
+          const int g = rep0 + (s - nh);
+          ex[u] = sPe[g];
+          cnt[u] = sPc[g];
+          wr[u] = (s - nh < B) ? E + (s - nh) : ex[u];
+        }
+        st[u] = sF[fb + min(s, nseg)];
+      }
+#pragma unroll
+      for (int u = 0; u < kSegUnroll; ++u) {
+        const int s = s0 + u * kWave;
+        if (s < ms) {
+          P[pl.seg_expert + row + s] = ex[u];
+          P[pl.seg_wrow + row + s] = wr[u];
+          P[pl.seg_count + row + s] = cnt[u];
+        }
+        if (s <= ms) P[pl.seg_start + row1 + s] = st[u] - f0;
+      }
+    }
   }
-  for (int g = tid; g < pl.max_pieces; g += kPlanThreads) {
+  for (int g = wt; g < pl.max_pieces; g += nthr) {
     int ex = -1, dd = -1, cnt = 0, line = -1, row = -1, wrow = -1, loc = 0;
     if (g < nP) {
       ex = sPe[g];
@@ -472,6 +509,17 @@ __device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int 
     P[pl.piece_line + g] = line;
     P[pl.piece_row + g] = row;
   }
+}
+
+// plan_build then plan_write by the whole workgroup: the plan from T_e at
+// threshold tau, with the blob and *status written.
+template <bool HOT>
+__device__ __forceinline__ void plan_core(const Dims& d, PlanSmem& m, const int tau,
+                                          const int32_t* __restrict__ counts,
+                                          const int* sCnt, int32_t* __restrict__ plan,
+                                          int32_t* __restrict__ status) {
+  plan_build<HOT>(d, m, tau);
+  plan_write<HOT>(d, m, counts, sCnt, plan, status, (int)threadIdx.x, kPlanThreads);
 }
 
 }  // namespace lbt

@@ -64,13 +64,13 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(const int32_t* __res
 // the CUs): exclusive prefix over the sub-tiles, written at each 128-token
 // tile's first sub-tile (tile-major, for the align step), and per-source-rank
 // sums (the load matrix) as differences of the prefix at the ranks' first
-// sub-tiles (sub-tiles never cross ranks).  The column is read in coalesced
-// 64-wide chunks, kScanBatch chunks per batch, the next batch's loads issued
-// before the current batch is scanned; each chunk is scanned across the wave
-// and carried into the next.  Measured on MI355X (DSV3, 1024 sub-tiles per
-// column): four 64-wide chunks per batch and four columns per workgroup took
-// 6.3 us.
-constexpr int kScanBatch = 16;
+// sub-tiles (sub-tiles never cross ranks).  Each lane takes kScanPer
+// consecutive sub-tiles of a batch of 64 * kScanPer, sums them in registers,
+// and one wave-wide scan of the lane sums gives every lane its offset, so a
+// batch costs one scan.  (Measured on MI355X, DSV3, 1024 sub-tiles per
+// column: one 64-wide chunk per scan, the chunks scanned one after another
+// with a carried total, took 6.3 us.)
+constexpr int kScanPer = 16;
 
 __global__ __launch_bounds__(kWave) void k_tile_scan(Dims d, int32_t* __restrict__ work,
                                                      int32_t* __restrict__ counts) {
@@ -80,46 +80,49 @@ __global__ __launch_bounds__(kWave) void k_tile_scan(Dims d, int32_t* __restrict
   const int ns = d.n_sub, spr = d.spr, tpr = d.tpr, E = d.E;
   const int32_t* col = work + (long long)e * ns;
   int32_t* base = work + work_tile_base(d);
+  // every column starts on 16 bytes when ns is a multiple of 4 (work itself is)
+  const bool vec4 = (ns & 3) == 0 && (reinterpret_cast<uintptr_t>(work) & 15) == 0;
   for (int r = lane; r <= d.R; r += kWave) sPre[r] = 0;   // ranks without tokens (S = 0) sum to 0
   __builtin_amdgcn_wave_barrier();
-  // rank and sub-tile within it of this lane's current element, advanced by 64 per chunk
-  int r = spr > 0 ? lane / spr : 0, j = spr > 0 ? lane - r * spr : 0;
   int carry = 0;
-  int nxt[kScanBatch];
+  for (int c0 = 0; c0 < ns; c0 += kScanPer * kWave) {
+    const int i0 = c0 + lane * kScanPer;
+    int v[kScanPer];
+    if (vec4 && i0 + kScanPer <= ns) {
+      // 16-byte loads: a quarter of the load instructions
+      const int4* c4 = reinterpret_cast<const int4*>(col + i0);
 #pragma unroll
-  for (int u = 0; u < kScanBatch; ++u) {
-    const int i = u * kWave + lane;
-    nxt[u] = i < ns ? col[i] : 0;
-  }
-  for (int c0 = 0; c0 < ns; c0 += kScanBatch * kWave) {
-    int v[kScanBatch];
+      for (int u = 0; u < kScanPer / 4; ++u) {
+        const int4 q = c4[u];
+        v[4 * u] = q.x;
+        v[4 * u + 1] = q.y;
+        v[4 * u + 2] = q.z;
+        v[4 * u + 3] = q.w;
+      }
+    } else {
 #pragma unroll
-    for (int u = 0; u < kScanBatch; ++u) v[u] = nxt[u];
-    if (c0 + kScanBatch * kWave < ns) {
+      for (int u = 0; u < kScanPer; ++u) v[u] = i0 + u < ns ? col[i0 + u] : 0;
+    }
+    int s = 0;
 #pragma unroll
-      for (int u = 0; u < kScanBatch; ++u) {
-        const int i = c0 + (kScanBatch + u) * kWave + lane;
-        nxt[u] = i < ns ? col[i] : 0;
+    for (int u = 0; u < kScanPer; ++u) s += v[u];
+    const int incl = wave_incl_scan_dpp(s);
+    int run = carry + incl - s;
+    // rank and sub-tile within it of element i0 (spr > 0 whenever ns > 0)
+    int r = i0 / spr, j = i0 - r * spr;
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) {
+      if (i0 + u < ns) {
+        if (j == 0) sPre[r] = run;
+        if (j % kSubTiles == 0) base[(long long)(r * tpr + j / kSubTiles) * E + e] = run;
+      }
+      run += v[u];
+      if (++j == spr) {
+        j = 0;
+        ++r;
       }
     }
-#pragma unroll
-    for (int u = 0; u < kScanBatch; ++u) {
-      const int i = c0 + u * kWave + lane;
-      if (c0 + u * kWave >= ns) break;       // wave-uniform
-      const int incl = wave_incl_scan_dpp(v[u]);
-      const int excl = carry + incl - v[u];
-      if (i < ns) {
-        if (j == 0) sPre[r] = excl;
-        if (j % kSubTiles == 0) base[(long long)(r * tpr + j / kSubTiles) * E + e] = excl;
-      }
-      carry += __builtin_amdgcn_readlane(incl, kWave - 1);
-      j += kWave;
-      if (j >= spr) {                  // crossed into a later rank (spr > 0 here)
-        const int q = j / spr;
-        r += q;
-        j -= q * spr;
-      }
-    }
+    carry += __builtin_amdgcn_readlane(incl, kWave - 1);
   }
   if (lane == 0) sPre[d.R] = carry;
   __builtin_amdgcn_wave_barrier();

@@ -88,6 +88,8 @@ def test_host_checks_reject_bad_pointers_before_any_launch():
                             None) == -1
     assert L.lbt_route_plan(ctypes.byref(sh), None, None, P(1), P(2), P(3), P(4), P(5), None,
                             None) == -1
+    assert L.lbt_front(ctypes.byref(sh), P(1), None, P(1), P(2), P(3), P(4), P(5), None, P(6),
+                       P(7), P(8), None, None) == -1
     assert L.lbt_align_sort(ctypes.byref(sh), P(1), P(2), None, P(3), P(4), P(5), P(6), None, None) == -1
     assert L.lbt_histogram(None, P(1), P(2), P(3), None, None) == -1
     # training side: row sizes, null and misaligned pointers

@@ -727,8 +727,10 @@ def test_corrupt_plan_is_flagged_not_followed(planner):
 def test_route_plan_matches_separate_calls(case, variant):
     """lbt_route_plan gives bit for bit the outputs of lbt_route_topk followed
     by lbt_plan_balance (ids, gates, counts, the tile offsets align reads,
-    the whole plan blob and the status), for batches that take the one-launch
-    small-batch kernel and for larger ones, and both equal the oracle."""
+    the whole plan blob and the status), and lbt_front those plus
+    lbt_align_sort's (slots, sorted ids, block tables), for batches that take
+    the one-launch small-batch kernel and for larger ones; all equal the
+    oracle."""
     import load_balanced_token_amd as lbt
     t = gu.torch()
     name, over = case
@@ -762,8 +764,22 @@ def test_route_plan_matches_separate_calls(case, variant):
     pf = lbt.plan_fields(gu.d2h(b["plan"]), z, w.R, w.E)
     gu.check_plan(pf, ref["plan"], w.P)
     # and align on the fused outputs
+    for k in ("sorted_ids", "slot"):
+        b[k].fill_(-5)
     path.align_sort(b["ids"], b["work"], b["plan"], b["slot"], b["sorted_ids"], b["block_wrow"],
                     b["block_expert"], b["status"])
     t.cuda.synchronize()
     out = {k: gu.d2h(b[k]) for k in ("slot", "sorted_ids", "block_wrow", "block_expert", "status")}
     gu.check_align(out, ref, w.R, z["C"])
+    # lbt_front: route, plan and align in one call, every output word equal
+    c = path.alloc()
+    del c["recv"], c["y"]
+    for k in ("sorted_ids", "slot"):
+        c[k].fill_(-5)
+    c["status"].fill_(-1)
+    path.front(lg, c, sel_bias=sb)
+    t.cuda.synchronize()
+    for k in ("ids", "gates", "counts", "plan", "status", "slot", "sorted_ids", "block_wrow",
+              "block_expert"):
+        assert t.equal(b[k], c[k]), f"front: {k}"
+    assert t.equal(b["work"][lo: lo + z["n_tiles"] * w.E], c["work"][lo: lo + z["n_tiles"] * w.E])

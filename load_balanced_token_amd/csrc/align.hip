@@ -31,6 +31,9 @@ namespace lbt {
 // Kimi-K3 62 / 49 / 37 / 36 us.)
 constexpr int kAlignThreads = 512;
 constexpr int kBlockWaves = kAlignThreads / kWave;   // blocks handled per workgroup
+// Tile workgroups the chip holds at once (256 CUs, four 512-thread
+// workgroups each).
+constexpr int kAlignTilesOneRound = 1024;
 
 template <int NT>
 __global__ __launch_bounds__(NT) void k_align(
@@ -38,9 +41,20 @@ __global__ __launch_bounds__(NT) void k_align(
     const int32_t* __restrict__ plan, Dims d, int32_t* __restrict__ slot,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_wrow,
     int32_t* __restrict__ block_expert, int32_t* __restrict__ status) {
-  if ((int)blockIdx.x >= d.n_tiles) {
-    const long long gb = (long long)(blockIdx.x - d.n_tiles) * (NT / kWave) + wave_id();
-    if (gb < (long long)d.R * d.n_blocks) align_blocks(plan, d, gb, sorted_ids, block_wrow, block_expert);
+  // Block-table workgroups and tile workgroups share the grid.  When the
+  // tiles fit the chip in one round they go first and the short block-table
+  // workgroups finish under them (DSV3: 256 tiles; dispatching the 510
+  // block-table workgroups first delayed every tile by ~0.8 us).  When the
+  // tiles take several rounds the block-table workgroups go first, or they
+  // would start only after the last tile was dispatched (Kimi-K3: 2048
+  // tiles; placed after them they ended ~3 us past the last tile).
+  const long long nblk = (long long)d.R * d.n_blocks;
+  const int nbw = (int)((nblk + NT / kWave - 1) / (NT / kWave));
+  const bool blocks_first = d.n_tiles > kAlignTilesOneRound;
+  const int bid = (int)blockIdx.x;
+  if (blocks_first ? bid < nbw : bid >= d.n_tiles) {
+    const long long gb = (long long)(blocks_first ? bid : bid - d.n_tiles) * (NT / kWave) + wave_id();
+    if (gb < nblk) align_blocks(plan, d, gb, sorted_ids, block_wrow, block_expert);
     return;
   }
   // LDS, carved to the shape (align_lds_bytes): per expert sH, sO, sHome,
@@ -49,7 +63,7 @@ __global__ __launch_bounds__(NT) void k_align(
   // (first piece << 16 | piece count; without the locality step, sP0: the
   // first piece), sLocCap / sLocRow (r's own instance of e: quota its tokens
   // take, start row), sLP (local pairs of instances on ranks <= r); the
-  // sub-tile masks and prefix counts; per piece sPl,
+  // sub-tile token masks; per piece sPl,
   // sPd, sPr, sPe, sPc, sPLoc (local count) and sRem (start of its share of
   // the pairs left after the local step).
   extern __shared__ int smem[];
@@ -66,8 +80,7 @@ __global__ __launch_bounds__(NT) void k_align(
   int* sLP = sLocRow + Ea;
   int* sP0 = sPN;   // plans without the locality step: first replica segment of e
   uint32_t* sMask = reinterpret_cast<uint32_t*>(sLP + Ea);   // [kSubTiles][E]
-  int* sSub = reinterpret_cast<int*>(sMask + kSubTiles * Ea); // [kSubTiles][E]
-  int* sPl = sSub + kSubTiles * Ea;
+  int* sPl = reinterpret_cast<int*>(sMask + kSubTiles * Ea);
   int* sPd = sPl + Pa;
   int* sPr = sPd + Pa;
   int* sPe = sPr + Pa;
@@ -77,7 +90,7 @@ __global__ __launch_bounds__(NT) void k_align(
 
   const PlanLayout& pl = d.pl;
   const int E = d.E, K = d.K, C = d.C, nh = d.nh;
-  const int tile = blockIdx.x;
+  const int tile = blocks_first ? bid - nbw : bid;
   const int r = tile / d.tpr, j = tile - r * d.tpr;
   const int t0 = r * d.S + j * kTileTokens;
   const int len = min(kTileTokens, d.S - j * kTileTokens);
@@ -181,15 +194,6 @@ __global__ __launch_bounds__(NT) void k_align(
       if (e >= 0 && e < E && (g == 0 || sPe[g - 1] != e)) sP0[e] = g;
     }
   __syncthreads();
-  for (int e = tid; e < E; e += NT) {
-    int run = 0;
-#pragma unroll
-    for (int s = 0; s < kSubTiles; ++s) {
-      sSub[s * E + e] = run;
-      run += __popc(sMask[s * E + e]);
-    }
-  }
-  __syncthreads();
 
   auto place = [&](int p, int e) {
     const long long f = f0 + p;
@@ -201,7 +205,12 @@ __global__ __launch_bounds__(NT) void k_align(
     const int ti = token_of(p);
     const int sub = ti / kSubTokens;
     const uint32_t bit = 1u << (ti % kSubTokens);
-    const int q = sBase[e] + sSub[sub * E + e] + __popc(sMask[sub * E + e] & (bit - 1u));
+    // earlier sub-tiles' pairs of e, read straight from their masks (all
+    // kSubTiles loads issued together; a separate prefix pass would cost a
+    // workgroup barrier)
+    int q = sBase[e] + __popc(sMask[sub * E + e] & (bit - 1u));
+#pragma unroll
+    for (int s = 0; s < kSubTiles; ++s) q += s < sub ? __popc(sMask[s * E + e]) : 0;
     const int h = sH[e];
     int dd, row;
     bool ok = true;
@@ -262,11 +271,11 @@ __global__ __launch_bounds__(NT) void k_align(
   if (flags && status != nullptr) atomicOr(status, flags);
 }
 
-// LDS of a tile workgroup: 10 per-expert arrays, the two [kSubTiles][E]
-// sub-tile tables and 7 per-piece arrays; at most 64 KiB (E = 512, 1024
-// pieces).
+// LDS of a tile workgroup: 10 per-expert arrays, the [kSubTiles][E]
+// sub-tile token masks and 7 per-piece arrays; at most 56 KiB (E = 512,
+// 1024 pieces).
 static size_t align_lds_bytes(const Dims& d) {
-  return sizeof(int) * ((size_t)(10 + 2 * kSubTiles) * d.E + (size_t)7 * d.pl.max_pieces);
+  return sizeof(int) * ((size_t)(10 + kSubTiles) * d.E + (size_t)7 * d.pl.max_pieces);
 }
 
 hipError_t launch_align(const Dims& d, const int32_t* ids, const int32_t* work, const int32_t* plan,

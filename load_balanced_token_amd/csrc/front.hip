@@ -4,11 +4,12 @@
 // A decode step routes a few tokens; each kernel of the path then costs its
 // fixed launch-to-end time, and each waits on what the one before wrote to
 // memory.  For batches of at most 32 tokens one workgroup of 1024 threads
-// routes every token (the route's eight waves), keeps every 32-token
-// sub-tile's expert histogram in LDS, writes the tile offsets and the load
-// matrix, plans from the column sums it already holds, and -- for
-// lbt_front -- places every pair from the plan still in LDS: the outputs of
-// lbt_route_topk, lbt_plan_balance and lbt_align_sort from one launch.
+// routes every token (one token per wave up to 16 tokens, else four per
+// wave on eight waves), keeps every 32-token sub-tile's expert histogram in
+// LDS, writes the tile offsets and the load matrix, plans from the column
+// sums it already holds, and -- for lbt_front -- places every pair from the
+// plan still in LDS: the outputs of lbt_route_topk, lbt_plan_balance and
+// lbt_align_sort from one launch.
 //
 // [MoonEP-GR] section "Online planning, zero copy και στατικά σχήματα" (the
 // plan is made online from the current router output, on the GPU, with no
@@ -25,6 +26,8 @@ namespace lbt {
 
 constexpr int kFrontHist = 16384;   // [sub-tile][E] ints
 constexpr int kFrontBlocks = 2048;  // block-table entries the one-workgroup align handles
+constexpr int kFrontWaveTokens = kPlanThreads / kWave < kWaveRouteTokens ? kPlanThreads / kWave
+                                                                         : kWaveRouteTokens;
 
 static bool front_fits(const Dims& d) {
   return d.N >= 1 && d.N <= kRouteTokens && (long long)d.n_sub * d.E <= kFrontHist;
@@ -85,7 +88,9 @@ __device__ __forceinline__ int front_place(const Dims& d, const PlanSmem& m, con
   }
   // block tables: one block per thread, its segment's real end kept in LDS
   const long long nblk = (long long)R * d.n_blocks;
-  for (long long gb = wt; gb < nblk; gb += nthr) {
+  // (blocks from the group's last thread down, pairs from its first up: a
+  // decode step's 64 pairs and 64 blocks run on two waves side by side)
+  for (long long gb = nthr - 1 - wt; gb < nblk; gb += nthr) {
     const int r = (int)(gb / d.n_blocks), b = (int)(gb - (long long)r * d.n_blocks);
     const int fb = r * nh + m.sRep[r];
     const int nseg = nh + m.sRep[r + 1] - m.sRep[r];
@@ -156,11 +161,17 @@ __global__ __launch_bounds__(kPlanThreads) void k_route_plan(
     for (int e = threadIdx.x; e < E; e += kPlanThreads) tmask[e] = 0u;
   if (threadIdx.x < 12) m.sStat[threadIdx.x] = 0;
   if (threadIdx.x == 0) sFlags = 0;
-  route_span<V, FULL>(logits, bias, d, vec, 0, d.N, ids, gates, rs, [&](long long t, int id) {
+  auto add = [&](long long t, int id) {
     const int r = (int)(t / S), j = (int)(t - (long long)r * S) / kSubTokens;
     atomicAdd(&hist[(r * spr + j) * E + id], 1);
     if (ALIGN) atomicOr(&tmask[id], 1u << (int)t);
-  });
+  };
+  // up to 16 tokens: one per wave (a lane sorts a quarter of the keys);
+  // else four per wave on the route's eight waves
+  if (d.N <= kFrontWaveTokens)
+    route_wave<V, FULL>(logits, bias, d, vec, d.N, ids, gates, rs, add);
+  else
+    route_span<V, FULL>(logits, bias, d, vec, 0, d.N, ids, gates, rs, add);
   __syncthreads();
   // per expert: the tile offsets align reads, the load matrix, and T_e
   int32_t* base = work + work_tile_base(d);

@@ -94,9 +94,10 @@ hipError_t launch_combine_bwd(const Dims& d, const uint16_t* out, const int32_t*
                               const float* gates, int dy_dtype, const void* dy, uint16_t* d_out,
                               float* d_gates, hipStream_t st);
 
-// Workspace layout: sub_counts [E][n_sub] (per 32-token sub-tile, expert-
-// major, for the column scan) followed by tile_base [n_tiles][E] (per
-// 128-token tile, tile-major, for the align step).  Sub-tiles and tiles
+// Workspace layout: sub_counts [n_sub][E] (per 32-token sub-tile, sub-tile-
+// major: each route workgroup writes one contiguous run) followed by
+// tile_base [n_tiles][E] (per 128-token tile, tile-major, for the align
+// step).  Sub-tiles and tiles
 // never cross ranks; tile j of rank r holds its sub-tiles 4j .. 4j+3.
 __host__ __device__ inline long long work_tile_base(const Dims& d) {
   return (long long)d.E * d.n_sub;

@@ -199,7 +199,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_quota(const int32_t* __re
   // ties to the lower index), the load ahead of it their sum, so the
   // per-rank prefix in that order needs no separate scan.  sHx[g] = the
   // load ahead of line position g within its rank (0 at the rank's first
-  // position), sQ[g] = the same plus the load at g.
+  // position), sQ[g] = the same plus the load at g.  (Four lanes per expert,
+  // each comparing every fourth expert of the rank and joined by quad DPP
+  // adds, measured no faster on MI355X: 1.44 vs 1.32 us at DSV3.)
   int maxL = 0;
   for (int e = tid; e < E; e += kPlanThreads) {
     const int rr = div_nh(e, d), r0 = rr * nh, T = m.sT[e];

@@ -4,6 +4,7 @@
 //
 // The top-K itself is in route_core.h.
 #include "route_core.h"
+#include "rows.h"
 
 namespace lbt {
 
@@ -57,77 +58,164 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(const int32_t* __res
   if (flags && status != nullptr) atomicOr(status, flags);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kHistThreads)
-    sub_counts[(long long)e * d.n_sub + sub] = hist[e];
+    sub_counts[(long long)sub * E + e] = hist[e];
 }
 
-// One wave per expert column (one workgroup each, so the columns spread over
-// the CUs): exclusive prefix over the sub-tiles, written at each 128-token
-// tile's first sub-tile (tile-major, for the align step), and per-source-rank
-// sums (the load matrix) as differences of the prefix at the ranks' first
-// sub-tiles (sub-tiles never cross ranks).  Each lane takes kScanPer
-// consecutive sub-tiles of a batch of 64 * kScanPer, sums them in registers,
-// and one wave-wide scan of the lane sums gives every lane its offset, so a
-// batch costs one scan.  (Measured on MI355X, DSV3, 1024 sub-tiles per
-// column: one 64-wide chunk per scan, the chunks scanned one after another
-// with a carried total, took 6.3 us.)
+// The column scan, one workgroup per expert column: exclusive prefix over
+// the sub-tiles, written at each 128-token tile's first sub-tile
+// (tile-major, for the align step), and per-source-rank sums (the load
+// matrix) as differences of the prefix at the ranks' first sub-tiles
+// (sub-tiles never cross ranks).  A batch is 64 * kScanPer consecutive
+// sub-tiles, kScanPer per lane: the lane sums its share in registers and
+// one wave-wide scan of the lane sums gives every lane its offset.  A
+// column of nb batches takes min(nb, 8) waves, each a contiguous run of
+// batches: the waves' totals meet in LDS, then each wave scans its own
+// batches from its offset, its first batches still in registers (so at
+// Kimi-K3, eight batches per column, every load is issued up front; one
+// wave walking the eight batches in turn took 26-29 us, against 4-5 at
+// DSV3's one batch).
+//
+// The sub-tile histograms are sub-tile-major ([n_sub][E]): each route
+// workgroup writes its E counts as one contiguous run (written expert-major,
+// E single counts 4 KB apart, they had cost the DSV3 route ~1.7 us and the
+// Kimi-K3 route ~9 us on MI355X).  A lane's loads then hit a different
+// 128-byte line each, and a line holds 32 neighbouring experts: the columns
+// go to the XCDs in contiguous ranges, so the 32 columns of a line are read
+// through one XCD's L2.  (Measured on MI355X: a workgroup per 16 experts
+// with lanes over sub-tile chunks read whole runs but spread a column's
+// sub-tiles over too few CUs: DSV3 5.6 us, Kimi-K3 36 us.)
 constexpr int kScanPer = 16;
+constexpr int kScanBatch = kScanPer * kWave;
+constexpr int kScanMaxWaves = 8;
 
-__global__ __launch_bounds__(kWave) void k_tile_scan(Dims d, int32_t* __restrict__ work,
-                                                     int32_t* __restrict__ counts) {
-  __shared__ int sPre[kMaxR + 1];   // prefix at each rank's first sub-tile, then the total
-  const int e = blockIdx.x;
-  const int lane = lane_id();
+// C columns per workgroup: C = 4 (E a multiple of 4, 16-byte aligned
+// workspace) reads four neighbouring experts' counts of a sub-tile with one
+// 16-byte load and writes their tile offsets with one 16-byte store, a
+// quarter of the memory requests of one column at a time.
+template <int C>
+__global__ __launch_bounds__(kScanMaxWaves * kWave) void k_tile_scan(Dims d,
+                                                                     int32_t* __restrict__ work,
+                                                                     int32_t* __restrict__ counts) {
+  constexpr int KEEP = C == 1 ? 2 : 1;   // batches a wave keeps in registers
+  __shared__ int sPre[kMaxR + 1][C];     // prefix at each rank's first sub-tile, then the total
+  __shared__ int sTot[kScanMaxWaves][C]; // each wave's total
+  const int e0 = xcd_contiguous(blockIdx.x, gridDim.x) * C;
+  const int lane = lane_id(), w = wave_id(), nw = blockDim.x / kWave;
   const int ns = d.n_sub, spr = d.spr, tpr = d.tpr, E = d.E;
-  const int32_t* col = work + (long long)e * ns;
   int32_t* base = work + work_tile_base(d);
-  // every column starts on 16 bytes when ns is a multiple of 4 (work itself is)
-  const bool vec4 = (ns & 3) == 0 && (reinterpret_cast<uintptr_t>(work) & 15) == 0;
-  for (int r = lane; r <= d.R; r += kWave) sPre[r] = 0;   // ranks without tokens (S = 0) sum to 0
-  __builtin_amdgcn_wave_barrier();
-  int carry = 0;
-  for (int c0 = 0; c0 < ns; c0 += kScanPer * kWave) {
-    const int i0 = c0 + lane * kScanPer;
-    int v[kScanPer];
-    if (vec4 && i0 + kScanPer <= ns) {
-      // 16-byte loads: a quarter of the load instructions
-      const int4* c4 = reinterpret_cast<const int4*>(col + i0);
+  for (int i = threadIdx.x; i < (d.R + 1) * C; i += blockDim.x) sPre[i / C][i % C] = 0;
+  const int nb = (ns + kScanBatch - 1) / kScanBatch;
+  const int bpw = (nb + nw - 1) / nw;
+  const int b0 = min(w * bpw, nb), b1 = min(b0 + bpw, nb);
+  // a batch's values, indices clamped into the column (the loads carry no
+  // branches; masked when used; ns > 0 whenever a wave has a batch)
+  auto load_batch = [&](int b, int (&dst)[kScanPer][C]) {
+    const int i0 = b * kScanBatch + lane * kScanPer;
 #pragma unroll
-      for (int u = 0; u < kScanPer / 4; ++u) {
-        const int4 q = c4[u];
-        v[4 * u] = q.x;
-        v[4 * u + 1] = q.y;
-        v[4 * u + 2] = q.z;
-        v[4 * u + 3] = q.w;
+    for (int u = 0; u < kScanPer; ++u) {
+      const int32_t* p = work + (long long)min(i0 + u, ns - 1) * E + e0;
+      if constexpr (C == 4) {
+        const int4 q = *reinterpret_cast<const int4*>(p);
+        dst[u][0] = q.x;
+        dst[u][1] = q.y;
+        dst[u][2] = q.z;
+        dst[u][3] = q.w;
+      } else {
+        dst[u][0] = *p;
       }
-    } else {
-#pragma unroll
-      for (int u = 0; u < kScanPer; ++u) v[u] = i0 + u < ns ? col[i0 + u] : 0;
     }
-    int s = 0;
+  };
+  auto lane_sums = [&](int b, const int (&v)[kScanPer][C], int (&acc)[C]) {
+    const int i0 = b * kScanBatch + lane * kScanPer;
 #pragma unroll
-    for (int u = 0; u < kScanPer; ++u) s += v[u];
-    const int incl = wave_incl_scan_dpp(s);
-    int run = carry + incl - s;
+    for (int u = 0; u < kScanPer; ++u)
+#pragma unroll
+      for (int c = 0; c < C; ++c) acc[c] += i0 + u < ns ? v[u][c] : 0;
+  };
+  int va[KEEP][kScanPer][C];
+#pragma unroll
+  for (int k = 0; k < KEEP; ++k)
+    if (b0 + k < b1) load_batch(b0 + k, va[k]);
+  // first pass: the wave's totals
+  int part[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) part[c] = 0;
+  for (int b = b0 + KEEP; b < b1; ++b) {
+    int q[kScanPer][C];
+    load_batch(b, q);
+    lane_sums(b, q, part);
+  }
+#pragma unroll
+  for (int k = 0; k < KEEP; ++k)
+    if (b0 + k < b1) lane_sums(b0 + k, va[k], part);
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int wtot = __builtin_amdgcn_readlane(wave_incl_scan_dpp(part[c]), kWave - 1);
+    if (lane == 0) sTot[w][c] = wtot;
+  }
+  __syncthreads();
+  int carry[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    carry[c] = 0;
+    for (int x = 0; x < w; ++x) carry[c] += sTot[x][c];
+  }
+  // second pass: the prefix at every sub-tile of the wave's batches
+  auto scan_batch = [&](int b, const int (&v)[kScanPer][C]) {
+    const int i0 = b * kScanBatch + lane * kScanPer;
+    int run[C], incl[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      int s = 0;
+#pragma unroll
+      for (int u = 0; u < kScanPer; ++u) s += i0 + u < ns ? v[u][c] : 0;
+      incl[c] = wave_incl_scan_dpp(s);
+      run[c] = carry[c] + incl[c] - s;
+    }
     // rank and sub-tile within it of element i0 (spr > 0 whenever ns > 0)
     int r = i0 / spr, j = i0 - r * spr;
 #pragma unroll
     for (int u = 0; u < kScanPer; ++u) {
       if (i0 + u < ns) {
-        if (j == 0) sPre[r] = run;
-        if (j % kSubTiles == 0) base[(long long)(r * tpr + j / kSubTiles) * E + e] = run;
+        if (j == 0)
+#pragma unroll
+          for (int c = 0; c < C; ++c) sPre[r][c] = run[c];
+        if (j % kSubTiles == 0) {
+          int32_t* o = base + (long long)(r * tpr + j / kSubTiles) * E + e0;
+          if constexpr (C == 4)
+            *reinterpret_cast<int4*>(o) = make_int4(run[0], run[1], run[2], run[3]);
+          else
+            *o = run[0];
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) run[c] += v[u][c];
       }
-      run += v[u];
       if (++j == spr) {
         j = 0;
         ++r;
       }
     }
-    carry += __builtin_amdgcn_readlane(incl, kWave - 1);
+#pragma unroll
+    for (int c = 0; c < C; ++c) carry[c] += __builtin_amdgcn_readlane(incl[c], kWave - 1);
+  };
+#pragma unroll
+  for (int k = 0; k < KEEP; ++k)
+    if (b0 + k < b1) scan_batch(b0 + k, va[k]);
+  for (int b = b0 + KEEP; b < b1; ++b) {
+    int q[kScanPer][C];
+    load_batch(b, q);
+    scan_batch(b, q);
   }
-  if (lane == 0) sPre[d.R] = carry;
-  __builtin_amdgcn_wave_barrier();
-  for (int rr = lane; rr < d.R; rr += kWave)
-    counts[(long long)rr * E + e] = sPre[rr + 1] - sPre[rr];
+  if ((int)threadIdx.x < C) {
+    int total = 0;
+    for (int x = 0; x < nw; ++x) total += sTot[x][threadIdx.x];
+    sPre[d.R][threadIdx.x] = total;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < d.R * C; i += blockDim.x) {
+    const int rr = i / C, c = i % C;
+    counts[(long long)rr * E + e0 + c] = sPre[rr + 1][c] - sPre[rr][c];
+  }
 }
 
 hipError_t launch_route(const Dims& d, const float* logits, const float* bias, int32_t* ids,
@@ -165,7 +253,12 @@ hipError_t launch_histogram(const Dims& d, const int32_t* ids, int32_t* work, in
 }
 
 hipError_t launch_tile_scan(const Dims& d, int32_t* work, int32_t* counts, hipStream_t st) {
-  hipLaunchKernelGGL(k_tile_scan, dim3(d.E), dim3(kWave), 0, st, d, work, counts);
+  const long long nb = ((long long)d.n_sub + kScanBatch - 1) / kScanBatch;
+  const int nw = nb < 1 ? 1 : (nb > kScanMaxWaves ? kScanMaxWaves : (int)nb);
+  if (d.E % 4 == 0 && (reinterpret_cast<uintptr_t>(work) & 15) == 0)
+    hipLaunchKernelGGL(k_tile_scan<4>, dim3(d.E / 4), dim3(nw * kWave), 0, st, d, work, counts);
+  else
+    hipLaunchKernelGGL(k_tile_scan<1>, dim3(d.E), dim3(nw * kWave), 0, st, d, work, counts);
   return hipGetLastError();
 }
 

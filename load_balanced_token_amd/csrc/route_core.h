@@ -165,6 +165,9 @@ __device__ __forceinline__ void build_list(const float (&key)[V], float tk, int 
   }
 }
 
+// Tokens route_wave can hold (one RouteScratch row each).
+constexpr int kWaveRouteTokens = kRouteWaves * kRowsPerWave;
+
 // LDS of one route workgroup.
 struct RouteSmem {
   int hist[kMaxE];
@@ -322,8 +325,132 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
   }
 }
 
+// Route tokens [0, N) of a small batch, one token per wave (N <= the
+// caller's waves and N <= kWaveRouteTokens, the winners' scratch rows;
+// every thread of the workgroup calls this, and like
+// route_span it contains one workgroup barrier, after the row loads).  Lane
+// l holds experts [l*W, l*W + W), W = ceil(V / 4) for the 16-lane layout's V,
+// so a lane sorts a quarter of the keys route_span's lanes sort.  A round
+// takes the wave-wide max of the list heads (row max by DPP, then the four
+// rows' maxima by readlane) and the lowest lane holding it (first set bit
+// of a ballot), i.e. the same "largest untaken key, lowest expert on ties".
+// The gates are computed by lanes 0..15 exactly as route_span's row lanes
+// compute them (same 16-lane layout of the row for the softmax, same
+// assignment of k to lanes, same order of additions), so ids and gates are
+// bit for bit route_span's.
+template <int V, bool FULL, typename HistAdd>
+__device__ __forceinline__ void route_wave(const float* __restrict__ logits,
+                                           const float* __restrict__ bias, const Dims& d, int vec,
+                                           int N, int32_t* __restrict__ ids,
+                                           float* __restrict__ gates, RouteScratch& sm,
+                                           HistAdd hist_add) {
+  constexpr int W = (V + 3) / 4;
+  constexpr bool FULLW = FULL && V % 4 == 0;   // E = 16 V = 64 W
+  const int E = d.E, K = d.K;
+  const int lane = lane_id(), t = wave_id();
+  const int e0 = lane * W;
+  const bool valid = t < N;
+  auto& s_id = sm.s_id[t / kRowsPerWave][t % kRowsPerWave];
+  auto& s_key = sm.s_key[t / kRowsPerWave][t % kRowsPerWave];
+  float raw[W];
+  if (valid) {
+    load_row<W, FULLW>(logits + (long long)t * E, E, e0, vec, raw);
+  } else {
+#pragma unroll
+    for (int v = 0; v < W; ++v) raw[v] = 0.f;
+  }
+  __syncthreads();   // the caller's histogram set-up is visible
+  if (!valid) return;
+  float key[W];
+#pragma unroll
+  for (int v = 0; v < W; ++v) {
+    const bool in = FULLW || e0 + v < E;
+    key[v] = in ? (bias != nullptr ? raw[v] + bias[e0 + v] : raw[v]) : -INFINITY;
+  }
+  constexpr int T = W < 4 ? W : 4;
+  float lk[T];
+  int lv[T];
+  build_list<W, T, false>(key, 0.f, 0, lk, lv);
+  bool more = W > T && lk[T - 1] != -INFINITY;
+  for (int k = 0; k < K; ++k) {
+    const uint32_t head = ordered_key(lk[0]);
+    const uint32_t rmax = row_max_u32(head);
+    const uint32_t m01 = max((uint32_t)__builtin_amdgcn_readlane((int)rmax, 0),
+                             (uint32_t)__builtin_amdgcn_readlane((int)rmax, 16));
+    const uint32_t m23 = max((uint32_t)__builtin_amdgcn_readlane((int)rmax, 32),
+                             (uint32_t)__builtin_amdgcn_readlane((int)rmax, 48));
+    const uint32_t wmax = max(m01, m23);
+    const unsigned long long bal = __ballot(head == wmax);
+    const bool win = lane == __ffsll((long long)bal) - 1;
+    const float tk = lk[0];
+    const int tv = lv[0];
+    if (win) {
+      s_id[k] = e0 + tv;
+      s_key[k] = tk;
+#pragma unroll
+      for (int j = 0; j + 1 < T; ++j) {
+        lk[j] = lk[j + 1];
+        lv[j] = lv[j + 1];
+      }
+      lk[T - 1] = -INFINITY;
+    }
+    if constexpr (W > T) {
+      const bool dry = win && more && lk[0] == -INFINITY;
+      if (__any(dry)) {
+        if (dry) {
+          build_list<W, T, true>(key, tk, tv, lk, lv);
+          more = lk[T - 1] != -INFINITY;
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  // gates: lanes 0..15 as the 16 lanes of route_span's row
+  if (lane >= kRowLanes) return;
+  const int rl = lane;
+  const float* lrow = logits + (long long)t * E;
+  const bool raw_keys = bias == nullptr;
+  auto logit_of = [&](int kk) -> double {
+    return raw_keys ? (double)s_key[kk] : (double)lrow[s_id[kk]];
+  };
+  double mx = 0.0, denom = 1.0;
+  if (d.score_fn == LBT_SOFTMAX) {
+    float r16[V];
+    load_row<V, FULL>(lrow, E, rl * V, vec, r16);
+#pragma unroll
+    for (int v = 0; v < V; ++v) r16[v] = (FULL || rl * V + v < E) ? r16[v] : -INFINITY;
+    float m = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < V; ++v) m = fmaxf(m, r16[v]);
+    mx = (double)row_max_f32(m);
+    double sacc = 0.0;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (FULL || rl * V + v < E) sacc += exp((double)r16[v] - mx);
+    denom = row_sum_f64(sacc);
+  }
+  double gsum = 1.0;
+  if (d.renorm) {
+    double part = 0.0;
+    for (int kk = rl; kk < K; kk += kRowLanes) {
+      const double lg = logit_of(kk);
+      part += d.score_fn == LBT_SIGMOID ? 1.0 / (1.0 + exp(-lg)) : exp(lg - mx) / denom;
+    }
+    gsum = row_sum_f64(part);
+  }
+  for (int kk = rl; kk < K; kk += kRowLanes) {
+    const int id = s_id[kk];
+    const double lg = logit_of(kk);
+    double g = d.score_fn == LBT_SIGMOID ? 1.0 / (1.0 + exp(-lg)) : exp(lg - mx) / denom;
+    if (d.renorm) g = g / gsum;
+    ids[(long long)t * K + kk] = id;
+    gates[(long long)t * K + kk] = (float)g;
+    hist_add((long long)t, id);
+  }
+}
+
 // Route the tokens of sub-tile `sub` (kRouteThreads threads) and write its
-// expert histogram to sub_counts[e][sub].
+// expert histogram to sub_counts[sub][e] (one contiguous run).
 template <int V, bool FULL>
 __device__ __forceinline__ void route_sub(const float* __restrict__ logits,
                                           const float* __restrict__ bias, const Dims& d, int vec,
@@ -339,7 +466,7 @@ __device__ __forceinline__ void route_sub(const float* __restrict__ logits,
                 [&](long long, int id) { atomicAdd(&hist[id], 1); });
   __syncthreads();
   for (int e = threadIdx.x; e < d.E; e += kRouteThreads)
-    sub_counts[(long long)e * d.n_sub + sub] = hist[e];
+    sub_counts[(long long)sub * d.E + e] = hist[e];
 }
 
 // Widest aligned logit load (floats) for rows of E floats starting at p.

@@ -132,6 +132,27 @@ __device__ __forceinline__ void front_sentinels(const Dims& d, const int* blk_en
   const int C = d.C, blk = d.blk;
   const long long nblk = (long long)d.R * d.n_blocks;
   const long long nrows = nblk * blk;
+  // C = n_blocks * blk, so row i of the flat [R][C] table is row i % blk of
+  // block i / blk.  With blk a multiple of 4 and a 16-byte aligned table,
+  // four rows share a block and a block's padding is mostly whole 16-byte
+  // groups: one store per four sentinels (the stores, not the LDS reads,
+  // are what this pass costs).
+  if (blk % 4 == 0 && (reinterpret_cast<uintptr_t>(sorted_ids) & 15) == 0) {
+    const int sent = (int)d.P;
+    for (long long q = threadIdx.x; q < nrows / 4; q += kPlanThreads) {
+      const long long i0 = 4 * q;
+      const long long gb = i0 / blk;
+      if (gb >= kFrontBlocks) continue;
+      const int row_b = (int)(gb - gb / d.n_blocks * d.n_blocks) * blk + (int)(i0 - gb * blk);
+      const int end = blk_end[gb];
+      if (row_b >= end) {
+        *reinterpret_cast<int4*>(sorted_ids + i0) = make_int4(sent, sent, sent, sent);
+      } else if (row_b + 4 > end) {
+        for (int t = end - row_b; t < 4; ++t) sorted_ids[i0 + t] = sent;
+      }
+    }
+    return;
+  }
   for (long long i = threadIdx.x; i < nrows; i += kPlanThreads) {
     const long long gb = i / blk;
     const int row = (int)(i - gb * blk);
@@ -173,25 +194,35 @@ __global__ __launch_bounds__(kPlanThreads) void k_route_plan(
   else
     route_span<V, FULL>(logits, bias, d, vec, 0, d.N, ids, gates, rs, add);
   __syncthreads();
-  // per expert: the tile offsets align reads, the load matrix, and T_e
-  int32_t* base = work + work_tile_base(d);
+  // per expert: T_e, the plan's input (LDS only)
   for (int e = threadIdx.x; e < E; e += kPlanThreads) {
     int run = 0;
 #pragma unroll 8
-    for (int r = 0; r < d.R; ++r) {
-      int sum = 0;
-      for (int j = 0; j < spr; ++j) {
-        const int c = hist[(r * spr + j) * E + e];
-        if (j % kSubTiles == 0) base[(long long)(r * tpr + j / kSubTiles) * E + e] = run;
-        run += c;
-        sum += c;
-      }
-      counts[(long long)r * E + e] = sum;
-    }
+    for (int i = 0; i < ns; ++i) run += hist[i * E + e];
     m.sT[e] = run;
     m.sX[e] = run;
   }
   __syncthreads();
+  // the tile offsets align reads and the load matrix, written by waves
+  // 1.. while wave 0 builds the plan (their stores are off the plan's
+  // critical path; decode S=1: 1.0 us of the kernel before)
+  if ((int)threadIdx.x >= kWave) {
+    int32_t* base = work + work_tile_base(d);
+    for (int e = threadIdx.x - kWave; e < E; e += kPlanThreads - kWave) {
+      int run = 0;
+#pragma unroll 8
+      for (int r = 0; r < d.R; ++r) {
+        int sum = 0;
+        for (int j = 0; j < spr; ++j) {
+          const int c = hist[(r * spr + j) * E + e];
+          if (j % kSubTiles == 0) base[(long long)(r * tpr + j / kSubTiles) * E + e] = run;
+          run += c;
+          sum += c;
+        }
+        counts[(long long)r * E + e] = sum;
+      }
+    }
+  }
   if constexpr (!ALIGN) {
     plan_core<false>(d, m, d.SK, counts, nullptr, plan, status);
   } else {

@@ -79,6 +79,11 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict
 // unconsumed position only moves forward, so one candidate costs O(R) steps
 // plus one step per replica segment.
 
+// Row pitch of the per-rank prefixes Q_r in LDS: odd, so that lanes over
+// ranks reading entry j of their rows hit different LDS banks (with the
+// pitch nh = 32 of DSV3 every lane of the threshold check read one bank).
+__device__ __forceinline__ int q_pitch(int nh) { return nh | 1; }
+
 // Whether threshold tau puts at most B replica segments on every rank.
 __device__ __forceinline__ bool tau_fits(int tau, const int* sQ, const int* sL, int R, int nh,
                                          int B) {
@@ -94,7 +99,7 @@ __device__ __forceinline__ bool tau_fits(int tau, const int* sQ, const int* sL, 
       const int ov = sL[ro] - tau;
       const int take = min(cap, ov - off);
       const int end = off + take;
-      const int* q = sQ + ro * nh;
+      const int* q = sQ + ro * q_pitch(nh);
       int ej = ei;                      // expert holding end - 1
       while (ej < nh - 1 && q[ej] < end) ++ej;
       cnt += ej - ei + 1;
@@ -135,7 +140,7 @@ __device__ __forceinline__ bool tau_fits_wave(int tau, const int* sQ, const int*
   // i.e. the ones whose prefix is below ov and the first that reaches it
   int nv = 0;
   if (ov > 0) {
-    const int* q = sQ + r * nh;
+    const int* q = sQ + r * q_pitch(nh);
 #pragma unroll 8
     for (int j = 0; j < nh; ++j) nv += q[j] < ov;
     ++nv;
@@ -158,8 +163,8 @@ __device__ __forceinline__ bool tau_fits_wave(int tau, const int* sQ, const int*
   // clamped so lanes without an interval still read in bounds
   const int ra = max(ca - 1, 0), rb = max(cb - 1, 0);
   const int ya = xa - ov_off[ra], yb = xb - ov_off[rb];
-  const int* qa = sQ + ra * nh;
-  const int* qb = sQ + rb * nh;
+  const int* qa = sQ + ra * q_pitch(nh);
+  const int* qb = sQ + rb * q_pitch(nh);
   int ja = 0, jb = 0;
 #pragma unroll 8
   for (int j = 0; j < nh; ++j) {
@@ -181,7 +186,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_quota(const int32_t* __re
                                                             Dims d, int32_t* __restrict__ plan,
                                                             int32_t* __restrict__ status) {
   __shared__ PlanSmem m;
-  __shared__ int sQ[kMaxE];     // per-rank inclusive prefix of the loads in shedding order
+  // per-rank inclusive prefix of the loads in shedding order, rank r's row
+  // at r * q_pitch(nh)
+  __shared__ int sQ[kMaxE + kMaxR];
   __shared__ int sLr[kMaxR];    // L_r
   __shared__ int sCnt[kQuotaCountsLds];   // the load matrix, when it fits
   alignas(16) __shared__ int sOvOff[kPlanThreads / kWave][kWave];   // per-wave scratch of the first stage
@@ -199,9 +206,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_quota(const int32_t* __re
   // ties to the lower index), the load ahead of it their sum, so the
   // per-rank prefix in that order needs no separate scan.  sHx[g] = the
   // load ahead of line position g within its rank (0 at the rank's first
-  // position), sQ[g] = the same plus the load at g.  (Four lanes per expert,
-  // each comparing every fourth expert of the rank and joined by quad DPP
-  // adds, measured no faster on MI355X: 1.44 vs 1.32 us at DSV3.)
+  // position), Q_r[pos] = the same plus the load at that position.  (Four
+  // lanes per expert, each comparing every fourth expert of the rank and
+  // joined by quad DPP adds, measured no faster on MI355X: 1.44 vs 1.32 us
+  // at DSV3.)
   int maxL = 0;
   for (int e = tid; e < E; e += kPlanThreads) {
     const int rr = div_nh(e, d), r0 = rr * nh, T = m.sT[e];
@@ -218,7 +226,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_quota(const int32_t* __re
     m.sLam[e] = g;
     m.sPerm[g] = e;
     m.sHx[g] = ahead;
-    sQ[g] = ahead + T;
+    sQ[rr * q_pitch(nh) + pos] = ahead + T;
     if (e == r0) sLr[rr] = L;
     maxL = max(maxL, L);
   }

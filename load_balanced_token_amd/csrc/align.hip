@@ -140,7 +140,7 @@ __global__ __launch_bounds__(NT) void k_align(
   if (local) {
     // per expert: walk its instances (home, then its pieces in line order)
     for (int e = tid; e < E; e += NT) {
-      const int he = e / nh;
+      const int he = div_nh(e, d);
       int cap = 0, row0 = 0, lp = 0;
       if (he == r) {
         cap = sHL[e];
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(NT) void k_align(
         const int qr = q - sLP[e];             // rank among the pairs left after the local step
         const int hrem = h - sHL[e];
         if (qr < hrem) {
-          dd = e / nh;
+          dd = div_nh(e, d);
           row = sHome[e] + sHL[e] + qr;
         } else {
           // the last of e's pieces whose share starts at or below qr
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(NT) void k_align(
         }
       }
     } else if (q < h) {
-      dd = e / nh;
+      dd = div_nh(e, d);
       row = sHome[e] + q;
     } else {
       // the last of e's segments starting at or below its line position o

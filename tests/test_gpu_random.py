@@ -108,13 +108,39 @@ def small_case(seed):
     E = R * int(rng.integers(1, 512 // R + 1)) if rng.random() < 0.5 else R * int(rng.integers(1, 9))
     E = min(E, 512)
     K = int(rng.integers(1, min(E, 64) + 1))
-    blk = int(rng.choice([1, 4, 16, 128]))
+    blk = int(rng.choice([1, 3, 4, 16, 128]))
     B = int(rng.integers(0, 4))
     score = "softmax" if rng.random() < 0.3 else "sigmoid"
     logits = rng.standard_normal((R * S, E)).astype(np.float32)
     planner = "quota" if seed % 2 else "fixed"
     w = WORKLOADS["tiny"].with_(E=E, K=K, R=R, S=S, H=64, B=B, blk=blk, score=score)
     return w, logits, planner
+
+
+def _front_matches_separate_calls(w, logits):
+    """lbt_front (route, fixed-rule plan and align in one launch: one token
+    per wave up to 16 tokens, four per wave above; padding sentinels four
+    rows per store when blk is a multiple of 4, else one) against
+    lbt_route_topk + lbt_plan_balance + lbt_align_sort, every output word."""
+    import load_balanced_token_amd as lbt
+    t = gu.torch()
+    path = lbt.Path(gu.shape_of(w))
+    a, b = path.alloc(), path.alloc()
+    for buf in (a, b):
+        del buf["recv"], buf["y"]
+        buf["sorted_ids"].fill_(-5)
+        buf["slot"].fill_(-5)
+        buf["status"].zero_()
+    lg = gu.h2d(logits)
+    path.route_topk(lg, a["ids"], a["gates"], a["counts"], a["work"])
+    path.plan_balance(a["counts"], a["plan"], a["status"])
+    path.align_sort(a["ids"], a["work"], a["plan"], a["slot"], a["sorted_ids"], a["block_wrow"],
+                    a["block_expert"], a["status"])
+    path.front(lg, b)
+    t.cuda.synchronize()
+    for k in ("ids", "gates", "counts", "plan", "status", "slot", "sorted_ids", "block_wrow",
+              "block_expert"):
+        assert t.equal(a[k], b[k]), f"front: {k}"
 
 
 @pytest.mark.parametrize("seed", range(24))
@@ -129,6 +155,7 @@ def test_small_batches(seed):
     gu.check_plan(res["plan_fields"], ref["plan"], w.P)
     gu.check_align(res, ref, w.R, res["sizes"]["C"])
     _full_move_check(w, res, ref, activations(w, 0))
+    _front_matches_separate_calls(w, logits)
 
 
 @pytest.mark.parametrize("planner", ["fixed", "quota"])

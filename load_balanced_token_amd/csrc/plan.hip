@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_quota(const int32_t* __re
   alignas(16) __shared__ int sOvOff[kPlanThreads / kWave][kWave];   // per-wave scratch of the first stage
   __shared__ int sNvOff[kPlanThreads / kWave][kWave];
   const int E = d.E, R = d.R, nh = d.nh, tid = threadIdx.x;
-  __shared__ int sFound[2];   // smallest qualifying tau of the first two stages
+  __shared__ int sFound[2];   // [1]: smallest qualifying tau of the wave stage
   // [10]: smallest qualifying tau of the batches, [11]: max_r L_r
   if (tid < 12) m.sStat[tid] = tid == 10 ? INT_MAX : 0;
   if (tid < 2) sFound[tid] = INT_MAX;
@@ -236,19 +236,30 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_quota(const int32_t* __re
 
   const int hi = min(m.sStat[11], d.tau_max);
   constexpr int kPlanWaves = kPlanThreads / kWave;
-  int found = INT_MAX;   // smallest qualifying candidate of the stages below (uniform)
+  int found = INT_MAX;   // smallest qualifying threshold found (uniform)
   int next = d.SK;       // first candidate not checked yet
-  if (R <= kWave) {
-    // tau = S*K first, by wave 0 alone, so no other wave competes for the
-    // LDS (with the slot counts the pages use it qualifies; measured on
-    // MI355X at DSV3: 16 candidates at once, one per wave, took 3.7 us)
-    if (wave_id() == 0 && d.SK <= hi &&
-        tau_fits_wave(d.SK, sQ, sLr, R, nh, d.B, sOvOff[0], sNvOff[0]) && lane_id() == 0)
-      sFound[0] = d.SK;
-    __syncthreads();
-    found = sFound[0];
-    next = d.SK + 1;
-    if (found == INT_MAX) {
+  bool built = false;
+  if (d.SK <= hi) {
+    // tau = S*K first, by building its plan: it stands when the load matrix
+    // is consistent and no rank takes more than B replica segments, which
+    // is the check the search makes (the plan's replicas per rank are the
+    // segments the search counts), so the common case -- the pages' slot
+    // counts -- pays for no separate check (a one-wave check of tau = S*K
+    // took 1.7 us at DSV3 before the plan; 16 candidates at once, 3.7 us)
+    plan_build<true>(d, m, d.SK);
+    const bool consistent = (m.sStat[4] & LBT_ST_BADCOUNT) == 0;
+    if (consistent && m.sStat[9] <= d.B) {
+      found = d.SK;
+      built = true;
+    } else if (consistent) {
+      next = d.SK + 1;   // S*K checked and too many segments on some rank
+    }
+    __syncthreads();     // every thread has read the stats before they are rewritten
+  }
+  if (!built) {
+    // plan_build scans T_e in place: restore it for the second build
+    for (int e = tid; e < E; e += kPlanThreads) m.sX[e] = m.sT[e];
+    if (R <= kWave && next <= hi) {
       // the next kPlanWaves candidates, one per wave
       const int tau = next + wave_id();
       if (tau <= hi &&
@@ -259,21 +270,23 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_quota(const int32_t* __re
       found = sFound[1];
       next += kPlanWaves;
     }
+    // then ascending batches, one candidate per thread (high throughput)
+    for (int base = next; found == INT_MAX && base <= hi; base += kPlanThreads) {
+      const int tau = base + tid;
+      const bool ok = tau <= hi && tau_fits(tau, sQ, sLr, R, nh, d.B);
+      const unsigned long long bal = __ballot(ok);
+      // lanes hold ascending candidates: the lowest set lane has the wave's smallest
+      if (bal != 0ull && lane_id() == __ffsll((long long)bal) - 1) atomicMin(&m.sStat[10], tau);
+      __syncthreads();
+      const int f = m.sStat[10];
+      __syncthreads();   // every thread has read it before the next batch writes
+      if (f != INT_MAX) found = f;
+    }
+    const int tau = found == INT_MAX ? d.tau_max : found;
+    __syncthreads();     // the restored T_e is visible
+    plan_build<true>(d, m, tau);
   }
-  // then ascending batches, one candidate per thread (high throughput)
-  for (int base = next; found == INT_MAX && base <= hi; base += kPlanThreads) {
-    const int tau = base + tid;
-    const bool ok = tau <= hi && tau_fits(tau, sQ, sLr, R, nh, d.B);
-    const unsigned long long bal = __ballot(ok);
-    // lanes hold ascending candidates: the lowest set lane has the wave's smallest
-    if (bal != 0ull && lane_id() == __ffsll((long long)bal) - 1) atomicMin(&m.sStat[10], tau);
-    __syncthreads();
-    const int f = m.sStat[10];
-    __syncthreads();   // every thread has read it before the next batch writes
-    if (f != INT_MAX) found = f;
-  }
-  const int tau = found == INT_MAX ? d.tau_max : found;
-  plan_core<true>(d, m, tau, counts, keep ? sCnt : nullptr, plan, status);
+  plan_write<true>(d, m, counts, keep ? sCnt : nullptr, plan, status, tid, kPlanThreads);
 }
 
 hipError_t launch_plan(const Dims& d, const int32_t* counts, int32_t* plan, int32_t* status,

@@ -212,10 +212,10 @@ int lbt_route_plan(const lbt_shape* s, const float* logits, const float* sel_bia
  * block-aligned sort -- the outputs of lbt_route_topk, lbt_plan_balance and
  * lbt_align_sort, bit for bit (status: the plan's bits ORed with the align
  * step's).  Batches of at most 32 tokens (with R * ceil(S / 32) * E <=
- * 16384) run as one workgroup that keeps the routing, the load matrix and
- * the plan in LDS and places every pair from them -- one launch where the
- * three calls make three; larger batches make the same launches as the
- * three calls.  [MoonEP-GR] section "Online planning, zero copy και στατικά
+ * 16384 and R * C / blk <= 2048) run as one workgroup that keeps the
+ * routing, the load matrix and the plan in LDS and places every pair from
+ * them -- one launch where the three calls make three; other batches make
+ * the same launches as the three calls.  [MoonEP-GR] section "Online planning, zero copy και στατικά
  * σχήματα"; [AlignSort]; [UltraEP] section "その仕組みは...".  Arguments as
  * for the three calls. */
 int lbt_front(const lbt_shape* s, const float* logits, const float* sel_bias, int32_t* ids,

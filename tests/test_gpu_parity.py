@@ -659,6 +659,20 @@ def test_route_width_ladder(E, K, R):
     _edge(w)
 
 
+@pytest.mark.parametrize("E,R,S", [(60, 5, 7000), (66, 3, 27000), (96, 2, 33000)])
+def test_column_scan_batches(E, R, S):
+    """Columns of more than 1024 sub-tiles, where the column scan spreads a
+    column's batches over several waves, with a ragged last batch and ranks
+    that end inside a batch: four columns per workgroup (E a multiple of
+    4) and one (E = 66); load matrix, plan and placement equal the
+    oracle's, full rows moved."""
+    w = WORKLOADS["dsv3"].with_(E=E, K=4, R=R, S=S, H=64, B=4, blk=16)
+    n_sub = R * -(-S // 32)
+    print(f"[parity] column scan E={E} R={R} S={S}: {n_sub} sub-tiles", flush=True)
+    assert n_sub > 1024
+    _edge(w)
+
+
 @pytest.mark.parametrize("case,planner", [("E512_K64", "fixed"), ("E512_K64", "quota"),
                                           ("R512", "fixed"), ("R512", "quota"),
                                           ("R65", "fixed"), ("R65", "quota"),

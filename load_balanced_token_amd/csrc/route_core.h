@@ -35,6 +35,27 @@ __device__ __forceinline__ uint32_t ordered_key(float v) {
   return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
+// The value of an ordered key (its inverse; -0.0 comes back as +0.0).
+__device__ __forceinline__ float ordered_value(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o ^ 0x80000000u) : ~o);
+}
+
+// Median of three (the compiler emits one v_med3_u32).
+__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+  return min(max(a, b), max(min(a, b), c));
+}
+
+// Insert x into l[0..T), kept descending, so that l holds the T largest of
+// the values inserted so far, repeats included: position j takes the median
+// of its old value, x and the old value above it.  0 (below every ordered
+// key) marks an empty entry; inserting 0 changes nothing.
+template <int T>
+__device__ __forceinline__ void list_insert(uint32_t (&l)[T], uint32_t x) {
+#pragma unroll
+  for (int j = T - 1; j > 0; --j) l[j] = med3_u32(l[j - 1], x, l[j]);
+  l[0] = max(l[0], x);
+}
+
 // DPP lane permutations inside a 16-lane row.
 constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
@@ -129,10 +150,12 @@ __device__ __forceinline__ void load_row(const float* __restrict__ row, int E, i
   for (int v = 0; v < V; ++v) raw[v] = (FULL || e0 + v < E) ? row[e0 + v] : 0.f;
 }
 
-// Winners of each round per wave, token row and k: expert and its key.
+// Winners of each round per wave, token row and k: the expert and the key
+// bits (route_span records the winning lane and its count of earlier wins
+// of the same value during the rounds, and the expert once it is known).
 struct RouteScratch {
   int s_id[kRouteWaves][kRowsPerWave][kMaxK];
-  float s_key[kRouteWaves][kRowsPerWave][kMaxK];
+  uint32_t s_key[kRouteWaves][kRowsPerWave][kMaxK];
 };
 
 // The lane's best T keys among those that come after (tk, tv) in the order
@@ -190,7 +213,7 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
                                            float* __restrict__ gates, RouteScratch& sm,
                                            HistAdd hist_add) {
   auto& s_id = sm.s_id;
-  auto& s_key = sm.s_key;
+  auto& s_okey = sm.s_key;   // ordered keys
   const int E = d.E, K = d.K;
 
   const int lane = lane_id(), wv = wave_id();
@@ -218,56 +241,63 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
     const int i = (u * kRouteWaves + wv) * kRowsPerWave + row;
     const bool valid = i < len;
     if (!__any(valid)) continue;
-    // keys only from here on: gates and the softmax re-read the row, so the
-    // raw values do not stay live through the rounds
-    float key[V];
-    if (bias != nullptr) {
+    // Keys as order-preserving u32 (equal floats, -0.0 and +0.0 included,
+    // give equal keys); 0 stands for "no expert" past E.  The raw values do
+    // not stay live through the rounds: the gates and the softmax re-read
+    // the row.
+    uint32_t ok[V];
 #pragma unroll
-      for (int v = 0; v < V; ++v)
-        key[v] = (FULL || e0 + v < E) ? rows[u][v] + bias[e0 + v] : -INFINITY;
-    } else {
-#pragma unroll
-      for (int v = 0; v < V; ++v) key[v] = (FULL || e0 + v < E) ? rows[u][v] : -INFINITY;
+    for (int v = 0; v < V; ++v) {
+      const float x = bias != nullptr ? rows[u][v] + bias[e0 + v] : rows[u][v];
+      ok[v] = (FULL || e0 + v < E) ? ordered_key(x) : 0u;
     }
-    // Each lane keeps its best T keys sorted (key desc, local index asc);
-    // a round compares list heads across the row and the winner pops.  A
-    // lane whose full list runs dry refills from the keys after the one it
-    // gave up last, so the order of choices is exactly the K rounds of
-    // "largest untaken key, lowest expert on ties".
+    // Each lane keeps its best T key values sorted, without their experts;
+    // a round compares list heads across the row, the lowest lane holding
+    // the largest wins and pops its head.  A lane whose full list runs dry
+    // refills from the values after the ones it gave up.  Which expert a
+    // win was is settled after the rounds: a lane's equal keys are taken in
+    // expert order, so its i-th win of a value is the i-th of its experts
+    // holding that value.  Together this is exactly K rounds of "largest
+    // untaken key, lowest expert on ties".
     constexpr int T = V < 4 ? V : 4;
-    float lk[T];
-    int lv[T];
-    build_list<V, T, false>(key, 0.f, 0, lk, lv);
-    bool more = V > T && lk[T - 1] != -INFINITY;   // the lane may hold keys past its list
+    uint32_t l[T];
+#pragma unroll
+    for (int j = 0; j < T; ++j) l[j] = 0u;
+#pragma unroll
+    for (int v = 0; v < V; ++v) list_insert<T>(l, ok[v]);
+    bool more = V > T && l[T - 1] != 0u;   // the lane may hold keys past its list
+    uint32_t last = 0u;                     // the value it gave up last
+    int eq = 0;                             // its wins of that value so far
     for (int k = 0; k < K; ++k) {
-      // the row max runs on order-preserving bits of the list heads
-      const uint32_t head = ordered_key(lk[0]);
+      const uint32_t head = l[0];
       const uint32_t rmax = row_max_u32(head);
       const bool cand = valid && head == rmax;
       // the lowest candidate lane of the row holds the lowest expert
       const uint32_t first = row_min_u32(cand ? (uint32_t)rl : (uint32_t)kRowLanes);
       const bool win = cand && (uint32_t)rl == first;
-      // the winner records its expert and pops its head
-      const float tk = lk[0];
-      const int tv = lv[0];
       if (win) {
-        s_id[wv][row][k] = e0 + tv;
-        s_key[wv][row][k] = tk;
+        eq = head == last ? eq + 1 : 1;
+        last = head;
+        s_id[wv][row][k] = (eq - 1) * kRowLanes + rl;
+        s_okey[wv][row][k] = head;
 #pragma unroll
-        for (int j = 0; j + 1 < T; ++j) {
-          lk[j] = lk[j + 1];
-          lv[j] = lv[j + 1];
-        }
-        lk[T - 1] = -INFINITY;
+        for (int j = 0; j + 1 < T; ++j) l[j] = l[j + 1];
+        l[T - 1] = 0u;
       }
       if constexpr (V > T) {
-        // a lane whose list ran dry while it may hold more keys refills
-        // from the keys after the one it just gave up (rare)
-        const bool dry = win && more && lk[0] == -INFINITY;
+        const bool dry = win && more && l[0] == 0u;
         if (__any(dry)) {
           if (dry) {
-            build_list<V, T, true>(key, tk, tv, lk, lv);
-            more = lk[T - 1] != -INFINITY;
+            // every key below `last`, and those equal to it past the first
+            // `eq` in expert order (rare)
+            int seen = 0;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+              const bool same = ok[v] == last;
+              list_insert<T>(l, (ok[v] < last || (same && seen >= eq)) ? ok[v] : 0u);
+              seen += same ? 1 : 0;
+            }
+            more = l[T - 1] != 0u;
           }
         }
       }
@@ -275,25 +305,44 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
     __builtin_amdgcn_wave_barrier();
 
     const long long t = (long long)t0 + i;
-    // Without a selection bias the keys are the raw logits, so the gates
-    // need no second read of the row; with one, the raw values are read
-    // back from the row just loaded (cache hits).
     const float* lrow = logits + (valid ? t : (long long)t0) * E;
-    const bool raw_keys = bias == nullptr;
-    auto logit_of = [&](int kk) -> double {
-      return raw_keys ? (double)s_key[wv][row][kk] : (double)lrow[s_id[wv][row][kk]];
+    // Winner kk's expert: with (lane wl, its wins of the value before this
+    // one) recorded in the round, the matching key among lane wl's experts,
+    // read back from the row just loaded (cache hits).
+    auto expert_of = [&](int kk) -> int {
+      const int code = s_id[wv][row][kk];
+      const int wl = code % kRowLanes, occ = code / kRowLanes;
+      const float xv = ordered_value(s_okey[wv][row][kk]);
+      const int w0 = wl * V;
+      float kv[V];
+      load_row<V, FULL>(lrow, E, w0, vec, kv);
+      if (bias != nullptr) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) kv[v] += (FULL || w0 + v < E) ? bias[w0 + v] : 0.f;
+      }
+      int at = 0;
+      if (occ == 0) {
+#pragma unroll
+        for (int v = V - 1; v >= 0; --v)
+          if ((FULL || w0 + v < E) && kv[v] == xv) at = v;
+      } else {
+        int seen = 0;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const bool same = (FULL || w0 + v < E) && kv[v] == xv;
+          if (same && seen == occ) at = v;
+          seen += same ? 1 : 0;
+        }
+      }
+      return w0 + at;
     };
+    const bool raw_keys = bias == nullptr;
     double mx = 0.0, denom = 1.0;
     if (d.score_fn == LBT_SOFTMAX) {
       float raw[V];
-      if (raw_keys) {
+      load_row<V, FULL>(lrow, E, e0, vec, raw);
 #pragma unroll
-        for (int v = 0; v < V; ++v) raw[v] = key[v];   // -inf past E
-      } else {
-        load_row<V, FULL>(lrow, E, e0, vec, raw);
-#pragma unroll
-        for (int v = 0; v < V; ++v) raw[v] = (FULL || e0 + v < E) ? raw[v] : -INFINITY;
-      }
+      for (int v = 0; v < V; ++v) raw[v] = (FULL || e0 + v < E) ? raw[v] : -INFINITY;
       float m = -INFINITY;
 #pragma unroll
       for (int v = 0; v < V; ++v) m = fmaxf(m, raw[v]);
@@ -304,24 +353,50 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
         if (FULL || e0 + v < E) s += exp((double)raw[v] - mx);
       denom = row_sum_f64(s);
     }
-    double gsum = 1.0;
-    if (d.renorm) {
-      double part = 0.0;
-      for (int kk = rl; kk < K; kk += kRowLanes) {
-        const double lg = valid ? logit_of(kk) : 0.0;
-        part += d.score_fn == LBT_SIGMOID ? 1.0 / (1.0 + exp(-lg)) : exp(lg - mx) / denom;
+    auto score = [&](double lg) -> double {
+      return d.score_fn == LBT_SIGMOID ? 1.0 / (1.0 + exp(-lg)) : exp(lg - mx) / denom;
+    };
+    // the logit of winner kk, expert id: without a selection bias the key
+    // is the logit (-0.0 comes back as +0.0, which scores the same)
+    auto logit_of = [&](int kk, int id) -> double {
+      return raw_keys ? (double)ordered_value(s_okey[wv][row][kk]) : (double)lrow[id];
+    };
+    if (K <= kRowLanes) {
+      // one choice per lane: its score serves both the row sum and the gate
+      const bool mine = valid && rl < K;
+      int id = 0;
+      double g = 0.0;
+      if (mine) {
+        id = expert_of(rl);
+        g = score(logit_of(rl, id));
       }
-      gsum = row_sum_f64(part);
-    }
-    if (valid) {
-      for (int kk = rl; kk < K; kk += kRowLanes) {
-        const int id = s_id[wv][row][kk];
-        const double lg = logit_of(kk);
-        double g = d.score_fn == LBT_SIGMOID ? 1.0 / (1.0 + exp(-lg)) : exp(lg - mx) / denom;
-        if (d.renorm) g = g / gsum;
-        ids[t * K + kk] = id;
-        gates[t * K + kk] = (float)g;
+      if (d.renorm) g = g / row_sum_f64(g);
+      if (mine) {
+        s_id[wv][row][rl] = id;   // the expert, for callers that read the winners back
+        ids[t * K + rl] = id;
+        gates[t * K + rl] = (float)g;
         hist_add(t, id);
+      }
+    } else {
+      if (valid)
+        for (int kk = rl; kk < K; kk += kRowLanes) s_id[wv][row][kk] = expert_of(kk);
+      __builtin_amdgcn_wave_barrier();
+      double gsum = 1.0;
+      if (d.renorm) {
+        double part = 0.0;
+        for (int kk = rl; kk < K; kk += kRowLanes)
+          part += valid ? score(logit_of(kk, s_id[wv][row][kk])) : 0.0;
+        gsum = row_sum_f64(part);
+      }
+      if (valid) {
+        for (int kk = rl; kk < K; kk += kRowLanes) {
+          const int id = s_id[wv][row][kk];
+          double g = score(logit_of(kk, id));
+          if (d.renorm) g = g / gsum;
+          ids[t * K + kk] = id;
+          gates[t * K + kk] = (float)g;
+          hist_add(t, id);
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -389,7 +464,7 @@ __device__ __forceinline__ void route_wave(const float* __restrict__ logits,
     const int tv = lv[0];
     if (win) {
       s_id[k] = e0 + tv;
-      s_key[k] = tk;
+      s_key[k] = __float_as_uint(tk);
 #pragma unroll
       for (int j = 0; j + 1 < T; ++j) {
         lk[j] = lk[j + 1];
@@ -414,7 +489,7 @@ __device__ __forceinline__ void route_wave(const float* __restrict__ logits,
   const float* lrow = logits + (long long)t * E;
   const bool raw_keys = bias == nullptr;
   auto logit_of = [&](int kk) -> double {
-    return raw_keys ? (double)s_key[kk] : (double)lrow[s_id[kk]];
+    return raw_keys ? (double)__uint_as_float(s_key[kk]) : (double)lrow[s_id[kk]];
   };
   double mx = 0.0, denom = 1.0;
   if (d.score_fn == LBT_SOFTMAX) {
@@ -432,19 +507,29 @@ __device__ __forceinline__ void route_wave(const float* __restrict__ logits,
       if (FULL || rl * V + v < E) sacc += exp((double)r16[v] - mx);
     denom = row_sum_f64(sacc);
   }
+  auto score = [&](double lg) -> double {
+    return d.score_fn == LBT_SIGMOID ? 1.0 / (1.0 + exp(-lg)) : exp(lg - mx) / denom;
+  };
+  if (K <= kRowLanes) {
+    double g = rl < K ? score(logit_of(rl)) : 0.0;
+    if (d.renorm) g = g / row_sum_f64(g);
+    if (rl < K) {
+      const int id = s_id[rl];
+      ids[(long long)t * K + rl] = id;
+      gates[(long long)t * K + rl] = (float)g;
+      hist_add((long long)t, id);
+    }
+    return;
+  }
   double gsum = 1.0;
   if (d.renorm) {
     double part = 0.0;
-    for (int kk = rl; kk < K; kk += kRowLanes) {
-      const double lg = logit_of(kk);
-      part += d.score_fn == LBT_SIGMOID ? 1.0 / (1.0 + exp(-lg)) : exp(lg - mx) / denom;
-    }
+    for (int kk = rl; kk < K; kk += kRowLanes) part += score(logit_of(kk));
     gsum = row_sum_f64(part);
   }
   for (int kk = rl; kk < K; kk += kRowLanes) {
     const int id = s_id[kk];
-    const double lg = logit_of(kk);
-    double g = d.score_fn == LBT_SIGMOID ? 1.0 / (1.0 + exp(-lg)) : exp(lg - mx) / denom;
+    double g = score(logit_of(kk));
     if (d.renorm) g = g / gsum;
     ids[(long long)t * K + kk] = id;
     gates[(long long)t * K + kk] = (float)g;

@@ -117,7 +117,7 @@ def small_case(seed):
     return w, logits, planner
 
 
-def _front_matches_separate_calls(w, logits):
+def _front_matches_separate_calls(w, logits, sel_bias=None):
     """lbt_front (route, fixed-rule plan and align in one launch: one token
     per wave up to 16 tokens, four per wave above; padding sentinels four
     rows per store when blk is a multiple of 4, else one) against
@@ -132,11 +132,12 @@ def _front_matches_separate_calls(w, logits):
         buf["slot"].fill_(-5)
         buf["status"].zero_()
     lg = gu.h2d(logits)
-    path.route_topk(lg, a["ids"], a["gates"], a["counts"], a["work"])
+    sb = None if sel_bias is None else gu.h2d(np.asarray(sel_bias, np.float32))
+    path.route_topk(lg, a["ids"], a["gates"], a["counts"], a["work"], sel_bias=sb)
     path.plan_balance(a["counts"], a["plan"], a["status"])
     path.align_sort(a["ids"], a["work"], a["plan"], a["slot"], a["sorted_ids"], a["block_wrow"],
                     a["block_expert"], a["status"])
-    path.front(lg, b)
+    path.front(lg, b, sel_bias=sb)
     t.cuda.synchronize()
     for k in ("ids", "gates", "counts", "plan", "status", "slot", "sorted_ids", "block_wrow",
               "block_expert"):
@@ -156,6 +157,39 @@ def test_small_batches(seed):
     gu.check_align(res, ref, w.R, res["sizes"]["C"])
     _full_move_check(w, res, ref, activations(w, 0))
     _front_matches_separate_calls(w, logits)
+
+
+@pytest.mark.parametrize("E,K,S,score,bias", [
+    (256, 8, 40, "sigmoid", False), (256, 8, 2, "sigmoid", True), (384, 8, 40, "sigmoid", True),
+    (256, 24, 40, "softmax", False), (512, 64, 4, "sigmoid", True), (384, 16, 1, "softmax", False),
+    (256, 5, 3, "sigmoid", False)])
+def test_ties_wide_rows(E, K, S, score, bias):
+    """Rows of 256-512 experts whose keys take a few values (many exact ties,
+    signed zeros, also in the selection bias), so equal keys meet inside
+    one lane's run of experts and across lanes; every third row has its
+    K + 4 first experts tied at the top, and every third row K distinct top
+    keys on consecutive experts, so one lane wins every round and its short
+    sorted list runs dry and refills.  ids must follow the oracle's order
+    (key descending, lower expert on equal keys) exactly; up to 32 tokens the
+    fused front must match the separate calls word for word."""
+    w = WORKLOADS["dsv3"].with_(E=E, K=K, R=8, S=S, H=64, B=4, blk=16, score=score)
+    print(f"[ties] E={E} K={K} S={S} {score} bias={bias}", flush=True)
+    rng = np.random.default_rng(E * 1000 + K * 10 + S)
+    logits = (rng.integers(-2, 3, size=(w.N, E)) * 0.5).astype(np.float32)
+    logits[rng.random(logits.shape) < 0.2] = np.float32(-0.0)
+    logits[0::3, :K + 4] = 3.0
+    logits[1::3, 20:20 + K] = 2.0 + 0.125 * np.arange(K, dtype=np.float32)
+    sb = None
+    if bias:
+        sb = (rng.integers(-1, 2, size=E) * 0.5).astype(np.float32)
+        sb[rng.random(E) < 0.2] = np.float32(-0.0)
+    res = gu.run_front(gu.shape_of(w), logits, sel_bias=sb)
+    ref = gu.run_oracle(w, logits, sel_bias=sb)
+    gu.check_route(res, ref)
+    gu.check_plan(res["plan_fields"], ref["plan"], w.P)
+    gu.check_align(res, ref, w.R, res["sizes"]["C"])
+    if w.N <= 32:
+        _front_matches_separate_calls(w, logits, sb)
 
 
 @pytest.mark.parametrize("planner", ["fixed", "quota"])

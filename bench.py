@@ -477,21 +477,32 @@ class StepRunner:
         rec(5)
 
     def timed(self, logits, steps, warmup):
-        """Warm up, then time ``steps`` steps: wall seconds, mean per-kernel
-        event times (us) and each step's device time (us)."""
+        """Warm up, then time ``steps`` steps with nothing but the steps on
+        the stream (wall seconds; the device time between one event before
+        and one after them is kept as ``timed_dev_us``, per step).  Then run
+        as many steps again, untimed, with an event between every two
+        kernels: mean per-kernel event times (us) and each of those steps'
+        device time (us)."""
         import numpy as np
-        torch = self.torch
+        torch, stream = self.torch, self.stream
         for _ in range(warmup):
             self.step(logits)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.names) + 1)]
-               for _ in range(steps)]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        a.record(stream)
+        for _ in range(steps):
+            self.step(logits)
+        b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        self.timed_dev_us = a.elapsed_time(b) * 1e3 / max(steps, 1)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.names) + 1)]
+               for _ in range(steps)]
         for i in range(steps):
             self.step(logits, evs[i])
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         per = {n: [] for n in self.names}
         for e in evs:
             for j, n in enumerate(self.names):
@@ -536,6 +547,7 @@ class StepRunner:
             "route_frac_peak": gb("route", avg_us["route"]) / HBM_PEAK_GBPS,
             "align_frac_peak": gb("align", avg_us["align"]) / HBM_PEAK_GBPS,
             "kernel_us": avg_us,
+            "step_device_us_timed": getattr(self, "timed_dev_us", None),
             "step_device_us_median": float(np.median(step_dev_us)),
             "step_device_us_min": float(np.min(step_dev_us)),
             "max_vio": float(hdr[1]) * w.E / w.P - 1.0,
@@ -770,6 +782,7 @@ def main():
                     for n in ("route", "align", "dispatch", "combine")},
         "plan_us": plan_alone_us,
         "plan_in_step_us": avg_us["plan"],
+        "step_device_us_timed": summ["step_device_us_timed"],
         "step_device_us_median": summ["step_device_us_median"],
         "step_device_us_min": summ["step_device_us_min"],
         "max_vio": summ["max_vio"],

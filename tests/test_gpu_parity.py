@@ -735,7 +735,11 @@ def test_corrupt_plan_is_flagged_not_followed(planner):
     ("decode1", {}), ("decode1", {"E": 384, "R": 8}), ("decode1", {"E": 512, "R": 16, "K": 16}),
     ("decode1", {"S": 4}), ("decode1", {"S": 3, "R": 4, "E": 40, "K": 6}),
     ("tiny", {"S": 8}), ("tiny", {"S": 5, "R": 2}),
-    ("decode16", {}), ("tiny", {}),              # past 32 tokens: the separate launches
+    # past 32 tokens: the separate launches
+    ("decode16", {}), ("tiny", {}), ("decode128", {}), ("decode16", {"S": 40}),
+    ("decode16", {"S": 33, "R": 4, "E": 40, "K": 6}), ("tiny", {"S": 300}),
+    ("tiny", {"S": 2100}), ("decode1", {"S": 100, "E": 512, "R": 16}),
+    ("decode1", {"S": 64, "E": 512, "R": 16, "K": 4}),
 ])
 @pytest.mark.parametrize("variant", ["plain", "bias_renorm"])
 def test_route_plan_matches_separate_calls(case, variant):

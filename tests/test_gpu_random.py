@@ -159,6 +159,46 @@ def test_small_batches(seed):
     _front_matches_separate_calls(w, logits)
 
 
+def medium_case(seed):
+    """33 to 1024 tokens (past the one-launch front) with at most 8192 pairs
+    and R * ceil(S / 32) * E <= 8192, blocks that are not all powers of
+    two."""
+    rng = np.random.default_rng(7000 + seed)
+    while True:
+        R = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        S = int(rng.integers(max(1, 33 // R + 1), 1024 // R + 1))
+        n_sub = R * -(-S // 32)
+        e_max = min(512, 8192 // n_sub) // R
+        if e_max < 1:
+            continue
+        E = R * int(rng.integers(1, e_max + 1))
+        K = int(rng.integers(1, min(E, 64, 8192 // (R * S)) + 1))
+        break
+    blk = int(rng.choice([12, 16, 64, 96, 128]))
+    B = int(rng.integers(0, 4))
+    score = "softmax" if rng.random() < 0.3 else "sigmoid"
+    logits = rng.standard_normal((R * S, E)).astype(np.float32)
+    w = WORKLOADS["tiny"].with_(E=E, K=K, R=R, S=S, H=64, B=B, blk=blk, score=score)
+    return w, logits
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_medium_batches(seed):
+    """Batches just past the one-launch front (lbt_front then makes the
+    separate launches): against the oracle, and lbt_front word for word
+    against the separate calls."""
+    w, logits = medium_case(seed)
+    assert 33 <= w.N <= 1024 and w.N * w.K <= 8192
+    print(f"[medium] seed {seed}: E={w.E} R={w.R} K={w.K} S={w.S} blk={w.blk} B={w.B}",
+          flush=True)
+    res = gu.run_front(gu.shape_of(w), logits)
+    ref = gu.run_oracle(w, logits)
+    gu.check_route(res, ref)
+    gu.check_plan(res["plan_fields"], ref["plan"], w.P)
+    gu.check_align(res, ref, w.R, res["sizes"]["C"])
+    _front_matches_separate_calls(w, logits)
+
+
 @pytest.mark.parametrize("E,K,S,score,bias", [
     (256, 8, 40, "sigmoid", False), (256, 8, 2, "sigmoid", True), (384, 8, 40, "sigmoid", True),
     (256, 24, 40, "softmax", False), (512, 64, 4, "sigmoid", True), (384, 16, 1, "softmax", False),

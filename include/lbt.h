@@ -201,7 +201,9 @@ int lbt_plan_balance(const lbt_shape* s, const int32_t* counts, int32_t* plan, i
  * output, on the GPU, with no host round trip).  Batches of at most 32
  * tokens (with R * ceil(S / 32) * E <= 16384) run as one workgroup that
  * keeps the load matrix in LDS and plans from it -- one launch where the
- * two calls make two; larger batches make the same launches as the two
+ * two calls make two.  Larger batches whose sub-tile histograms fit in
+ * 8192 words (R * ceil(S / 32) * E <= 8192) route, then run the column scan
+ * and the plan as one launch; others make the same launches as the two
  * calls.  Arguments as for the two calls; plan [plan_words] int32 out,
  * status int32 out (may be NULL). */
 int lbt_route_plan(const lbt_shape* s, const float* logits, const float* sel_bias, int32_t* ids,
@@ -214,8 +216,10 @@ int lbt_route_plan(const lbt_shape* s, const float* logits, const float* sel_bia
  * step's).  Batches of at most 32 tokens (with R * ceil(S / 32) * E <=
  * 16384 and R * C / blk <= 2048) run as one workgroup that keeps the
  * routing, the load matrix and the plan in LDS and places every pair from
- * them -- one launch where the three calls make three; other batches make
- * the same launches as the three calls.  [MoonEP-GR] section "Online planning, zero copy και στατικά
+ * them -- one launch where the three calls make three.  Batches past 32
+ * tokens with R * ceil(S / 32) * E <= 8192 make three launches (route;
+ * column scan and plan; align); others make the same launches as the three
+ * calls.  [MoonEP-GR] section "Online planning, zero copy και στατικά
  * σχήματα"; [AlignSort]; [UltraEP] section "その仕組みは...".  Arguments as
  * for the three calls. */
 int lbt_front(const lbt_shape* s, const float* logits, const float* sel_bias, int32_t* ids,

@@ -281,6 +281,11 @@ hipError_t launch_route_plan(const Dims& d, const float* logits, const float* bi
                              float* gates, int32_t* work, int32_t* counts, int32_t* plan,
                              int32_t* status, hipStream_t st) {
   if (!front_fits(d)) {
+    if (scan_plan_fits(d)) {   // mid-size batch: route, then column scan + plan in one launch
+      hipError_t e = launch_route(d, logits, bias, ids, gates, work, st);
+      if (e == hipSuccess) e = launch_scan_plan(d, work, counts, plan, status, st);
+      return e;
+    }
     hipError_t e = launch_route_and_scan(d, logits, bias, ids, gates, work, counts, st);
     if (e == hipSuccess) e = launch_plan(d, counts, plan, status, st);
     return e;
@@ -295,8 +300,14 @@ hipError_t launch_front(const Dims& d, const float* logits, const float* bias, i
                         int32_t* slot, int32_t* sorted_ids, int32_t* block_wrow,
                         int32_t* block_expert, int32_t* status, hipStream_t st) {
   if (!front_align_fits(d)) {
-    hipError_t e = launch_route_and_scan(d, logits, bias, ids, gates, work, counts, st);
-    if (e == hipSuccess) e = launch_plan(d, counts, plan, status, st);
+    hipError_t e;
+    if (!front_fits(d) && scan_plan_fits(d)) {   // mid-size batch: scan + plan in one launch
+      e = launch_route(d, logits, bias, ids, gates, work, st);
+      if (e == hipSuccess) e = launch_scan_plan(d, work, counts, plan, status, st);
+    } else {
+      e = launch_route_and_scan(d, logits, bias, ids, gates, work, counts, st);
+      if (e == hipSuccess) e = launch_plan(d, counts, plan, status, st);
+    }
     if (e == hipSuccess)
       e = launch_align(d, ids, work, plan, slot, sorted_ids, block_wrow, block_expert, status, st);
     return e;

@@ -58,6 +58,67 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict
   plan_core<false>(d, m, d.SK, counts, nullptr, plan, status);
 }
 
+// Column scan and fixed-rule plan in one launch, for batches whose sub-tile
+// histograms fit in LDS (n_sub * E <= kScanPlanWords; the route kernel has
+// written them).  The outputs of k_tile_scan (tile offsets, load matrix)
+// and of k_plan, bit for bit, one launch and one dependent global round
+// trip fewer.  All threads copy the histograms into LDS with their loads in
+// flight together; then one thread per expert walks its column in
+// sub-tile order (ranks ascending), writing the running prefix at each
+// tile's first sub-tile and each rank's sum, and leaves T_e for the plan.
+__global__ __launch_bounds__(kPlanThreads) void k_scan_plan(int32_t* __restrict__ work, Dims d,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ plan,
+                                                           int32_t* __restrict__ status) {
+  __shared__ PlanSmem m;
+  __shared__ int sSub[kScanPlanWords];   // [sub-tile][E]
+  const int E = d.E, spr = d.spr, tpr = d.tpr, tid = threadIdx.x;
+  const int n = d.n_sub * E;
+  if (tid < 12) m.sStat[tid] = 0;
+  constexpr int kPer = kScanPlanWords / kPlanThreads;
+  int v[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = u * kPlanThreads + tid;
+    v[u] = i < n ? work[i] : 0;
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = u * kPlanThreads + tid;
+    if (i < n) sSub[i] = v[u];
+  }
+  __syncthreads();
+  int32_t* base = work + work_tile_base(d);
+  for (int e = tid; e < E; e += kPlanThreads) {
+    int run = 0;
+    for (int r = 0; r < d.R; ++r) {
+      int sum = 0;
+      for (int j = 0; j < spr; ++j) {
+        const int c = sSub[(r * spr + j) * E + e];
+        if (j % kSubTiles == 0) base[(long long)(r * tpr + j / kSubTiles) * E + e] = run;
+        run += c;
+        sum += c;
+      }
+      counts[(long long)r * E + e] = sum;
+    }
+    m.sT[e] = run;
+    m.sX[e] = run;
+  }
+  __syncthreads();
+  plan_core<false>(d, m, d.SK, counts, nullptr, plan, status);
+}
+
+bool scan_plan_fits(const Dims& d) {
+  return d.n_sub >= 1 && (long long)d.n_sub * d.E <= kScanPlanWords;
+}
+
+hipError_t launch_scan_plan(const Dims& d, int32_t* work, int32_t* counts, int32_t* plan,
+                            int32_t* status, hipStream_t st) {
+  hipLaunchKernelGGL(k_scan_plan, dim3(1), dim3(kPlanThreads), 0, st, work, d, counts, plan,
+                     status);
+  return hipGetLastError();
+}
+
 // ---- quota plan ---------------------------------------------------------------
 //
 // [UltraEP] section "その仕組みは高速なエキスパート複製に依存する": the runtime

@@ -182,11 +182,12 @@ def medium_case(seed):
     return w, logits
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(40))
 def test_medium_batches(seed):
-    """Batches just past the one-launch front (lbt_front then makes the
-    separate launches): against the oracle, and lbt_front word for word
-    against the separate calls."""
+    """Batches just past the one-launch front, whose sub-tile histograms fit
+    the fused column scan + plan launch (lbt_front: route, scan + plan,
+    align): against the oracle, and lbt_front word for word against the
+    separate calls (route + column scan, plan, align)."""
     w, logits = medium_case(seed)
     assert 33 <= w.N <= 1024 and w.N * w.K <= 8192
     print(f"[medium] seed {seed}: E={w.E} R={w.R} K={w.K} S={w.S} blk={w.blk} B={w.B}",

@@ -1,7 +1,7 @@
 // Reference HBM streams for bench.py --ceilings: what plain reads, writes
 // and copies reach on this GPU, in the shapes measured fastest on MI355X
-// (one 16-byte access per thread: reads in 1024-thread workgroups with
-// non-temporal loads, writes and copies in 256-thread workgroups).  They
+// (one 16-byte access per thread: reads in 1024-thread workgroups, writes
+// and copies in 256-thread workgroups; reads non-temporal).  They
 // bound the row-movement kernels: dispatch and prefetch are copies with
 // fan-out, combine and reduce_grad mostly reads.  Measurement support for
 // the benchmark, not part of the path.
@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void k_write(u32x4* __restrict__ p, long long 
 __global__ __launch_bounds__(256) void k_copy(const u32x4* __restrict__ s, u32x4* __restrict__ d,
                                               long long n) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) d[i] = s[i];
+  if (i < n) d[i] = __builtin_nontemporal_load(s + i);
 }
 
 // kind 0: read `bytes` at a (b: 16-byte sink); 1: write `bytes` at a;

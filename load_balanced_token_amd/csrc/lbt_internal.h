@@ -62,12 +62,6 @@ hipError_t launch_route_and_scan(const Dims& d, const float* logits, const float
                                  hipStream_t st);
 hipError_t launch_plan(const Dims& d, const int32_t* counts, int32_t* plan, int32_t* status,
                        hipStream_t st);
-// column scan + fixed-rule plan in one launch, after launch_route, for
-// batches with n_sub * E <= kScanPlanWords (scan_plan_fits)
-constexpr int kScanPlanWords = 8192;
-bool scan_plan_fits(const Dims& d);
-hipError_t launch_scan_plan(const Dims& d, int32_t* work, int32_t* counts, int32_t* plan,
-                            int32_t* status, hipStream_t st);
 // route + histogram + fixed-rule plan (one launch for small batches)
 hipError_t launch_route_plan(const Dims& d, const float* logits, const float* bias, int32_t* ids,
                              float* gates, int32_t* work, int32_t* counts, int32_t* plan,

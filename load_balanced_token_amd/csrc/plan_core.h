@@ -29,6 +29,14 @@
 namespace lbt {
 
 constexpr int kPlanThreads = 1024;
+
+// Column scan + fixed-rule plan in one launch (plan.hip), after
+// launch_route, for batches with n_sub * E <= kScanPlanWords
+// (scan_plan_fits).
+constexpr int kScanPlanWords = 8192;
+bool scan_plan_fits(const Dims& d);
+hipError_t launch_scan_plan(const Dims& d, int32_t* work, int32_t* counts, int32_t* plan,
+                            int32_t* status, hipStream_t st);
 // The pieces per line position are counted one of three ways, by size:
 // with at most kDirectCompares (deficit rank, position) pairs per lane,
 // both ends of every position by register-broadcast counting; with at most

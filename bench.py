@@ -388,7 +388,7 @@ def training_report(lbt, torch, w, path, buf, dev, Hp, reps):
 
 def hbm_ceilings(torch, dev, nbytes, reps=10):
     """Reference HBM streams (bench_ceiling.so): a plain read, write and copy
-    of ``nbytes`` each, median of ``reps`` launches timed with HIP events on
+    of ``nbytes`` each, and the copy with non-temporal loads, median of ``reps`` launches timed with HIP events on
     the current stream; GB/s counts the bytes read plus the bytes written."""
     import ctypes
     import numpy as np
@@ -405,7 +405,8 @@ def hbm_ceilings(torch, dev, nbytes, reps=10):
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     out = {"bytes_per_launch": nbytes}
-    for name, kind, moved in (("read", 0, nbytes), ("write", 1, nbytes), ("copy", 2, 2 * nbytes)):
+    for name, kind, moved in (("read", 0, nbytes), ("write", 1, nbytes), ("copy", 2, 2 * nbytes),
+                              ("copy_nt", 3, 2 * nbytes)):
         bp = b.data_ptr() if kind != 1 else None
         for _ in range(3):
             assert L.hbm_stream(kind, ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(bp), nbytes, sp) == 0

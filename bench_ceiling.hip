@@ -1,7 +1,10 @@
 // Reference HBM streams for bench.py --ceilings: what plain reads, writes
 // and copies reach on this GPU, in the shapes measured fastest on MI355X
-// (one 16-byte access per thread: reads in 1024-thread workgroups, writes
-// and copies in 256-thread workgroups; reads non-temporal).  They
+// (one 16-byte access per thread: reads in 1024-thread workgroups with
+// non-temporal loads, writes and copies in 256-thread workgroups), plus
+// the copy with non-temporal loads, the fastest copy shape measured.  The
+// plain copy is also the known-size kernel the HBM traffic counters are
+// calibrated on.  They
 // bound the row-movement kernels: dispatch and prefetch are copies with
 // fan-out, combine and reduce_grad mostly reads.  Measurement support for
 // the benchmark, not part of the path.
@@ -27,11 +30,18 @@ __global__ __launch_bounds__(256) void k_write(u32x4* __restrict__ p, long long 
 __global__ __launch_bounds__(256) void k_copy(const u32x4* __restrict__ s, u32x4* __restrict__ d,
                                               long long n) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) d[i] = s[i];
+}
+
+__global__ __launch_bounds__(256) void k_copy_nt(const u32x4* __restrict__ s,
+                                                 u32x4* __restrict__ d, long long n) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i < n) d[i] = __builtin_nontemporal_load(s + i);
 }
 
 // kind 0: read `bytes` at a (b: 16-byte sink); 1: write `bytes` at a;
-// 2: copy `bytes` from a to b.  bytes a multiple of 16, pointers 16-byte
+// 2: copy `bytes` from a to b; 3: the same copy with non-temporal loads.
+// bytes a multiple of 16, pointers 16-byte
 // aligned.  0 on success, -1 for bad arguments, -2 for a failed launch.
 extern "C" int hbm_stream(int kind, void* a, void* b, long long bytes, void* stream) {
   if (a == nullptr || bytes <= 0 || bytes % 16 != 0 || (kind != 1 && b == nullptr)) return -1;
@@ -46,6 +56,9 @@ extern "C" int hbm_stream(int kind, void* a, void* b, long long bytes, void* str
                        static_cast<u32x4*>(a), n);
   } else if (kind == 2) {
     hipLaunchKernelGGL(k_copy, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       static_cast<const u32x4*>(a), static_cast<u32x4*>(b), n);
+  } else if (kind == 3) {
+    hipLaunchKernelGGL(k_copy_nt, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                        static_cast<const u32x4*>(a), static_cast<u32x4*>(b), n);
   } else {
     return -1;

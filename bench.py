@@ -158,7 +158,8 @@ def device_report(torch, dev_index=0):
 def decode_latency(path, buf, w, x, n_steps, dev, planner="fixed"):
     """p50/p99 latency of one step over ``n_steps`` fresh routings, for the
     whole step (route -> plan -> align -> dispatch -> combine; the first
-    three are one lbt_front call) and for the step without the combine.
+    four are one lbt_front_dispatch call) and for the step without the
+    combine.
 
     Every routing is resident in HBM before timing starts.  Step i is
     captured as its own HIP graph, bound to routing i where it lies, and the
@@ -184,14 +185,13 @@ def decode_latency(path, buf, w, x, n_steps, dev, planner="fixed"):
 
     def no_combine(i):
         if planner == "fixed":
-            path.front(all_logits[i], buf)
+            path.front_dispatch(all_logits[i], x, buf)
         else:
             path.route_topk(all_logits[i], buf["ids"], buf["gates"], buf["counts"], buf["work"])
             plan_fn(buf["counts"], buf["plan"], buf["status"])
-            path.align_sort(buf["ids"], buf["work"], buf["plan"], buf["slot"],
-                            buf["sorted_ids"], buf["block_wrow"], buf["block_expert"],
-                            buf["status"])
-        path.dispatch(x, buf["slot"], buf["recv"])
+            path.align_dispatch(buf["ids"], buf["work"], buf["plan"], x, buf["slot"],
+                                buf["sorted_ids"], buf["block_wrow"], buf["block_expert"],
+                                buf["recv"], buf["status"])
 
     def replay(body):
         with torch.cuda.stream(stream):        # warm up outside the graphs

@@ -307,6 +307,37 @@ int lbt_align_sort_noalloc(const lbt_shape* s, const int32_t* ids, const int32_t
 int lbt_dispatch(const lbt_shape* s, const uint16_t* x, const int32_t* slot, uint16_t* recv,
                  void* stream);
 
+/* lbt_align_sort followed by lbt_dispatch in one call: every output of the
+ * two (slot, sorted_ids, block tables, status, recv rows) bit for bit.
+ * [AlignSort] (a pair's target row is its expert-grouped, block-padded
+ * position); [MoonEP-GR] "Online planning, zero copy και στατικά σχήματα"
+ * (each row written once, straight into its final row).  Batches of 1 to
+ * 1024 tokens run as one launch: one workgroup per token places that
+ * token's K pairs, repeating its 128-token tile's prefix work, and copies
+ * the token's row to their rows; larger batches make the launches of the
+ * two calls.  Any plan (either planner, with or without the locality
+ * step).  Arguments as for the two calls; x [N, H] and recv [R*C, H] bf16
+ * bits, 16-byte aligned. */
+int lbt_align_dispatch(const lbt_shape* s, const int32_t* ids, const int32_t* work,
+                       const int32_t* plan, const uint16_t* x, int32_t* slot, int32_t* sorted_ids,
+                       int32_t* block_wrow, int32_t* block_expert, uint16_t* recv,
+                       int32_t* status, void* stream);
+
+/* lbt_front followed by lbt_dispatch in one call (the fixed-rule front of
+ * the step and the zero-copy dispatch): the outputs of the two, bit for
+ * bit.  Batches lbt_front runs as one workgroup make that launch and the
+ * dispatch; batches past 32 tokens with R * ceil(S / 32) * E <= 8192 make
+ * three launches (route; column scan and plan; align and dispatch); other
+ * batches make the launches of the separate calls, with align and dispatch
+ * as in lbt_align_dispatch.  [MoonEP-GR] "Online planning, zero copy και
+ * στατικά σχήματα"; [AlignSort]; [UltraEP] "その仕組みは...".  Arguments as
+ * for lbt_front and lbt_dispatch. */
+int lbt_front_dispatch(const lbt_shape* s, const float* logits, const float* sel_bias,
+                       int32_t* ids, float* gates, int32_t* counts, int32_t* work, int32_t* plan,
+                       int32_t* slot, int32_t* sorted_ids, int32_t* block_wrow,
+                       int32_t* block_expert, const uint16_t* x, uint16_t* recv,
+                       int32_t* status, void* stream);
+
 /* Combine, the inverse of dispatch: y[t] = sum_k gates[t,k] * out[slot[t*K+k]]
  * with fp32 accumulation in ascending k (fused multiply-add), from the
  * expert outputs laid out like recv ([MoonEP-GR]: combine returns expert

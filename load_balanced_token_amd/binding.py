@@ -45,8 +45,9 @@ HDR_FEASIBLE = 11
 HDR_LOCAL = 12
 
 EXPORTS = ("lbt_query_sizes", "lbt_route_topk", "lbt_histogram", "lbt_plan_balance",
-           "lbt_route_plan", "lbt_front",
-           "lbt_plan_quota", "lbt_align_sort", "lbt_align_sort_noalloc", "lbt_dispatch",
+           "lbt_route_plan", "lbt_front", "lbt_front_dispatch",
+           "lbt_plan_quota", "lbt_align_sort", "lbt_align_sort_noalloc", "lbt_align_dispatch",
+           "lbt_dispatch",
            "lbt_combine",
            "lbt_prefetch_weights", "lbt_reduce_grad", "lbt_combine_bwd", "lbt_dispatch_bwd",
            "lbt_strerror", "lbt_last_hip_error", "lbt_version")
@@ -103,6 +104,8 @@ def lib() -> ctypes.CDLL:
         L.lbt_plan_quota.argtypes = [SP, P, P, P, P]
         L.lbt_route_plan.argtypes = [SP, P, P, P, P, P, P, P, P, P]
         L.lbt_front.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        L.lbt_front_dispatch.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        L.lbt_align_dispatch.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P]
         L.lbt_align_sort.argtypes = [SP, P, P, P, P, P, P, P, P, P]
         L.lbt_align_sort_noalloc.argtypes = [SP, P, P, P, P, P, P, P, P]
         L.lbt_dispatch.argtypes = [SP, P, P, P, P]
@@ -332,6 +335,50 @@ class Path:
         _check(rc, "lbt_plan_quota")
 
     # a4
+    def front_dispatch(self, logits, x, buf, sel_bias=None, stream=None):
+        """lbt_front then lbt_dispatch in one call, into the buffers of
+        ``alloc()`` (those of front, and recv)."""
+        torch = _torch()
+        s, z = self.shape, self.sizes
+        rc = lib().lbt_front_dispatch(
+            ctypes.byref(self._c),
+            _ptr(logits, torch.float32, s.N * s.E, "logits"),
+            _ptr(sel_bias, torch.float32, s.E, "sel_bias"),
+            _ptr(buf["ids"], torch.int32, s.N * s.K, "ids"),
+            _ptr(buf["gates"], torch.float32, s.N * s.K, "gates"),
+            _ptr(buf["counts"], torch.int32, s.R * s.E, "counts"),
+            _ptr(buf["work"], torch.int32, z["work_words"], "work"),
+            _ptr(buf["plan"], torch.int32, z["plan_words"], "plan"),
+            _ptr(buf["slot"], torch.int32, z["P"], "slot"),
+            _ptr(buf["sorted_ids"], torch.int32, s.R * z["C"], "sorted_ids"),
+            _ptr(buf["block_wrow"], torch.int32, s.R * z["n_blocks"], "block_wrow"),
+            _ptr(buf["block_expert"], torch.int32, s.R * z["n_blocks"], "block_expert"),
+            _ptr(x, torch.int16, s.N * s.H, "x", align16=True),
+            _ptr(buf["recv"], torch.int16, s.R * z["C"] * s.H, "recv", align16=True),
+            _ptr(buf["status"], torch.int32, 1, "status"),
+            _stream(stream))
+        _check(rc, "lbt_front_dispatch")
+
+    # a4 + a5 in one call
+    def align_dispatch(self, ids, work, plan, x, slot, sorted_ids, block_wrow, block_expert,
+                       recv, status=None, stream=None):
+        torch = _torch()
+        s, z = self.shape, self.sizes
+        rc = lib().lbt_align_dispatch(
+            ctypes.byref(self._c),
+            _ptr(ids, torch.int32, s.N * s.K, "ids"),
+            _ptr(work, torch.int32, z["work_words"], "work"),
+            _ptr(plan, torch.int32, z["plan_words"], "plan"),
+            _ptr(x, torch.int16, s.N * s.H, "x", align16=True),
+            _ptr(slot, torch.int32, z["P"], "slot"),
+            _ptr(sorted_ids, torch.int32, s.R * z["C"], "sorted_ids"),
+            _ptr(block_wrow, torch.int32, s.R * z["n_blocks"], "block_wrow"),
+            _ptr(block_expert, torch.int32, s.R * z["n_blocks"], "block_expert"),
+            _ptr(recv, torch.int16, s.R * z["C"] * s.H, "recv", align16=True),
+            _ptr(status, torch.int32, 1, "status"),
+            _stream(stream))
+        _check(rc, "lbt_align_dispatch")
+
     def align_sort(self, ids, work, plan, slot, sorted_ids, block_wrow, block_expert,
                    status=None, stream=None):
         torch = _torch()
@@ -454,21 +501,21 @@ class Path:
 
     def step(self, logits, x, buf, sel_bias=None, out=None, stream=None, planner="fixed"):
         """One pass of the whole path; ``out`` defaults to recv (identity
-        expert); ``planner`` is "fixed" (route, plan and align in one
-        lbt_front call) or "quota" (lbt_route_topk, lbt_plan_quota,
-        lbt_align_sort).  Returns nothing; results land in ``buf``."""
+        expert); ``planner`` is "fixed" (route, plan, align and dispatch in
+        one lbt_front_dispatch call) or "quota" (lbt_route_topk,
+        lbt_plan_quota, lbt_align_dispatch); then lbt_combine.  Returns
+        nothing; results land in ``buf``."""
         if planner not in ("fixed", "quota"):
             raise LbtError(f"unknown planner {planner!r}")
         if planner == "fixed":
-            self.front(logits, buf, sel_bias=sel_bias, stream=stream)
+            self.front_dispatch(logits, x, buf, sel_bias=sel_bias, stream=stream)
         else:
             self.route_topk(logits, buf["ids"], buf["gates"], buf["counts"], buf["work"],
                             sel_bias=sel_bias, stream=stream)
             self.plan_quota(buf["counts"], buf["plan"], buf["status"], stream=stream)
-            self.align_sort(buf["ids"], buf["work"], buf["plan"], buf["slot"],
-                            buf["sorted_ids"], buf["block_wrow"], buf["block_expert"],
-                            buf["status"], stream=stream)
-        self.dispatch(x, buf["slot"], buf["recv"], stream=stream)
+            self.align_dispatch(buf["ids"], buf["work"], buf["plan"], x, buf["slot"],
+                                buf["sorted_ids"], buf["block_wrow"], buf["block_expert"],
+                                buf["recv"], buf["status"], stream=stream)
         self.combine(buf["recv"] if out is None else out, buf["slot"], buf["gates"], buf["y"],
                      stream=stream)
 

@@ -20,6 +20,8 @@
 // token.  A token holds K distinct experts, so ranks by token order equal
 // ranks by flat index f = t*K + k.
 #include "align_core.h"
+#include "fused.h"
+#include "rows.h"
 
 namespace lbt {
 
@@ -35,12 +37,20 @@ constexpr int kBlockWaves = kAlignThreads / kWave;   // blocks handled per workg
 // workgroups each).
 constexpr int kAlignTilesOneRound = 1024;
 
-template <int NT>
+// MOVE: the dispatch fused in (batches of at most kMoveTokens tokens).  Each
+// tile has D = min(128, S) workgroups, workgroup g of a tile handling the
+// tile's token g: it builds the tile's masks and plan arrays like a tile
+// workgroup, places only its token's K pairs (so every pair is still placed
+// once), then copies the token's row x[t] to each of their rows of recv.
+// The outputs are lbt_align_sort's and lbt_dispatch's, one launch and one
+// dependent round trip (slot written, then read back) fewer.
+template <int NT, bool MOVE>
 __global__ __launch_bounds__(NT) void k_align(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ work,
     const int32_t* __restrict__ plan, Dims d, int32_t* __restrict__ slot,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_wrow,
-    int32_t* __restrict__ block_expert, int32_t* __restrict__ status) {
+    int32_t* __restrict__ block_expert, int32_t* __restrict__ status,
+    const u32x4* __restrict__ x, u32x4* __restrict__ recv) {
   // Block-table workgroups and tile workgroups share the grid.  When the
   // tiles fit the chip in one round they go first and the short block-table
   // workgroups finish under them (DSV3: 256 tiles; dispatching the 510
@@ -50,10 +60,12 @@ __global__ __launch_bounds__(NT) void k_align(
   // tiles; placed after them they ended ~3 us past the last tile).
   const long long nblk = (long long)d.R * d.n_blocks;
   const int nbw = (int)((nblk + NT / kWave - 1) / (NT / kWave));
-  const bool blocks_first = d.n_tiles > kAlignTilesOneRound;
+  const int D = MOVE ? min(kTileTokens, d.S) : 1;   // workgroups per tile
+  const int ntw = d.n_tiles * D;                    // tile workgroups
+  const bool blocks_first = ntw > kAlignTilesOneRound;
   const int bid = (int)blockIdx.x;
-  if (blocks_first ? bid < nbw : bid >= d.n_tiles) {
-    const long long gb = (long long)(blocks_first ? bid : bid - d.n_tiles) * (NT / kWave) + wave_id();
+  if (blocks_first ? bid < nbw : bid >= ntw) {
+    const long long gb = (long long)(blocks_first ? bid : bid - ntw) * (NT / kWave) + wave_id();
     if (gb < nblk) align_blocks(plan, d, gb, sorted_ids, block_wrow, block_expert);
     return;
   }
@@ -90,10 +102,13 @@ __global__ __launch_bounds__(NT) void k_align(
 
   const PlanLayout& pl = d.pl;
   const int E = d.E, K = d.K, C = d.C, nh = d.nh;
-  const int tile = blocks_first ? bid - nbw : bid;
+  const int tw = blocks_first ? bid - nbw : bid;
+  const int tile = MOVE ? tw / D : tw;
+  const int tg = MOVE ? tw - tile * D : 0;          // MOVE: the workgroup's token in the tile
   const int r = tile / d.tpr, j = tile - r * d.tpr;
   const int t0 = r * d.S + j * kTileTokens;
   const int len = min(kTileTokens, d.S - j * kTileTokens);
+  if (MOVE && tg >= len) return;                    // past a short tile (before any barrier)
   const int nP = min(plan[pl.hdr + LBT_HDR_N_PIECES], pl.max_pieces);
   const int totOv = plan[pl.hdr + LBT_HDR_TOTAL_OVERFLOW];
   const bool local = plan[pl.hdr + LBT_HDR_LOCAL] != 0;
@@ -112,6 +127,22 @@ __global__ __launch_bounds__(NT) void k_align(
   for (int u = 0; u < kPre; ++u) {
     const int p = tid + u * NT;
     idp[u] = p < np ? ids[f0 + p] : -1;
+  }
+  // MOVE: the token's own ids (thread k < K holds pair k) and the first
+  // chunks of its row, loaded now so that their latency overlaps the
+  // tile's prefix work
+  constexpr int kXPre = MOVE ? 2 : 1;
+  const int H8 = d.H / 8;
+  const u32x4* src = MOVE ? x + (long long)(t0 + tg) * H8 : nullptr;
+  int own_id = -1;
+  u32x4 xv[kXPre];
+  if constexpr (MOVE) {
+    if (tid < K) own_id = ids[f0 + tg * K + tid];
+#pragma unroll
+    for (int i = 0; i < kXPre; ++i) {
+      const int c = tid + i * NT;
+      xv[i] = c < H8 ? src[c] : u32x4{0u, 0u, 0u, 0u};
+    }
   }
 
   for (int e = tid; e < E; e += NT) {
@@ -195,12 +226,13 @@ __global__ __launch_bounds__(NT) void k_align(
     }
   __syncthreads();
 
-  auto place = [&](int p, int e) {
+  // the pair's row of recv (also written to slot and sorted_ids), or -1
+  auto place = [&](int p, int e) -> long long {
     const long long f = f0 + p;
     if (e < 0 || e >= E) {
       flags |= LBT_ST_BADID;
       slot[f] = -1;
-      return;
+      return -1;
     }
     const int ti = token_of(p);
     const int sub = ti / kSubTokens;
@@ -256,19 +288,44 @@ __global__ __launch_bounds__(NT) void k_align(
     if (!ok || row >= C || row < 0 || dd < 0 || dd >= d.R) {
       flags |= LBT_ST_CAPACITY;
       slot[f] = -1;
-      return;
+      return -1;
     }
     const long long dst = (long long)dd * C + row;
     slot[f] = (int)dst;
     sorted_ids[dst] = (int)f;
+    return dst;
   };
+  if constexpr (MOVE) {
+    // the token's K pairs, one per thread, then its row to each of them
+    __shared__ long long sDst[kMaxK];
+    if (tid < K) sDst[tid] = place(tg * K + tid, own_id);
+    if (flags && status != nullptr) atomicOr(status, flags);
+    __syncthreads();
 #pragma unroll
-  for (int u = 0; u < kPre; ++u) {
-    const int p = tid + u * NT;
-    if (p < np) place(p, idp[u]);
+    for (int i = 0; i < kXPre; ++i) {
+      const int c = tid + i * NT;
+      if (c < H8)
+        for (int k = 0; k < K; ++k) {
+          const long long dst = sDst[k];
+          if (dst >= 0) recv[dst * H8 + c] = xv[i];
+        }
+    }
+    for (int c = tid + kXPre * NT; c < H8; c += NT) {
+      const u32x4 v = src[c];
+      for (int k = 0; k < K; ++k) {
+        const long long dst = sDst[k];
+        if (dst >= 0) recv[dst * H8 + c] = v;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int p = tid + u * NT;
+      if (p < np) place(p, idp[u]);
+    }
+    for (int p = tid + kPre * NT; p < np; p += NT) place(p, ids[f0 + p]);
+    if (flags && status != nullptr) atomicOr(status, flags);
   }
-  for (int p = tid + kPre * NT; p < np; p += NT) place(p, ids[f0 + p]);
-  if (flags && status != nullptr) atomicOr(status, flags);
 }
 
 // LDS of a tile workgroup: 10 per-expert arrays, the [kSubTiles][E]
@@ -284,9 +341,35 @@ hipError_t launch_align(const Dims& d, const int32_t* ids, const int32_t* work, 
   const long long nblk = (long long)d.R * d.n_blocks;
   const long long grid = d.n_tiles + (nblk + kBlockWaves - 1) / kBlockWaves;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_align<kAlignThreads>, dim3((unsigned)grid), dim3(kAlignThreads),
+  hipLaunchKernelGGL((k_align<kAlignThreads, false>), dim3((unsigned)grid), dim3(kAlignThreads),
                      align_lds_bytes(d), st, ids, work, plan, d, slot, sorted_ids, block_wrow,
-                     block_expert, status);
+                     block_expert, status, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+// Batches the fused align + dispatch launch takes: one workgroup per token
+// (with the tile's placement work repeated in each) pays off while the
+// tokens are few; larger batches make the two launches.
+constexpr int kMoveTokens = 1024;
+
+hipError_t launch_align_dispatch(const Dims& d, const int32_t* ids, const int32_t* work,
+                                 const int32_t* plan, const uint16_t* x, int32_t* slot,
+                                 int32_t* sorted_ids, int32_t* block_wrow, int32_t* block_expert,
+                                 uint16_t* recv, int32_t* status, hipStream_t st) {
+  if (d.N < 1 || d.N > kMoveTokens) {
+    hipError_t e = launch_align(d, ids, work, plan, slot, sorted_ids, block_wrow, block_expert,
+                                status, st);
+    if (e == hipSuccess) e = launch_dispatch(d, x, slot, recv, st);
+    return e;
+  }
+  const long long nblk = (long long)d.R * d.n_blocks;
+  const long long grid = (long long)d.n_tiles * (d.S < kTileTokens ? d.S : kTileTokens) +
+                         (nblk + kBlockWaves - 1) / kBlockWaves;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_align<kAlignThreads, true>), dim3((unsigned)grid), dim3(kAlignThreads),
+                     align_lds_bytes(d), st, ids, work, plan, d, slot, sorted_ids, block_wrow,
+                     block_expert, status, reinterpret_cast<const u32x4*>(x),
+                     reinterpret_cast<u32x4*>(recv));
   return hipGetLastError();
 }
 

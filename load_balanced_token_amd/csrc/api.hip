@@ -3,6 +3,7 @@
 // or synchronises with the device.
 #include <string.h>
 
+#include "fused.h"
 #include "lbt_internal.h"
 
 namespace lbt {
@@ -224,6 +225,37 @@ int lbt_align_sort(const lbt_shape* s, const int32_t* ids, const int32_t* work, 
   if (d.N > 0 && (!ids || !work || !slot)) return LBT_EINVAL;
   return hip_rc(launch_align(d, ids, work, plan, slot, sorted_ids, block_wrow, block_expert, status,
                              begin_launches(stream)));
+}
+
+int lbt_align_dispatch(const lbt_shape* s, const int32_t* ids, const int32_t* work,
+                       const int32_t* plan, const uint16_t* x, int32_t* slot, int32_t* sorted_ids,
+                       int32_t* block_wrow, int32_t* block_expert, uint16_t* recv,
+                       int32_t* status, void* stream) {
+  Dims d;
+  const int rc = make_dims(s, &d, nullptr);
+  if (rc) return rc;
+  if (!plan || !sorted_ids || !block_wrow || !block_expert) return LBT_EINVAL;
+  if (d.N > 0 && (!ids || !work || !slot || !x || !recv || !aligned16(x) || !aligned16(recv)))
+    return LBT_EINVAL;
+  return hip_rc(launch_align_dispatch(d, ids, work, plan, x, slot, sorted_ids, block_wrow,
+                                      block_expert, recv, status, begin_launches(stream)));
+}
+
+int lbt_front_dispatch(const lbt_shape* s, const float* logits, const float* sel_bias,
+                       int32_t* ids, float* gates, int32_t* counts, int32_t* work, int32_t* plan,
+                       int32_t* slot, int32_t* sorted_ids, int32_t* block_wrow,
+                       int32_t* block_expert, const uint16_t* x, uint16_t* recv,
+                       int32_t* status, void* stream) {
+  Dims d;
+  const int rc = make_dims(s, &d, nullptr);
+  if (rc) return rc;
+  if (counts == nullptr || plan == nullptr || !sorted_ids || !block_wrow || !block_expert ||
+      (d.N > 0 && (!logits || !ids || !gates || !work || !slot || !x || !recv ||
+                   !aligned16(x) || !aligned16(recv))))
+    return LBT_EINVAL;
+  return hip_rc(launch_front_dispatch(d, logits, sel_bias, ids, gates, work, counts, plan, slot,
+                                      sorted_ids, block_wrow, block_expert, x, recv, status,
+                                      begin_launches(stream)));
 }
 
 int lbt_align_sort_noalloc(const lbt_shape* s, const int32_t* ids, const int32_t* plan,

@@ -19,6 +19,7 @@
 // sorted by expert, each expert's share padded to the grouped GEMM's block).
 #include <limits.h>
 
+#include "fused.h"
 #include "plan_core.h"
 #include "route_core.h"
 
@@ -315,6 +316,38 @@ hipError_t launch_front(const Dims& d, const float* logits, const float* bias, i
   launch_front_small<true>(d, logits, bias, ids, gates, work, counts, plan, slot, sorted_ids,
                            block_wrow, block_expert, status, st);
   return hipGetLastError();
+}
+
+// The front and the dispatch: batches the one-workgroup front takes run it,
+// then the dispatch; batches past 32 tokens whose sub-tile histograms fit
+// 8192 words route, then scan and plan in one launch, then align and
+// dispatch in one launch (three launches where lbt_front and lbt_dispatch
+// make five); others make the launches of the separate calls, with align
+// and dispatch fused up to 1024 tokens.
+hipError_t launch_front_dispatch(const Dims& d, const float* logits, const float* bias,
+                                 int32_t* ids, float* gates, int32_t* work, int32_t* counts,
+                                 int32_t* plan, int32_t* slot, int32_t* sorted_ids,
+                                 int32_t* block_wrow, int32_t* block_expert, const uint16_t* x,
+                                 uint16_t* recv, int32_t* status, hipStream_t st) {
+  if (front_align_fits(d)) {
+    launch_front_small<true>(d, logits, bias, ids, gates, work, counts, plan, slot, sorted_ids,
+                             block_wrow, block_expert, status, st);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = launch_dispatch(d, x, slot, recv, st);
+    return e;
+  }
+  hipError_t e;
+  if (!front_fits(d) && scan_plan_fits(d)) {
+    e = launch_route(d, logits, bias, ids, gates, work, st);
+    if (e == hipSuccess) e = launch_scan_plan(d, work, counts, plan, status, st);
+  } else {
+    e = launch_route_and_scan(d, logits, bias, ids, gates, work, counts, st);
+    if (e == hipSuccess) e = launch_plan(d, counts, plan, status, st);
+  }
+  if (e == hipSuccess)
+    e = launch_align_dispatch(d, ids, work, plan, x, slot, sorted_ids, block_wrow, block_expert,
+                              recv, status, st);
+  return e;
 }
 
 }  // namespace lbt

@@ -325,8 +325,10 @@ int lbt_align_dispatch(const lbt_shape* s, const int32_t* ids, const int32_t* wo
 
 /* lbt_front followed by lbt_dispatch in one call (the fixed-rule front of
  * the step and the zero-copy dispatch): the outputs of the two, bit for
- * bit.  Batches lbt_front runs as one workgroup make that launch and the
- * dispatch; batches past 32 tokens with R * ceil(S / 32) * E <= 8192 make
+ * bit.  Batches of at most 16 tokens that lbt_front runs as one workgroup
+ * make one launch (one workgroup per token, each computing the whole front;
+ * the first writes its outputs, each copies its token's row); up to 32
+ * tokens, the front's launch and the dispatch; batches past 32 tokens with R * ceil(S / 32) * E <= 8192 make
  * three launches (route; column scan and plan; align and dispatch); other
  * batches make the launches of the separate calls, with align and dispatch
  * as in lbt_align_dispatch.  [MoonEP-GR] "Online planning, zero copy και

@@ -22,6 +22,7 @@
 #include "fused.h"
 #include "plan_core.h"
 #include "route_core.h"
+#include "rows.h"
 
 namespace lbt {
 
@@ -47,14 +48,17 @@ static bool front_align_fits(const Dims& d) {
 // same rule and row arithmetic as k_align -- and each block-table entry the
 // segment covering the block's first row, whose real end goes to blk_end
 // for the padding pass.  Returns the LBT_ST_* bits it raises (only
-// LBT_ST_CAPACITY can arise: the route's ids are valid and distinct).
+// LBT_ST_CAPACITY can arise: the route's ids are valid and distinct).  With
+// store false nothing goes to global memory; sDst (if not null) receives
+// every pair's row of recv, or -1.
 __device__ __forceinline__ int front_place(const Dims& d, const PlanSmem& m, const uint32_t* tmask,
                                            const RouteScratch& rs, int* blk_end,
                                            int32_t* __restrict__ slot,
                                            int32_t* __restrict__ sorted_ids,
                                            int32_t* __restrict__ block_wrow,
                                            int32_t* __restrict__ block_expert, const int wt,
-                                           const int nthr) {
+                                           const int nthr, const bool store = true,
+                                           int* sDst = nullptr) {
   const int E = d.E, K = d.K, R = d.R, nh = d.nh, C = d.C, blk = d.blk, B = d.B;
   const int nP = m.sStat[5], totOv = m.sStat[6];
   int flags = 0;
@@ -80,13 +84,18 @@ __device__ __forceinline__ int front_place(const Dims& d, const PlanSmem& m, con
     }
     if (!ok || row >= C || row < 0 || dd < 0 || dd >= R) {
       flags |= LBT_ST_CAPACITY;
-      slot[f] = -1;
+      if (store) slot[f] = -1;
+      if (sDst != nullptr) sDst[f] = -1;
       continue;
     }
     const long long dst = (long long)dd * C + row;
-    slot[f] = (int)dst;
-    sorted_ids[dst] = f;
+    if (store) {
+      slot[f] = (int)dst;
+      sorted_ids[dst] = f;
+    }
+    if (sDst != nullptr) sDst[f] = (int)dst;
   }
+  if (!store) return flags;
   // block tables: one block per thread, its segment's real end kept in LDS
   const long long nblk = (long long)R * d.n_blocks;
   // (blocks from the group's last thread down, pairs from its first up: a
@@ -164,13 +173,22 @@ __device__ __forceinline__ void front_sentinels(const Dims& d, const int* blk_en
   }
 }
 
-template <int V, bool FULL, bool ALIGN>
+// MOVE (ALIGN, at most kFrontWaveTokens tokens): the dispatch fused in.
+// The grid has one workgroup per token; every workgroup routes, plans and
+// places the whole batch (the same integer plan and placement in each), the
+// first one alone writes the outputs, and workgroup t then copies token t's
+// row x[t] to its K rows of recv.  One launch for the front and the
+// dispatch, whose outputs it gives bit for bit.
+template <int V, bool FULL, bool ALIGN, bool MOVE>
 __global__ __launch_bounds__(kPlanThreads) void k_route_plan(
     const float* __restrict__ logits, const float* __restrict__ bias, Dims d, int vec,
     int32_t* __restrict__ ids, float* __restrict__ gates, int32_t* __restrict__ work,
     int32_t* __restrict__ counts, int32_t* __restrict__ plan, int32_t* __restrict__ slot,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_wrow,
-    int32_t* __restrict__ block_expert, int32_t* __restrict__ status) {
+    int32_t* __restrict__ block_expert, int32_t* __restrict__ status,
+    const u32x4* __restrict__ x, u32x4* __restrict__ recv) {
+  static_assert(!MOVE || ALIGN, "the fused dispatch needs the placement");
+  const bool lead = !MOVE || blockIdx.x == 0;     // the workgroup that writes the outputs
   __shared__ RouteScratch rs;
   __shared__ int hist[kFrontHist];     // [sub-tile][E]
   __shared__ uint32_t tmask[kMaxE];    // per expert: the tokens holding it (ALIGN)
@@ -191,7 +209,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_route_plan(
   // up to 16 tokens: one per wave (a lane sorts a quarter of the keys);
   // else four per wave on the route's eight waves
   if (d.N <= kFrontWaveTokens)
-    route_wave<V, FULL>(logits, bias, d, vec, d.N, ids, gates, rs, add);
+    route_wave<V, FULL>(logits, bias, d, vec, d.N, ids, gates, rs, add, lead);
   else
     route_span<V, FULL>(logits, bias, d, vec, 0, d.N, ids, gates, rs, add);
   __syncthreads();
@@ -207,7 +225,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_route_plan(
   // the tile offsets align reads and the load matrix, written by waves
   // 1.. while wave 0 builds the plan (their stores are off the plan's
   // critical path; decode S=1: 1.0 us of the kernel before)
-  if ((int)threadIdx.x >= kWave) {
+  if (lead && (int)threadIdx.x >= kWave) {
     int32_t* base = work + work_tile_base(d);
     for (int e = threadIdx.x - kWave; e < E; e += kPlanThreads - kWave) {
       int run = 0;
@@ -232,41 +250,62 @@ __global__ __launch_bounds__(kPlanThreads) void k_route_plan(
     // and writes the block tables; then everyone writes the padding
     // sentinels.  The status word is written once, after the align step.
     plan_build<false>(d, m, d.SK);
+    // MOVE: every pair's row lands in LDS; the histograms are dead after
+    // plan_build's closing barrier, so their space holds it
+    int* sDst = MOVE ? hist : nullptr;
     constexpr int kHalf = kPlanThreads / 2;
     if ((int)threadIdx.x >= kHalf) {
-      plan_write<false>(d, m, counts, nullptr, plan, nullptr, (int)threadIdx.x - kHalf, kHalf);
+      if (lead)
+        plan_write<false>(d, m, counts, nullptr, plan, nullptr, (int)threadIdx.x - kHalf, kHalf);
     } else {
       const int fl = front_place(d, m, tmask, rs, blk_end, slot, sorted_ids, block_wrow,
-                                 block_expert, (int)threadIdx.x, kHalf);
+                                 block_expert, (int)threadIdx.x, kHalf, lead, sDst);
       if (fl) atomicOr(&sFlags, fl);
     }
     __syncthreads();
-    front_sentinels(d, blk_end, sorted_ids);
-    if (threadIdx.x == 0 && status != nullptr) *status = m.sStat[4] | sFlags;
+    if (lead) {
+      front_sentinels(d, blk_end, sorted_ids);
+      if (threadIdx.x == 0 && status != nullptr) *status = m.sStat[4] | sFlags;
+    }
+    if constexpr (MOVE) {
+      const int t = blockIdx.x, K = d.K, H8 = d.H / 8;
+      const u32x4* src = x + (long long)t * H8;
+      for (int c = threadIdx.x; c < H8; c += kPlanThreads) {
+        const u32x4 v = src[c];
+        for (int k = 0; k < K; ++k) {
+          const int dst = sDst[t * K + k];
+          if (dst >= 0) recv[(long long)dst * H8 + c] = v;
+        }
+      }
+    }
   }
 }
 
 // One small-batch launch: route + plan (ALIGN false) or route + plan +
-// align (ALIGN true).
-template <bool ALIGN>
+// align (ALIGN true), and with MOVE the dispatch too (one workgroup per
+// token, x and recv given).
+template <bool ALIGN, bool MOVE = false>
 static void launch_front_small(const Dims& d, const float* logits, const float* bias,
                                int32_t* ids, float* gates, int32_t* work, int32_t* counts,
                                int32_t* plan, int32_t* slot, int32_t* sorted_ids,
                                int32_t* block_wrow, int32_t* block_expert, int32_t* status,
-                               hipStream_t st) {
+                               hipStream_t st, const uint16_t* x = nullptr,
+                               uint16_t* recv = nullptr) {
   const int vec = route_vec(logits, d.E);
-  const dim3 grid(1), block(kPlanThreads);
+  const dim3 grid(MOVE ? d.N : 1), block(kPlanThreads);
   const int V = (d.E + kRowLanes - 1) / kRowLanes;
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  u32x4* rv = reinterpret_cast<u32x4*>(recv);
 #define LBT_FRONT(VV)                                                                      \
   do {                                                                                     \
     if (d.E == kRowLanes * (VV))                                                           \
-      hipLaunchKernelGGL((k_route_plan<VV, true, ALIGN>), grid, block, 0, st, logits,      \
-                         bias, d, vec, ids, gates, work, counts, plan, slot, sorted_ids,   \
-                         block_wrow, block_expert, status);                                \
+      hipLaunchKernelGGL((k_route_plan<VV, true, ALIGN, MOVE>), grid, block, 0, st,        \
+                         logits, bias, d, vec, ids, gates, work, counts, plan, slot,       \
+                         sorted_ids, block_wrow, block_expert, status, xv, rv);            \
     else                                                                                   \
-      hipLaunchKernelGGL((k_route_plan<VV, false, ALIGN>), grid, block, 0, st, logits,     \
-                         bias, d, vec, ids, gates, work, counts, plan, slot, sorted_ids,   \
-                         block_wrow, block_expert, status);                                \
+      hipLaunchKernelGGL((k_route_plan<VV, false, ALIGN, MOVE>), grid, block, 0, st,       \
+                         logits, bias, d, vec, ids, gates, work, counts, plan, slot,       \
+                         sorted_ids, block_wrow, block_expert, status, xv, rv);            \
   } while (0)
   if (V <= 1) LBT_FRONT(1);
   else if (V <= 2) LBT_FRONT(2);
@@ -318,8 +357,10 @@ hipError_t launch_front(const Dims& d, const float* logits, const float* bias, i
   return hipGetLastError();
 }
 
-// The front and the dispatch: batches the one-workgroup front takes run it,
-// then the dispatch; batches past 32 tokens whose sub-tile histograms fit
+// The front and the dispatch: batches of at most 16 tokens the
+// one-workgroup front takes run it with the dispatch fused in (one launch,
+// one workgroup per token); up to 32 tokens the front, then the dispatch;
+// batches past 32 tokens whose sub-tile histograms fit
 // 8192 words route, then scan and plan in one launch, then align and
 // dispatch in one launch (three launches where lbt_front and lbt_dispatch
 // make five); others make the launches of the separate calls, with align
@@ -329,6 +370,11 @@ hipError_t launch_front_dispatch(const Dims& d, const float* logits, const float
                                  int32_t* plan, int32_t* slot, int32_t* sorted_ids,
                                  int32_t* block_wrow, int32_t* block_expert, const uint16_t* x,
                                  uint16_t* recv, int32_t* status, hipStream_t st) {
+  if (front_align_fits(d) && d.N <= kFrontWaveTokens) {
+    launch_front_small<true, true>(d, logits, bias, ids, gates, work, counts, plan, slot,
+                                   sorted_ids, block_wrow, block_expert, status, st, x, recv);
+    return hipGetLastError();
+  }
   if (front_align_fits(d)) {
     launch_front_small<true>(d, logits, bias, ids, gates, work, counts, plan, slot, sorted_ids,
                              block_wrow, block_expert, status, st);

@@ -415,13 +415,14 @@ __device__ __forceinline__ void route_span(const float* __restrict__ logits,
 // The gates are computed by lanes 0..15 exactly as route_span's row lanes
 // compute them (same 16-lane layout of the row for the softmax, same
 // assignment of k to lanes, same order of additions), so ids and gates are
-// bit for bit route_span's.
+// bit for bit route_span's.  With store false the ids and gates are not
+// written (the winners still reach sm.s_id and hist_add).
 template <int V, bool FULL, typename HistAdd>
 __device__ __forceinline__ void route_wave(const float* __restrict__ logits,
                                            const float* __restrict__ bias, const Dims& d, int vec,
                                            int N, int32_t* __restrict__ ids,
                                            float* __restrict__ gates, RouteScratch& sm,
-                                           HistAdd hist_add) {
+                                           HistAdd hist_add, const bool store = true) {
   constexpr int W = (V + 3) / 4;
   constexpr bool FULLW = FULL && V % 4 == 0;   // E = 16 V = 64 W
   const int E = d.E, K = d.K;
@@ -515,8 +516,10 @@ __device__ __forceinline__ void route_wave(const float* __restrict__ logits,
     if (d.renorm) g = g / row_sum_f64(g);
     if (rl < K) {
       const int id = s_id[rl];
-      ids[(long long)t * K + rl] = id;
-      gates[(long long)t * K + rl] = (float)g;
+      if (store) {
+        ids[(long long)t * K + rl] = id;
+        gates[(long long)t * K + rl] = (float)g;
+      }
       hist_add((long long)t, id);
     }
     return;
@@ -531,8 +534,10 @@ __device__ __forceinline__ void route_wave(const float* __restrict__ logits,
     const int id = s_id[kk];
     double g = score(logit_of(kk));
     if (d.renorm) g = g / gsum;
-    ids[(long long)t * K + kk] = id;
-    gates[(long long)t * K + kk] = (float)g;
+    if (store) {
+      ids[(long long)t * K + kk] = id;
+      gates[(long long)t * K + kk] = (float)g;
+    }
     hist_add((long long)t, id);
   }
 }

@@ -2,7 +2,9 @@
 lbt_align_dispatch against lbt_align_sort + lbt_dispatch (both planners,
 the quota plan's locality step, ragged tiles, dropped pairs, batches past
 the one-launch limit) and lbt_front_dispatch against lbt_front +
-lbt_dispatch; the align outputs also against the oracle."""
+lbt_dispatch (the one-launch front and dispatch up to 16 tokens, the front
+then the dispatch up to 32, the fused scan + plan and align + dispatch
+past that); the align outputs also against the oracle."""
 import numpy as np
 import pytest
 
@@ -106,7 +108,11 @@ def test_align_dispatch_dropped_pairs():
 
 
 @pytest.mark.parametrize("case", [
-    ("decode1", {}), ("decode16", {}), ("decode128", {}), ("tiny", {}),
+    ("decode1", {}), ("decode1", {"S": 2}), ("decode1", {"E": 384}),
+    ("decode1", {"S": 1, "R": 4, "E": 40, "K": 6, "H": 136}),
+    ("decode1", {"S": 1, "R": 16, "E": 512, "K": 16, "H": 512}),
+    ("tiny", {"S": 4}), ("tiny", {"S": 5, "R": 2}), ("tiny", {"S": 8}),
+    ("decode16", {}), ("decode128", {}), ("tiny", {}),
     ("decode16", {"S": 40}), ("decode16", {"S": 33, "R": 4, "E": 40, "K": 6, "H": 136}),
     ("decode1", {"S": 100, "E": 512, "R": 16, "H": 512}),
     ("dsv3", {"S": 64}), ("dsv3", {"S": 160, "H": 512}),
@@ -133,3 +139,30 @@ def test_front_dispatch_matches_separate_calls(case):
     out = {k: gu.d2h(b[k]) for k in ("slot", "sorted_ids", "block_wrow", "block_expert",
                                       "status")}
     gu.check_align(out, ref, w.R, path.sizes["C"])
+
+
+def test_front_dispatch_dropped_pairs():
+    """The one-launch front + dispatch with a capacity below the plan's
+    need: the same slots (-1 where a pair does not fit) and rows as lbt_front
+    + lbt_dispatch."""
+    import load_balanced_token_amd as lbt
+    t = gu.torch()
+    w = WORKLOADS["decode1"].with_(H=512)
+    logits = router_logits(w, 0)
+    ref = gu.run_oracle(w, logits)
+    need = int(ref["plan"]["n_rows_padded"].max())
+    cap = max(w.blk, (need // w.blk - 1) * w.blk)
+    print(f"[fused] front_dispatch dropped pairs cap={cap}", flush=True)
+    path = lbt.Path(gu.shape_of(w, cap=cap))
+    a, b = _fresh(path, t), _fresh(path, t)
+    lg = gu.h2d(logits)
+    x = gu.h2d(activations(w, 0))
+    path.front(lg, a)
+    path.dispatch(x, a["slot"], a["recv"])
+    path.front_dispatch(lg, x, b)
+    t.cuda.synchronize()
+    for k in ("ids", "gates", "counts", "plan", "status", "slot", "sorted_ids", "block_wrow",
+              "block_expert", "recv"):
+        assert t.equal(a[k], b[k]), f"front_dispatch: {k}"
+    slot = gu.d2h(b["slot"])
+    assert (slot == -1).any() and (slot >= 0).any()

@@ -92,6 +92,23 @@ def test_host_checks_reject_bad_pointers_before_any_launch():
                        P(7), P(8), None, None) == -1
     assert L.lbt_align_sort(ctypes.byref(sh), P(1), P(2), None, P(3), P(4), P(5), P(6), None, None) == -1
     assert L.lbt_histogram(None, P(1), P(2), P(3), None, None) == -1
+    # align + dispatch: null and misaligned rows, missing outputs
+    ad = lambda *a: L.lbt_align_dispatch(ctypes.byref(sh), *a, None)   # noqa: E731
+    assert ad(P(1), P(2), P(3), P(0x1008), P(4), P(5), P(6), P(7), P(0x2000), None) == -1
+    assert ad(P(1), P(2), P(3), P(0x1000), P(4), P(5), P(6), P(7), P(0x2004), None) == -1
+    assert ad(P(1), P(2), P(3), None, P(4), P(5), P(6), P(7), P(0x2000), None) == -1
+    assert ad(P(1), P(2), P(3), P(0x1000), P(4), P(5), P(6), P(7), None, None) == -1
+    assert ad(P(1), P(2), None, P(0x1000), P(4), P(5), P(6), P(7), P(0x2000), None) == -1
+    # front + dispatch: the same, and the front's own arguments
+    fd = lambda *a: L.lbt_front_dispatch(ctypes.byref(sh), *a, None)   # noqa: E731
+    assert fd(P(1), None, P(1), P(2), P(3), P(4), P(5), P(6), P(7), P(8), P(9), P(0x1008),
+              P(0x2000), None) == -1
+    assert fd(P(1), None, P(1), P(2), P(3), P(4), P(5), P(6), P(7), P(8), P(9), P(0x1000),
+              None, None) == -1
+    assert fd(None, None, P(1), P(2), P(3), P(4), P(5), P(6), P(7), P(8), P(9), P(0x1000),
+              P(0x2000), None) == -1
+    assert fd(P(1), None, P(1), P(2), None, P(4), P(5), P(6), P(7), P(8), P(9), P(0x1000),
+              P(0x2000), None) == -1
     # training side: row sizes, null and misaligned pointers
     assert L.lbt_prefetch_weights(ctypes.byref(sh), P(0x1000), P(0x2000), P(0x3000), 24, None) == -1
     assert L.lbt_prefetch_weights(ctypes.byref(sh), P(0x1000), P(0x2008), P(0x3000), 32, None) == -1

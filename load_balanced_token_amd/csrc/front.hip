@@ -201,6 +201,12 @@ __global__ __launch_bounds__(kPlanThreads) void k_route_plan(
     for (int e = threadIdx.x; e < E; e += kPlanThreads) tmask[e] = 0u;
   if (threadIdx.x < 12) m.sStat[threadIdx.x] = 0;
   if (threadIdx.x == 0) sFlags = 0;
+  // MOVE: the first chunk of this workgroup's token row, loaded now so that
+  // its latency hides under the route and the plan
+  u32x4 x0 = {0u, 0u, 0u, 0u};
+  if constexpr (MOVE) {
+    if ((int)threadIdx.x < d.H / 8) x0 = x[(long long)blockIdx.x * (d.H / 8) + threadIdx.x];
+  }
   auto add = [&](long long t, int id) {
     const int r = (int)(t / S), j = (int)(t - (long long)r * S) / kSubTokens;
     atomicAdd(&hist[(r * spr + j) * E + id], 1);
@@ -271,7 +277,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_route_plan(
       const int t = blockIdx.x, K = d.K, H8 = d.H / 8;
       const u32x4* src = x + (long long)t * H8;
       for (int c = threadIdx.x; c < H8; c += kPlanThreads) {
-        const u32x4 v = src[c];
+        const u32x4 v = c < kPlanThreads ? x0 : src[c];
         for (int k = 0; k < K; ++k) {
           const int dst = sDst[t * K + k];
           if (dst >= 0) recv[(long long)dst * H8 + c] = v;
